@@ -1,0 +1,515 @@
+/*
+ * ssu_oracle.c -- CPU reference ("oracle") for the checkpointing selective
+ * state update (ReplaySSM / MTP-replay SSU).  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, obviously-correct definition that the GPU
+ * library is checked against.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load it; the product never does.  It
+ * shares no code, header, table or constant with the HIP path.
+ *
+ * Everything is computed in fp64 with the textbook sequential recurrence,
+ * replayed from the checkpoint one token at a time:
+ *
+ *     dt'  = softplus(dt + dt_bias[h])
+ *     h   <- exp(A[h] * dt') * h  +  dt' * x (outer) B
+ *     y    = h . C  +  D[h] * x
+ *
+ * Sources (cited by page title and section):
+ *  - FlashInfer PR "mamba checkpointing SSU: two-kernel split + ring-buffer
+ *    cache", Description item 2 (ring-buffer cache contract table): the
+ *    head-major rings x_cache (slot, nheads, L, dim), B_cache (slot, ngroups,
+ *    L, dstate), dt_cache (slot, nheads, L) f32, ring_start (slot,) i32; live
+ *    token j sits at (ring_start + j) mod L for j < pnat, append i goes to
+ *    (ring_start + pnat + i) mod L; the host advances ring_start on flush;
+ *    the decay prefix is recomputed, never cached.
+ *  - vLLM API page "replayssm_cutedsl", selective_state_update_replayssm:
+ *    softplus is applied to dt plus dt_bias; dt, A, dt_bias are one value per
+ *    head, D is per head; B and C are per group; x/B/C are BF16; slot zero is
+ *    reserved for padding; nonpositive / out-of-range slots are ignored
+ *    (initialize_replayssm_state docstring).
+ *  - vLLM PR "Add separate CuTeDSL ReplaySSM checkpoints", Overview and
+ *    Claims: the flush works in FP32 and the FP8 read checkpoint is written
+ *    with nearest encoding and an FP32 scale per row; only the accepted
+ *    prefix may change the checkpoint.
+ *
+ * Readings where the pages are silent (each one is also listed in the design
+ * notes of the repository):
+ *  - dt_cache holds dt' (after softplus), as fp32.
+ *  - softplus(v) = v for v > 20, else log1p(exp(v)).
+ *  - A flush folds the first k live ring tokens into the checkpoint and
+ *    advances ring_start by k (mod L); k = 0 changes nothing.
+ *  - The flush result is an FP32 state; it is then encoded.  fp32: stored;
+ *    bf16 / fp16: round to nearest, ties to even (fp16 overflow -> inf);
+ *    fp8 e4m3fn (OCP, max 448), per row of dstate: m = max |h|, scale =
+ *    fp32(m / 448) (1 when that is 0), code = nearest e4m3fn value of
+ *    fp32(h / scale) after clamping to [-448, 448], ties to even code.
+ *  - A padding entry (slot <= 0 or slot >= num_slots) writes zero output rows
+ *    and touches no cache.  An entry with pnat < 0 or pnat + T_b > L is
+ *    treated the same way and raises status bit 1; a flush entry with k < 0
+ *    or k > L is skipped and raises status bit 2; a varlen entry whose token
+ *    count is negative or above max_seqlen is skipped (no output written) and
+ *    raises status bit 4.
+ *
+ * Layouts (all byte strides between slots are arguments; inside a slot the
+ * layout is packed):
+ *   state     [slot][H][P][N]  element type = state dtype
+ *   scale     [slot][H][P]     f32 (fp8 state only)
+ *   x_cache   [slot][H][L][P]  bf16 bits
+ *   B_cache   [slot][G][L][N]  bf16 bits
+ *   dt_cache  [slot][H][L]     f32
+ *   ring_start[slot]           i32
+ *   x   [tok][H][P] bf16 bits,  B, C [tok][G][N] bf16 bits,  dt [tok][H] f32
+ *   out [tok][H][P] f64
+ * Token rows of entry b are tok = bos + i, with bos = cu_seqlens[b] when
+ * cu_seqlens is given (varlen) and bos = b * T otherwise.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_FP8 = 3, OR_F64 = 4 };
+
+/* ---------------------------------------------------------------------- */
+/* Number formats, written from their definitions.                         */
+/* ---------------------------------------------------------------------- */
+
+double or_bf16_value(uint16_t bits) {
+  /* bfloat16 is the upper half of an IEEE binary32. */
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+double or_f16_value(uint16_t bits) {
+  /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
+  int s = bits >> 15, e = (bits >> 10) & 31, m = bits & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+double or_e4m3_value(uint8_t code) {
+  /* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
+   * infinities; exponent 15 with mantissa 7 is NaN, so the largest finite
+   * magnitude is 1.75 * 2^8 = 448. */
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* Round to nearest, ties to even, by searching the sorted table of the
+ * format's non-negative representable values.  `table[i]` is the value of
+ * code i (codes 0..n-1 increase with value).  Returns the code of the
+ * nearest entry; on a tie the entry whose code is even wins. */
+static int nearest_code(const double *table, int n, double a) {
+  int lo = 0, hi = n - 1;
+  if (a <= table[0]) return 0;
+  if (a >= table[n - 1]) return n - 1;
+  while (hi - lo > 1) { /* invariant: table[lo] <= a < table[hi] */
+    int mid = (lo + hi) / 2;
+    if (table[mid] <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  double dl = a - table[lo], dh = table[hi] - a;
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (lo % 2 == 0) ? lo : hi;
+}
+
+static double g_e4m3_tab[127];   /* codes 0x00..0x7E */
+static double g_f16_tab[0x7C01]; /* codes 0x0000..0x7C00, 0x7C00 = 2^16 */
+static double *g_bf16_tab;       /* codes 0x0000..0x7F80, 0x7F80 = 2^128 */
+static int g_tabs_ready = 0;
+
+static void build_tables(void) {
+  if (g_tabs_ready) return;
+  for (int c = 0; c < 127; ++c) g_e4m3_tab[c] = or_e4m3_value((uint8_t)c);
+  /* For IEEE rounding the first code past the largest finite value stands
+   * for the next power of two: a value at least halfway to it rounds to
+   * infinity, and infinity's code is even, as IEEE ties-to-even requires. */
+  for (int c = 0; c < 0x7C00; ++c) g_f16_tab[c] = or_f16_value((uint16_t)c);
+  g_f16_tab[0x7C00] = 65536.0;
+  double *t = (double *)malloc(sizeof(double) * 0x7F81);
+  for (int c = 0; c < 0x7F80; ++c) t[c] = or_bf16_value((uint16_t)c);
+  t[0x7F80] = ldexp(1.0, 128);
+  g_bf16_tab = t;
+  g_tabs_ready = 1;
+}
+
+void or_init_tables(void) { build_tables(); }
+
+uint16_t or_enc_bf16(double v) {
+  build_tables();
+  if (isnan(v)) return 0x7FC0;
+  uint16_t s = signbit(v) ? 0x8000 : 0;
+  return s | (uint16_t)nearest_code(g_bf16_tab, 0x7F81, fabs(v));
+}
+
+uint16_t or_enc_f16(double v) {
+  build_tables();
+  if (isnan(v)) return 0x7E00;
+  uint16_t s = signbit(v) ? 0x8000 : 0;
+  return s | (uint16_t)nearest_code(g_f16_tab, 0x7C01, fabs(v));
+}
+
+/* Saturating e4m3fn encoder: clamp to [-448, 448], then nearest. NaN -> 0x7F. */
+uint8_t or_enc_e4m3_sat(double v) {
+  build_tables();
+  if (isnan(v)) return 0x7F;
+  uint8_t s = signbit(v) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  return s | (uint8_t)nearest_code(g_e4m3_tab, 127, a);
+}
+
+double or_softplus(double v) { return v > 20.0 ? v : log1p(exp(v)); }
+
+/* ---------------------------------------------------------------------- */
+/* Cache description.                                                      */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+  int num_slots, nheads, ngroups, headdim, dstate, ring_len;
+  int state_dtype;
+  uint8_t *state;
+  int64_t state_stride; /* bytes between slots */
+  uint8_t *scale;
+  int64_t scale_stride;
+  uint8_t *x_cache;
+  int64_t x_stride;
+  uint8_t *B_cache;
+  int64_t B_stride;
+  uint8_t *dt_cache;
+  int64_t dt_stride;
+  int32_t *ring_start;
+} or_cache;
+
+static int state_elem_bytes(int dt) {
+  switch (dt) {
+  case OR_F32: return 4;
+  case OR_BF16: return 2;
+  case OR_F16: return 2;
+  case OR_FP8: return 1;
+  default: return 8;
+  }
+}
+
+/* Decode the checkpoint of (slot, head) into h[P*N] (fp64). */
+static void decode_state(const or_cache *c, int slot, int head, double *h) {
+  const int P = c->headdim, N = c->dstate, eb = state_elem_bytes(c->state_dtype);
+  const uint8_t *base = c->state + (int64_t)slot * c->state_stride +
+                        (int64_t)head * P * N * eb;
+  for (int p = 0; p < P; ++p) {
+    double sc = 1.0;
+    if (c->state_dtype == OR_FP8) {
+      float f;
+      memcpy(&f, c->scale + (int64_t)slot * c->scale_stride +
+                     ((int64_t)head * P + p) * 4, 4);
+      sc = (double)f;
+    }
+    for (int n = 0; n < N; ++n) {
+      const uint8_t *e = base + ((int64_t)p * N + n) * eb;
+      double v;
+      switch (c->state_dtype) {
+      case OR_F32: { float f; memcpy(&f, e, 4); v = f; } break;
+      case OR_BF16: { uint16_t u; memcpy(&u, e, 2); v = or_bf16_value(u); } break;
+      case OR_F16: { uint16_t u; memcpy(&u, e, 2); v = or_f16_value(u); } break;
+      case OR_FP8: v = or_e4m3_value(*e) * sc; break;
+      default: memcpy(&v, e, 8); break;
+      }
+      h[p * N + n] = v;
+    }
+  }
+}
+
+/* Encode one row of an fp32 state (the flush result) into the checkpoint. */
+static void encode_row(const or_cache *c, int slot, int head, int p,
+                       const float *row) {
+  const int P = c->headdim, N = c->dstate, eb = state_elem_bytes(c->state_dtype);
+  uint8_t *base = c->state + (int64_t)slot * c->state_stride +
+                  ((int64_t)head * P * N + (int64_t)p * N) * eb;
+  if (c->state_dtype == OR_FP8) {
+    float m = 0.0f;
+    for (int n = 0; n < N; ++n)
+      if (fabsf(row[n]) > m) m = fabsf(row[n]);
+    float scale = m / 448.0f; /* IEEE single division, correctly rounded */
+    if (!(scale > 0.0f)) scale = 1.0f;
+    memcpy(c->scale + (int64_t)slot * c->scale_stride + ((int64_t)head * P + p) * 4,
+           &scale, 4);
+    for (int n = 0; n < N; ++n) {
+      float q = row[n] / scale;
+      base[n] = or_enc_e4m3_sat((double)q);
+    }
+    return;
+  }
+  for (int n = 0; n < N; ++n) {
+    uint8_t *e = base + (int64_t)n * eb;
+    switch (c->state_dtype) {
+    case OR_F32: memcpy(e, &row[n], 4); break;
+    case OR_BF16: { uint16_t u = or_enc_bf16((double)row[n]); memcpy(e, &u, 2); } break;
+    case OR_F16: { uint16_t u = or_enc_f16((double)row[n]); memcpy(e, &u, 2); } break;
+    default: break;
+    }
+  }
+}
+
+/* fp64 state mode (test only): store without rounding. */
+static void store_state_f64(const or_cache *c, int slot, int head, const double *h) {
+  const int PN = c->headdim * c->dstate;
+  uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * PN * 8;
+  memcpy(base, h, sizeof(double) * PN);
+}
+
+static uint16_t rd_u16(const uint8_t *p) { uint16_t u; memcpy(&u, p, 2); return u; }
+static float rd_f32(const uint8_t *p) { float f; memcpy(&f, p, 4); return f; }
+
+/* One recurrence step on h[P*N]:  h <- exp(a*d) h + d x B^T.  */
+static void ssu_token(double *h, int P, int N, double a, double d,
+                      const double *xv, const double *Bv) {
+  const double decay = exp(a * d);
+  for (int p = 0; p < P; ++p)
+    for (int n = 0; n < N; ++n)
+      h[p * N + n] = decay * h[p * N + n] + d * xv[p] * Bv[n];
+}
+
+/* ---------------------------------------------------------------------- */
+/* Replay step.                                                            */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * For each batch entry: replay the checkpoint through the pnat live ring
+ * tokens and then the T_b new tokens, reading out y after every new token;
+ * append the new tokens' x, B and dt' to the ring.  The checkpoint and
+ * ring_start are not modified.  Returns the status bits.
+ */
+int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlens,
+                   const int32_t *slot_idx, const int32_t *pnat,
+                   const uint16_t *x, const uint16_t *Bm, const uint16_t *Cm,
+                   const float *dt, const float *A, const float *D,
+                   const float *dt_bias, double *out) {
+  const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
+            L = c->ring_len, HPG = H / G;
+  int status = 0;
+  build_tables(); /* before any parallel region */
+  /* Pass 1: validity of each entry (serial; cheap). */
+  int *ok = (int *)calloc(batch > 0 ? batch : 1, sizeof(int));
+  for (int b = 0; b < batch; ++b) {
+    int bos = cu_seqlens ? cu_seqlens[b] : b * T;
+    int Tb = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : T;
+    int slot = slot_idx[b];
+    if (Tb < 0 || Tb > T) { status |= 4; ok[b] = 0; continue; }
+    if (slot <= 0 || slot >= c->num_slots) { ok[b] = 1; /* padding */ }
+    else if (pnat[b] < 0 || pnat[b] + Tb > L) { status |= 1; ok[b] = 1; }
+    else ok[b] = 2;
+    if (ok[b] == 1)
+      for (int i = 0; i < Tb; ++i)
+        for (int hh = 0; hh < H; ++hh)
+          for (int p = 0; p < P; ++p)
+            out[((int64_t)(bos + i) * H + hh) * P + p] = 0.0;
+  }
+  /* Pass 2: the recurrence, one (entry, head) at a time. */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < batch; ++b) {
+    for (int hh = 0; hh < H; ++hh) {
+      if (ok[b] != 2) continue;
+      const int bos = cu_seqlens ? cu_seqlens[b] : b * T;
+      const int Tb = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : T;
+      const int slot = slot_idx[b], p0 = pnat[b], r = c->ring_start[slot];
+      const int g = hh / HPG;
+      double *h = (double *)malloc(sizeof(double) * P * N);
+      double *xv = (double *)malloc(sizeof(double) * P);
+      double *Bv = (double *)malloc(sizeof(double) * N);
+      decode_state(c, slot, hh, h);
+      const uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
+      const uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
+      const uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
+      /* live ring tokens: stored dt' is used as is */
+      for (int s = 0; s < p0; ++s) {
+        int pos = (r + s) % L;
+        double d = rd_f32(ds + ((int64_t)hh * L + pos) * 4);
+        for (int p = 0; p < P; ++p)
+          xv[p] = or_bf16_value(rd_u16(xs + (((int64_t)hh * L + pos) * P + p) * 2));
+        for (int n = 0; n < N; ++n)
+          Bv[n] = or_bf16_value(rd_u16(Bs + (((int64_t)g * L + pos) * N + n) * 2));
+        ssu_token(h, P, N, A[hh], d, xv, Bv);
+      }
+      /* new tokens: softplus, update, read out */
+      for (int i = 0; i < Tb; ++i) {
+        int64_t tok = bos + i;
+        double d = or_softplus((double)dt[tok * H + hh] + (double)dt_bias[hh]);
+        for (int p = 0; p < P; ++p) xv[p] = or_bf16_value(x[(tok * H + hh) * P + p]);
+        for (int n = 0; n < N; ++n) Bv[n] = or_bf16_value(Bm[(tok * G + g) * N + n]);
+        ssu_token(h, P, N, A[hh], d, xv, Bv);
+        for (int p = 0; p < P; ++p) {
+          double y = 0.0;
+          for (int n = 0; n < N; ++n)
+            y += h[p * N + n] * or_bf16_value(Cm[(tok * G + g) * N + n]);
+          out[(tok * H + hh) * P + p] = y + (double)D[hh] * xv[p];
+        }
+      }
+      free(h); free(xv); free(Bv);
+    }
+  }
+  /* Pass 3: ring appends (after every read of this call). */
+  for (int b = 0; b < batch; ++b) {
+    if (ok[b] != 2) continue;
+    const int bos = cu_seqlens ? cu_seqlens[b] : b * T;
+    const int Tb = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : T;
+    const int slot = slot_idx[b], p0 = pnat[b], r = c->ring_start[slot];
+    uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
+    uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
+    uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
+    for (int i = 0; i < Tb; ++i) {
+      int64_t tok = bos + i;
+      int pos = (r + p0 + i) % L;
+      for (int hh = 0; hh < H; ++hh) {
+        float d = (float)or_softplus((double)dt[tok * H + hh] + (double)dt_bias[hh]);
+        memcpy(ds + ((int64_t)hh * L + pos) * 4, &d, 4);
+        memcpy(xs + ((int64_t)hh * L + pos) * P * 2, x + (tok * H + hh) * P, (size_t)P * 2);
+      }
+      for (int g = 0; g < G; ++g)
+        memcpy(Bs + ((int64_t)g * L + pos) * N * 2, Bm + (tok * G + g) * N, (size_t)N * 2);
+    }
+  }
+  free(ok);
+  return status;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Flush.                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * For each entry j with k = num_fold[j] > 0: fold the first k live ring
+ * tokens into the checkpoint (fp64 recurrence, result rounded to fp32 as the
+ * flush's FP32 state), re-encode it, and advance ring_start by k (mod L).
+ */
+int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
+             const int32_t *num_fold, const float *A) {
+  const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
+            L = c->ring_len, HPG = H / G;
+  int status = 0;
+  build_tables(); /* before any parallel region */
+  for (int j = 0; j < n; ++j) {
+    int slot = slot_idx[j], k = num_fold[j];
+    if (slot <= 0 || slot >= c->num_slots) continue;
+    if (k < 0 || k > L) { status |= 2; continue; }
+  }
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int j = 0; j < n; ++j) {
+    for (int hh = 0; hh < H; ++hh) {
+      const int slot = slot_idx[j], k = num_fold[j];
+      if (slot <= 0 || slot >= c->num_slots || k <= 0 || k > L) continue;
+      const int r = c->ring_start[slot], g = hh / HPG;
+      double *h = (double *)malloc(sizeof(double) * P * N);
+      double *xv = (double *)malloc(sizeof(double) * P);
+      double *Bv = (double *)malloc(sizeof(double) * N);
+      float *row = (float *)malloc(sizeof(float) * N);
+      decode_state(c, slot, hh, h);
+      const uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
+      const uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
+      const uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
+      for (int s = 0; s < k; ++s) {
+        int pos = (r + s) % L;
+        double d = rd_f32(ds + ((int64_t)hh * L + pos) * 4);
+        for (int p = 0; p < P; ++p)
+          xv[p] = or_bf16_value(rd_u16(xs + (((int64_t)hh * L + pos) * P + p) * 2));
+        for (int q = 0; q < N; ++q)
+          Bv[q] = or_bf16_value(rd_u16(Bs + (((int64_t)g * L + pos) * N + q) * 2));
+        ssu_token(h, P, N, A[hh], d, xv, Bv);
+      }
+      if (c->state_dtype == OR_F64) {
+        store_state_f64(c, slot, hh, h);
+      } else {
+        for (int p = 0; p < P; ++p) {
+          for (int q = 0; q < N; ++q) row[q] = (float)h[p * N + q];
+          encode_row(c, slot, hh, p, row);
+        }
+      }
+      free(h); free(xv); free(Bv); free(row);
+    }
+  }
+  for (int j = 0; j < n; ++j) {
+    int slot = slot_idx[j], k = num_fold[j];
+    if (slot <= 0 || slot >= c->num_slots || k <= 0 || k > L) continue;
+    c->ring_start[slot] = (c->ring_start[slot] + k) % L;
+  }
+  return status;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Initialisation from FP32 prefill states.                                */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * states: [n][H][P][N] f32 with `states_stride` elements between entries
+ * (0 broadcasts entry 0).  For each valid slot: encode the state, zero the
+ * slot's x/B/dt rings and set ring_start to 0.  Invalid slots are ignored.
+ */
+void or_init_state(const or_cache *c, const float *states, int64_t states_stride,
+                   const int32_t *slot_idx, int n) {
+  const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
+            L = c->ring_len;
+  build_tables();
+  for (int j = 0; j < n; ++j) {
+    int slot = slot_idx[j];
+    if (slot <= 0 || slot >= c->num_slots) continue;
+    const float *src = states + (int64_t)j * states_stride;
+    for (int hh = 0; hh < H; ++hh) {
+      if (c->state_dtype == OR_F64) {
+        double *h = (double *)malloc(sizeof(double) * P * N);
+        for (int e = 0; e < P * N; ++e) h[e] = src[(int64_t)hh * P * N + e];
+        store_state_f64(c, slot, hh, h);
+        free(h);
+      } else {
+        for (int p = 0; p < P; ++p)
+          encode_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N);
+      }
+    }
+    memset(c->x_cache + (int64_t)slot * c->x_stride, 0, (size_t)H * L * P * 2);
+    memset(c->B_cache + (int64_t)slot * c->B_stride, 0, (size_t)G * L * N * 2);
+    memset(c->dt_cache + (int64_t)slot * c->dt_stride, 0, (size_t)H * L * 4);
+    c->ring_start[slot] = 0;
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Array forms of the format helpers (used by the tests' pins).            */
+/* ---------------------------------------------------------------------- */
+
+void or_enc_bf16_array(const double *v, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_enc_bf16(v[i]);
+}
+void or_enc_f16_array(const double *v, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_enc_f16(v[i]);
+}
+void or_enc_e4m3_array(const double *v, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_enc_e4m3_sat(v[i]);
+}
+void or_bf16_value_array(const uint16_t *b, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_bf16_value(b[i]);
+}
+void or_f16_value_array(const uint16_t *b, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_f16_value(b[i]);
+}
+void or_e4m3_value_array(const uint8_t *b, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_e4m3_value(b[i]);
+}
+void or_softplus_array(const double *v, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_softplus(v[i]);
+}

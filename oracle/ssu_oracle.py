@@ -1,0 +1,201 @@
+"""Python front end of the CPU oracle (oracle/ssu_oracle.c).  TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+module; the product path never imports it.  It loads (building it with gcc if
+it is missing) the plain fp64 C implementation and passes numpy buffers to it.
+The cache and step objects are the ones `synth` generates (attribute access
+only; nothing else is shared with the GPU library).
+
+Functions:
+  replay_step(cache, step)              -> (out fp64 [tokens, H, P], status)
+  flush(cache, slot_idx, num_fold, A)   -> status
+  init_state(cache, states, slot_idx, states_stride=None)
+  encoders / decoders / softplus on arrays, for the pins.
+The cache passed in is modified in place (ring appends, flushed checkpoints,
+ring_start), exactly as the library modifies device memory.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssu_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssu_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "f64": 4}
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) into oracle/libssu_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _OrCache(ctypes.Structure):
+    _fields_ = [
+        ("num_slots", ctypes.c_int), ("nheads", ctypes.c_int), ("ngroups", ctypes.c_int),
+        ("headdim", ctypes.c_int), ("dstate", ctypes.c_int), ("ring_len", ctypes.c_int),
+        ("state_dtype", ctypes.c_int),
+        ("state", ctypes.c_void_p), ("state_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p), ("scale_stride", ctypes.c_int64),
+        ("x_cache", ctypes.c_void_p), ("x_stride", ctypes.c_int64),
+        ("B_cache", ctypes.c_void_p), ("B_stride", ctypes.c_int64),
+        ("dt_cache", ctypes.c_void_p), ("dt_stride", ctypes.c_int64),
+        ("ring_start", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            L = ctypes.CDLL(build())
+            P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+            L.or_replay_step.restype = I
+            L.or_replay_step.argtypes = [ctypes.POINTER(_OrCache), I, I, P, P, P, P, P, P, P,
+                                         P, P, P, P]
+            L.or_flush.restype = I
+            L.or_flush.argtypes = [ctypes.POINTER(_OrCache), I, P, P, P]
+            L.or_init_state.restype = None
+            L.or_init_state.argtypes = [ctypes.POINTER(_OrCache), P, I64, P, I]
+            for name in ("or_enc_bf16_array", "or_enc_f16_array", "or_enc_e4m3_array",
+                         "or_bf16_value_array", "or_f16_value_array", "or_e4m3_value_array",
+                         "or_softplus_array"):
+                f = getattr(L, name)
+                f.restype = None
+                f.argtypes = [P, P, I64]
+            L.or_init_tables()
+            _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _as_orcache(cache) -> _OrCache:
+    s = cache.spec
+    for a in (cache.state, cache.scale, cache.x_cache, cache.B_cache, cache.dt_cache,
+              cache.ring_start):
+        assert a.flags["C_CONTIGUOUS"]
+    assert cache.ring_start.dtype == np.int32
+    return _OrCache(
+        s.num_slots, s.nheads, s.ngroups, s.headdim, s.dstate, s.ring_len,
+        _DTYPE_CODE[s.state_dtype],
+        cache.state.ctypes.data, cache.state.shape[1],
+        cache.scale.ctypes.data, cache.scale.shape[1],
+        cache.x_cache.ctypes.data, cache.x_cache.shape[1],
+        cache.B_cache.ctypes.data, cache.B_cache.shape[1],
+        cache.dt_cache.ctypes.data, cache.dt_cache.shape[1],
+        cache.ring_start.ctypes.data)
+
+
+def replay_step(cache, step):
+    """Replay step (see or_replay_step).  Returns (out fp64 [tokens, H, P], status)."""
+    s = cache.spec
+    oc = _as_orcache(cache)
+    ntok = step.tokens
+    out = np.full((ntok, s.nheads, s.headdim), np.nan, np.float64)
+    x = _c(step.x, np.uint16)
+    B = _c(step.B, np.uint16)
+    C = _c(step.C, np.uint16)
+    dt = _c(step.dt, np.float32)
+    A = _c(step.A, np.float32)
+    D = _c(step.D, np.float32)
+    db = _c(step.dt_bias, np.float32)
+    slots = _c(step.slot_idx, np.int32)
+    pnat = _c(step.pnat, np.int32)
+    cu = None if step.cu_seqlens is None else _c(step.cu_seqlens, np.int32)
+    assert x.shape == (ntok, s.nheads, s.headdim) and B.shape == (ntok, s.ngroups, s.dstate)
+    st = lib().or_replay_step(ctypes.byref(oc), step.batch, step.T, _ptr(cu), _ptr(slots),
+                              _ptr(pnat), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                              _ptr(D), _ptr(db), out.ctypes.data)
+    return out, st
+
+
+def flush(cache, slot_idx, num_fold, A):
+    """Fold the first k live ring tokens into each listed slot's checkpoint."""
+    oc = _as_orcache(cache)
+    slots = _c(slot_idx, np.int32)
+    k = _c(num_fold, np.int32)
+    A = _c(A, np.float32)
+    assert slots.shape == k.shape
+    return lib().or_flush(ctypes.byref(oc), slots.shape[0], _ptr(slots), _ptr(k), _ptr(A))
+
+
+def init_state(cache, states, slot_idx, states_stride=None):
+    """Encode fp32 states [n, H, P, N] into the listed slots and clear their rings."""
+    s = cache.spec
+    oc = _as_orcache(cache)
+    states = np.asarray(states, np.float32)
+    slots = _c(slot_idx, np.int32)
+    if states_stride is None:
+        states = np.ascontiguousarray(states)
+        states_stride = s.nheads * s.headdim * s.dstate
+    lib().or_init_state(ctypes.byref(oc), states.ctypes.data, int(states_stride), _ptr(slots),
+                        slots.shape[0])
+
+
+def _arr(fn, a, in_dtype, out_dtype):
+    a = np.ascontiguousarray(a, dtype=in_dtype)
+    out = np.empty(a.shape, out_dtype)
+    getattr(lib(), fn)(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def enc_bf16(v):
+    return _arr("or_enc_bf16_array", v, np.float64, np.uint16)
+
+
+def enc_f16(v):
+    return _arr("or_enc_f16_array", v, np.float64, np.uint16)
+
+
+def enc_e4m3(v):
+    return _arr("or_enc_e4m3_array", v, np.float64, np.uint8)
+
+
+def bf16_value(b):
+    return _arr("or_bf16_value_array", b, np.uint16, np.float64)
+
+
+def f16_value(b):
+    return _arr("or_f16_value_array", b, np.uint16, np.float64)
+
+
+def e4m3_value(b):
+    return _arr("or_e4m3_value_array", b, np.uint8, np.float64)
+
+
+def softplus(v):
+    return _arr("or_softplus_array", v, np.float64, np.float64)
+
+
+def decode_state(cache, slot):
+    """fp64 [H, P, N] value of one slot's checkpoint (decode rule of the oracle)."""
+    s = cache.spec
+    raw = cache.state_view(slot)
+    if s.state_dtype in ("f32", "f64"):
+        return raw.astype(np.float64)
+    if s.state_dtype == "bf16":
+        return bf16_value(raw)
+    if s.state_dtype == "f16":
+        return f16_value(raw)
+    return e4m3_value(raw) * cache.scale_view(slot).astype(np.float64)[:, :, None]

@@ -1,0 +1,298 @@
+"""Seeded synthetic inputs for the ReplaySSM step and flush.
+
+This module draws random numbers into the cache and step layouts and nothing
+else: it holds none of the method's arithmetic (no softplus, no decay, no
+encoding rule), so that the GPU library and the CPU oracle, which both read
+these arrays, cannot share a mistake through it.  Casting a random fp32 sample
+to bf16 / fp16 / fp8 is done with PyTorch's own CPU casts.
+
+Cache layout (one slot = one request), matching the ring-buffer cache contract
+of the FlashInfer checkpointing-SSU page (Description, item 2) and the vLLM
+replayssm_cutedsl page (slot 0 reserved for padding, padding allowed between
+slot pages):
+
+    state     [slot][H][P][N]   state dtype
+    scale     [slot][H][P]      f32 (fp8 state only)
+    x_cache   [slot][H][L][P]   bf16
+    B_cache   [slot][G][L][N]   bf16
+    dt_cache  [slot][H][L]      f32 (holds dt' = softplus(dt + dt_bias))
+    ring_start[slot]            i32
+
+Every per-slot tensor is stored as a byte array [num_slots, stride] whose
+stride is the packed size plus `slot_pad` bytes; pad bytes hold a canary.
+
+Value laws (the synthetic workloads' recipe): x, B, C ~ N(0, 1) in bf16;
+dt ~ N(0, 0.5^2); dt_bias ~ U(-4, -2); A = -exp(U(0, ln 16)); D ~ N(0, 1);
+checkpoint h0 ~ N(0, 0.1^2).  Ring dt' values are drawn log-uniform on
+[0.004, 0.5], the range softplus(dt + dt_bias) covers under the laws above.
+An fp8 checkpoint is drawn as random e4m3 codes (a N(0, 32^2) sample cast to
+e4m3fn) with a per-row scale 0.1/32 * U(0.5, 1.5), which gives h0 of about the
+same spread.  All L ring entries (live and dead) hold random data, so reading
+a wrong entry changes the result.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+DTYPES = ("f32", "bf16", "f16", "fp8", "f64")
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "f64": 8}
+CANARY = 0xA5
+
+
+def _round16(n: int) -> int:
+    return (n + 15) // 16 * 16
+
+
+@dataclasses.dataclass
+class CacheSpec:
+    num_slots: int
+    nheads: int
+    ngroups: int
+    headdim: int = 64
+    dstate: int = 128
+    ring_len: int = 16
+    state_dtype: str = "bf16"
+    slot_pad: int = 0  # bytes appended to every per-slot stride
+
+    def __post_init__(self):
+        assert self.state_dtype in DTYPES
+        assert self.nheads % self.ngroups == 0
+
+    # packed per-slot byte sizes
+    def state_bytes(self):
+        return self.nheads * self.headdim * self.dstate * ELEM_BYTES[self.state_dtype]
+
+    def scale_bytes(self):
+        return self.nheads * self.headdim * 4
+
+    def x_bytes(self):
+        return self.nheads * self.ring_len * self.headdim * 2
+
+    def B_bytes(self):
+        return self.ngroups * self.ring_len * self.dstate * 2
+
+    def dt_bytes(self):
+        return self.nheads * self.ring_len * 4
+
+    def strides(self):
+        """Per-slot byte strides (packed size rounded to 16 B, plus the pad)."""
+        p = self.slot_pad
+        return dict(
+            state=_round16(self.state_bytes()) + p,
+            scale=_round16(self.scale_bytes()) + p,
+            x=_round16(self.x_bytes()) + p,
+            B=_round16(self.B_bytes()) + p,
+            dt=_round16(self.dt_bytes()) + p,
+        )
+
+
+@dataclasses.dataclass
+class CacheArrays:
+    spec: CacheSpec
+    state: np.ndarray  # uint8 [num_slots, stride]
+    scale: np.ndarray
+    x_cache: np.ndarray
+    B_cache: np.ndarray
+    dt_cache: np.ndarray
+    ring_start: np.ndarray  # int32 [num_slots]
+
+    def copy(self) -> "CacheArrays":
+        return CacheArrays(self.spec, *(a.copy() for a in (
+            self.state, self.scale, self.x_cache, self.B_cache, self.dt_cache,
+            self.ring_start)))
+
+    # typed views of the packed part of one slot (for tests)
+    def state_view(self, slot):
+        s = self.spec
+        dt = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16,
+              "fp8": np.uint8, "f64": np.float64}[s.state_dtype]
+        raw = self.state[slot, : s.state_bytes()]
+        return raw.view(dt).reshape(s.nheads, s.headdim, s.dstate)
+
+    def scale_view(self, slot):
+        s = self.spec
+        return self.scale[slot, : s.scale_bytes()].view(np.float32).reshape(s.nheads, s.headdim)
+
+    def x_view(self, slot):
+        s = self.spec
+        return self.x_cache[slot, : s.x_bytes()].view(np.uint16).reshape(
+            s.nheads, s.ring_len, s.headdim)
+
+    def B_view(self, slot):
+        s = self.spec
+        return self.B_cache[slot, : s.B_bytes()].view(np.uint16).reshape(
+            s.ngroups, s.ring_len, s.dstate)
+
+    def dt_view(self, slot):
+        s = self.spec
+        return self.dt_cache[slot, : s.dt_bytes()].view(np.float32).reshape(s.nheads, s.ring_len)
+
+
+@dataclasses.dataclass
+class StepInputs:
+    batch: int
+    T: int  # tokens per entry, or the maximum per entry when varlen
+    slot_idx: np.ndarray  # int32 [batch]
+    pnat: np.ndarray  # int32 [batch]
+    cu_seqlens: Optional[np.ndarray]  # int32 [batch+1] or None
+    x: np.ndarray  # uint16 (bf16 bits) [tokens, H, P]
+    B: np.ndarray  # uint16 [tokens, G, N]
+    C: np.ndarray  # uint16 [tokens, G, N]
+    dt: np.ndarray  # f32 [tokens, H]
+    A: np.ndarray  # f32 [H]
+    D: np.ndarray  # f32 [H]
+    dt_bias: np.ndarray  # f32 [H]
+
+    @property
+    def tokens(self) -> int:
+        return int(self.cu_seqlens[-1]) if self.cu_seqlens is not None else self.batch * self.T
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator()
+    g.manual_seed(int(seed))
+    return g
+
+
+def _bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _f16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _fill_slots(arr: np.ndarray, packed: np.ndarray):
+    """Write `packed` (shape [num_slots, nbytes], uint8) into the slot pages."""
+    arr[:, : packed.shape[1]] = packed
+
+
+def random_state_bytes(spec: CacheSpec, n: int, g: torch.Generator, h0_std: float = 0.1):
+    """Random checkpoints for n slots: (state bytes [n, state_bytes], scale bytes)."""
+    H, P, N = spec.nheads, spec.headdim, spec.dstate
+    dt = spec.state_dtype
+    scale = np.zeros((n, H * P * 4), np.uint8)
+    if dt == "fp8":
+        codes = (torch.randn(n, H, P, N, generator=g) * 32.0).clamp(-448, 448)
+        codes = codes.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        sc = (h0_std / 32.0) * (0.5 + torch.rand(n, H, P, generator=g))
+        scale = sc.to(torch.float32).numpy().view(np.uint8).reshape(n, -1)
+        return codes.reshape(n, -1), scale
+    h0 = torch.randn(n, H, P, N, generator=g, dtype=torch.float64) * h0_std
+    if dt == "f64":
+        raw = h0.numpy().view(np.uint8)
+    elif dt == "f32":
+        raw = h0.to(torch.float32).numpy().view(np.uint8)
+    elif dt == "bf16":
+        raw = _bf16_bits(h0.to(torch.float32)).view(np.uint8)
+    else:
+        raw = _f16_bits(h0.to(torch.float32)).view(np.uint8)
+    return raw.reshape(n, -1), scale
+
+
+def make_cache(spec: CacheSpec, seed: int, h0_std: float = 0.1) -> CacheArrays:
+    """A cache with random checkpoints, random rings and random ring_start."""
+    g = _gen(seed)
+    S, H, G, P, N, L = (spec.num_slots, spec.nheads, spec.ngroups, spec.headdim,
+                        spec.dstate, spec.ring_len)
+    st = spec.strides()
+    arrs = {k: np.full((S, st[k]), CANARY, np.uint8) for k in st}
+    state, scale = random_state_bytes(spec, S, g, h0_std)
+    _fill_slots(arrs["state"], state)
+    if spec.state_dtype == "fp8":
+        _fill_slots(arrs["scale"], scale)
+    xr = _bf16_bits(torch.randn(S, H, L, P, generator=g)).view(np.uint8).reshape(S, -1)
+    Br = _bf16_bits(torch.randn(S, G, L, N, generator=g)).view(np.uint8).reshape(S, -1)
+    lo, hi = math.log(0.004), math.log(0.5)
+    dtr = torch.exp(lo + (hi - lo) * torch.rand(S, H, L, generator=g, dtype=torch.float64))
+    dtr = dtr.to(torch.float32).numpy().view(np.uint8).reshape(S, -1)
+    _fill_slots(arrs["x"], xr)
+    _fill_slots(arrs["B"], Br)
+    _fill_slots(arrs["dt"], dtr)
+    ring_start = torch.randint(0, L, (S,), generator=g, dtype=torch.int32).numpy()
+    return CacheArrays(spec, arrs["state"], arrs["scale"], arrs["x"], arrs["B"], arrs["dt"],
+                       ring_start.copy())
+
+
+def make_params(spec: CacheSpec, seed: int):
+    """Per-head parameters A, D, dt_bias (f32 [H])."""
+    g = _gen(seed)
+    H = spec.nheads
+    A = -torch.exp(torch.rand(H, generator=g, dtype=torch.float64) * math.log(16.0))
+    D = torch.randn(H, generator=g, dtype=torch.float64)
+    dt_bias = -4.0 + 2.0 * torch.rand(H, generator=g, dtype=torch.float64)
+    f = lambda t: t.to(torch.float32).numpy().copy()
+    return f(A), f(D), f(dt_bias)
+
+
+def make_step(spec: CacheSpec, batch: int, T: int, seed: int, pnat_max: int,
+              varlen: bool = False, slots: Optional[np.ndarray] = None,
+              n_padding: int = 0, pnat_fixed: Optional[int] = None) -> StepInputs:
+    """One decode step over `batch` entries.
+
+    Active entries use unique random slots from [1, num_slots) (or `slots`);
+    the first `n_padding` entries (after a seeded shuffle) are padding (slot 0).
+    pnat ~ U{0..pnat_max} (or `pnat_fixed`); with `varlen`, T_b ~ U{1..T} and
+    the inputs are packed along cu_seqlens.
+    """
+    g = _gen(seed)
+    H, G, P, N = spec.nheads, spec.ngroups, spec.headdim, spec.dstate
+    if slots is None:
+        perm = torch.randperm(spec.num_slots - 1, generator=g)[: batch - n_padding] + 1
+        slots = np.concatenate([np.zeros(n_padding, np.int32), perm.numpy().astype(np.int32)])
+        order = torch.randperm(batch, generator=g).numpy()
+        slots = slots[order]
+    slots = np.asarray(slots, np.int32)
+    assert slots.shape == (batch,)
+    if pnat_fixed is not None:
+        pnat = np.full(batch, pnat_fixed, np.int32)
+    else:
+        pnat = torch.randint(0, pnat_max + 1, (batch,), generator=g, dtype=torch.int32).numpy()
+    if varlen:
+        Tb = torch.randint(1, T + 1, (batch,), generator=g, dtype=torch.int32).numpy()
+        cu = np.zeros(batch + 1, np.int32)
+        cu[1:] = np.cumsum(Tb)
+        ntok = int(cu[-1])
+    else:
+        cu = None
+        ntok = batch * T
+    x = _bf16_bits(torch.randn(ntok, H, P, generator=g))
+    B = _bf16_bits(torch.randn(ntok, G, N, generator=g))
+    C = _bf16_bits(torch.randn(ntok, G, N, generator=g))
+    dt = (torch.randn(ntok, H, generator=g, dtype=torch.float64) * 0.5).to(torch.float32).numpy()
+    A, D, dt_bias = make_params(spec, seed + 7919)
+    return StepInputs(batch, T, slots, pnat.astype(np.int32), cu, x, B, C, dt, A, D, dt_bias)
+
+
+# ---------------------------------------------------------------------------
+# The five synthetic workloads (cache geometry, step shape, value laws above).
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    # tiny reference: 2 active of 4 slots (slot 0 padding), fp32 state, T=1
+    "tiny": dict(num_slots=4, nheads=8, ngroups=1, state_dtype="f32", batch=2, T=1,
+                 pnat_max=8, out_dtype="f32"),
+    # MTP decode: batch 64 of 128 slots, H64 G8, bf16 state, T=4 (1 + 3 drafts)
+    "mtp": dict(num_slots=128, nheads=64, ngroups=8, state_dtype="bf16", batch=64, T=4,
+                pnat_max=4, out_dtype="bf16"),
+    # production mixed-pnat sweep: H128 G8, fp16 state, T=8 (1 + 7 drafts)
+    "prod": dict(num_slots=None, nheads=128, ngroups=8, state_dtype="f16", batch=256, T=8,
+                 pnat_max=8, out_dtype="bf16"),
+    # quantised checkpoint: batch 256, fp8 e4m3 + row scales, T=4, flush every step
+    "fp8": dict(num_slots=None, nheads=128, ngroups=8, state_dtype="fp8", batch=256, T=4,
+                pnat_max=0, out_dtype="bf16", flush_k=(1, 4)),
+    # large batch: 1024 active of 2048 slots, bf16 state, varlen T_b ~ U{1..8}, 256 B slot pad
+    "large": dict(num_slots=2048, nheads=128, ngroups=8, state_dtype="bf16", batch=1024, T=8,
+                  pnat_max=8, out_dtype="bf16", varlen=True, slot_pad=256),
+}
+
+
+def flush_counts(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """k ~ U{lo..hi} per entry (int32)."""
+    g = _gen(seed)
+    return torch.randint(lo, hi + 1, (batch,), generator=g, dtype=torch.int32).numpy()
