@@ -1,0 +1,222 @@
+/*
+ * ssu.h -- C ABI of libssu: the checkpointing selective state update
+ * (ReplaySSM / MTP-replay SSU) of Mamba-2 speculative decode, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * For every cache slot (one request) and head the library keeps a checkpoint
+ * state h[headdim=64][dstate=128] and head-major rings holding the inputs of
+ * the accepted tokens that are not yet folded into it.  A replay step reads
+ * the checkpoint, replays it through the live ring tokens and this step's new
+ * (draft) tokens, writes one output row per new token and appends the new
+ * tokens to the ring; a flush folds accepted tokens into the checkpoint.
+ *
+ * Sources, by page and section:
+ *  [FI]  FlashInfer PR "mamba checkpointing SSU: two-kernel split +
+ *        ring-buffer cache for checkpointing SSU" -- Description item 1 (the
+ *        two-kernel split, caller-provided graph-safe scratch, auto-dispatch
+ *        on batch x nheads, the algorithm override) and item 2 (the ring
+ *        contract table: x_cache, B_cache, dt_cache f32, ring_start i32; the
+ *        live / append positions; the host owns ring bookkeeping; the decay
+ *        prefix is recomputed, never cached).
+ *  [VD]  vLLM API page "replayssm_cutedsl" -- initialize_replayssm_state
+ *        (FP32 [batch, heads, 64, 128] prefill states, a stride-0 broadcast
+ *        state, nonpositive / out-of-range slots ignored, rings cleared) and
+ *        selective_state_update_replayssm (softplus of dt + dt_bias; per-head
+ *        dt, A, dt_bias, D; per-group B and C; BF16 x, B, C and output;
+ *        unique active slots; slot 0 reserved for padding; padding allowed
+ *        between slot pages; invalid arguments raise ValueError).
+ *  [VP]  vLLM PR "Add separate CuTeDSL ReplaySSM checkpoints" -- Overview
+ *        and Claims (FP32 flush work; the FP8 read checkpoint uses nearest
+ *        encoding with an FP32 scale per row; only the accepted prefix may
+ *        change the checkpoint).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises, and every kernel is enqueued on
+ *    the given stream (NULL = the default stream), so calls can be captured
+ *    in a HIP graph.  Calls that touch the same slots must be ordered by the
+ *    caller (same stream or events).
+ *  - Returns SSU_OK (0) or a negative error code; nothing is launched when an
+ *    error is returned.  ssu_last_error() gives the calling thread's last
+ *    message.  SSU_ERR_INVALID corresponds to the pages' ValueError,
+ *    SSU_ERR_UNSUPPORTED to a shape/type the kernels do not implement.
+ *  - Device-side preconditions that the host cannot see (slot ids, token
+ *    counts, ring positions) are checked in the kernels: a padding entry
+ *    (slot <= 0 or slot >= num_slots, [VD]) writes zero output rows and
+ *    touches no cache; an entry that breaks the ring contract is skipped the
+ *    same way and ORs a bit into *cache->status when status is not NULL.
+ */
+#ifndef SSU_H
+#define SSU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssu_dtype {
+  SSU_F32 = 0,
+  SSU_BF16 = 1,
+  SSU_F16 = 2,
+  SSU_FP8_E4M3 = 3 /* OCP e4m3fn codes (max 448) with an fp32 scale per state row */
+} ssu_dtype;
+
+typedef enum ssu_algo {
+  SSU_ALGO_AUTO = 0,     /* monolith below the work-unit threshold, split above [FI item 1] */
+  SSU_ALGO_MONOLITH = 1, /* one kernel per step */
+  SSU_ALGO_SPLIT = 2     /* precompute (C.B per group) + persistent replay kernel */
+} ssu_algo;
+
+enum {
+  SSU_OK = 0,
+  SSU_ERR_INVALID = -1,     /* bad argument: null pointer, shape, alignment, dtype */
+  SSU_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. headdim != 64) */
+  SSU_ERR_HIP = -3,         /* a HIP launch / runtime call failed */
+  SSU_ERR_WORKSPACE = -4    /* SPLIT chosen and workspace missing or too small */
+};
+
+/* Bits ORed into *ssu_cache.status by the kernels (device-side checks). */
+enum {
+  SSU_STATUS_BAD_PNAT = 1,   /* replay entry with pnat < 0 or pnat + T_b > ring_len */
+  SSU_STATUS_BAD_FOLD = 2,   /* flush entry with k < 0 or k > ring_len */
+  SSU_STATUS_BAD_SEQLEN = 4, /* varlen entry with T_b < 0 or T_b > max_seqlen */
+  SSU_STATUS_BAD_RING = 8    /* ring_start[slot] outside [0, ring_len) */
+};
+
+/*
+ * The per-slot cache [FI item 2; VD].  Inside one slot page every tensor is
+ * packed; *_slot_stride is the distance in BYTES between slot pages (it may
+ * include padding).  Layouts:
+ *   state       [slot][nheads][headdim][dstate]  state_dtype
+ *   state_scale [slot][nheads][headdim]          f32, fp8 state only: the row's
+ *                                                value is code * scale
+ *   x_cache     [slot][nheads][ring_len][headdim] io_dtype
+ *   B_cache     [slot][ngroups][ring_len][dstate] io_dtype
+ *   dt_cache    [slot][nheads][ring_len]          f32, holds dt' = softplus(dt + dt_bias)
+ *   ring_start  [slot]                            i32, in [0, ring_len)
+ * Live token j (j < pnat) of a slot is ring entry (ring_start + j) mod L; new
+ * token i is appended at (ring_start + pnat + i) mod L.
+ * Requirements: headdim == 64, dstate == 128, nheads % ngroups == 0,
+ * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer and slot stride
+ * 16-byte aligned.  status may be NULL.
+ */
+typedef struct ssu_cache {
+  int32_t num_slots, nheads, ngroups, headdim, dstate, ring_len;
+  ssu_dtype state_dtype;
+  ssu_dtype io_dtype;
+  void *state;
+  int64_t state_slot_stride;
+  float *state_scale;
+  int64_t scale_slot_stride;
+  void *x_cache;
+  int64_t x_slot_stride;
+  void *B_cache;
+  int64_t B_slot_stride;
+  float *dt_cache;
+  int64_t dt_slot_stride;
+  int32_t *ring_start;
+  int32_t *status;
+} ssu_cache;
+
+/*
+ * One decode step over `batch` entries [FI item 1-2; VD].
+ *   slot_idx, prev_num_accepted  [batch] i32   (prev_num_accepted = pnat, the
+ *                                               live ring tokens ahead of the
+ *                                               new ones)
+ *   cu_seqlens  [batch+1] i32 or NULL.  NULL: every entry has T = max_seqlen
+ *               new tokens and token t of entry b is row b*T + t.  Otherwise
+ *               entry b owns rows [cu_seqlens[b], cu_seqlens[b+1]) (varlen).
+ *   x   [rows][nheads][64]   io_dtype      B, C [rows][ngroups][128] io_dtype
+ *   dt  [rows][nheads] f32 (raw; softplus(dt + dt_bias) is applied here)
+ *   A, D, dt_bias  [nheads] f32
+ *   out [rows][nheads][64]   out_dtype (SSU_BF16 or SSU_F32)
+ *   workspace / workspace_bytes: scratch for SPLIT, at least
+ *               ssu_workspace_size(cache, batch, max_seqlen) bytes, 16-byte
+ *               aligned; may be NULL for MONOLITH.
+ * Requirements: 1 <= max_seqlen <= min(16, ring_len); pointers 16-byte
+ * aligned (dt, A, D, dt_bias: 4-byte).  Active slots must be unique.
+ */
+typedef struct ssu_step {
+  int32_t batch, max_seqlen;
+  const int32_t *slot_idx;
+  const int32_t *prev_num_accepted;
+  const int32_t *cu_seqlens;
+  const void *x;
+  const void *B;
+  const void *C;
+  const float *dt;
+  const float *A;
+  const float *D;
+  const float *dt_bias;
+  void *out;
+  ssu_dtype out_dtype;
+  void *workspace;
+  size_t workspace_bytes;
+  ssu_algo algo;
+} ssu_step;
+
+/* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen):
+ * the fp32 C.B products of every (entry, group).  Returns 0 for an invalid
+ * cache description. */
+size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen);
+
+/*
+ * Initialise n slots from FP32 prefill states [VD initialize_replayssm_state].
+ * states: device f32, entry j at states + j * states_batch_stride elements,
+ * each [nheads][64][128] packed; states_batch_stride == 0 broadcasts entry 0
+ * to every slot.  For each slot_idx[j] in [1, num_slots): encode the state
+ * (fp32 stored, bf16/fp16 round to nearest even, fp8 per row:
+ * scale = max|h| / 448 (1 if zero), code = nearest e4m3fn of h / scale),
+ * zero its x/B/dt rings and set ring_start to 0.  Other ids are ignored.
+ * slot ids must be unique.  n == 0 is a no-op.
+ */
+int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
+                   const int32_t *slot_idx, int32_t n, hipStream_t stream);
+
+/*
+ * One replay step [FI items 1-2; VD selective_state_update_replayssm].
+ * Per entry b and head h, with S = pnat + T_b combined tokens (live ring
+ * tokens then new tokens), dt'_s from the ring for s < pnat and
+ * softplus(dt + dt_bias[h]) for new ones, cumA_s = sum_{u<=s} A[h] dt'_u:
+ *   y_t = exp(cumA_t) C_t.h0 + sum_{s<=t} exp(cumA_t - cumA_s) dt'_s (C_t.B_s) x_s + D[h] x_t
+ * for every new token t, written to out.  The new tokens' x, B and dt' are
+ * appended to the ring.  The checkpoint and ring_start are not modified, so
+ * repeating a step with the same inputs gives the same result.
+ * Requires pnat + T_b <= ring_len per entry (else SSU_STATUS_BAD_PNAT).
+ */
+int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t stream);
+
+/*
+ * Flush [FI item 2 (host owns the ring); VP (FP32 flush, nearest-encoded FP8
+ * with FP32 row scales)].  For each j with slot = slot_idx[j] valid and
+ * k = num_fold[j] in [1, ring_len]: fold the first k live ring tokens into
+ * the checkpoint in fp32,
+ *   h <- exp(cumA_{k-1}) h + sum_{s<k} exp(cumA_{k-1} - cumA_s) dt'_s x_s B_s^T,
+ * re-encode it in state_dtype, then advance ring_start[slot] by k (mod L).
+ * k == 0 changes nothing.  A: [nheads] f32, the same A the steps use.
+ * The caller's next pnat for the slot is pnat + accepted - k.
+ */
+int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold,
+              const float *A, int32_t n, hipStream_t stream);
+
+/* The algorithm SSU_ALGO_AUTO resolves to for this step (MONOLITH or SPLIT),
+ * or a negative error code. */
+int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step);
+
+/* Work-unit threshold (batch * nheads) at or above which AUTO picks SPLIT.
+ * Process-wide; set_ returns the previous value. */
+int64_t ssu_get_split_threshold(void);
+int64_t ssu_set_split_threshold(int64_t work_units);
+
+/* The calling thread's last error message ("" if none). */
+const char *ssu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSU_H */

@@ -1,0 +1,221 @@
+"""Python binding of libssu (include/ssu.h): the checkpointing selective state
+update (ReplaySSM / MTP-replay SSU) on AMD MI355X.
+
+This module only marshals arguments: it builds the C descriptors from device
+tensors and calls the library.  Every step of the computation runs in the
+library's HIP kernels.  Importing fails loudly when libssu.so has not been
+built (python -m speculative_replay_state_amd.build); there is no fallback.
+
+Names follow the C ABI: ssu_init_state, ssu_replay_step, ssu_flush,
+ssu_workspace_size, ssu_resolve_algo, ssu_last_error, plus DeviceCache (the
+device tensors of one cache, in the layout of ssu_cache) and replay_step /
+flush / init_state helpers that take torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssu.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libssu.so is not built at %s; run `python -m speculative_replay_state_amd.build` "
+        "(needs ROCm hipcc)" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ssu_dtype / ssu_algo / return codes / status bits (include/ssu.h)
+SSU_F32, SSU_BF16, SSU_F16, SSU_FP8_E4M3 = 0, 1, 2, 3
+SSU_ALGO_AUTO, SSU_ALGO_MONOLITH, SSU_ALGO_SPLIT = 0, 1, 2
+SSU_OK, SSU_ERR_INVALID, SSU_ERR_UNSUPPORTED, SSU_ERR_HIP, SSU_ERR_WORKSPACE = 0, -1, -2, -3, -4
+SSU_STATUS_BAD_PNAT, SSU_STATUS_BAD_FOLD, SSU_STATUS_BAD_SEQLEN, SSU_STATUS_BAD_RING = 1, 2, 4, 8
+
+DTYPE_CODES = {"f32": SSU_F32, "bf16": SSU_BF16, "f16": SSU_F16, "fp8": SSU_FP8_E4M3}
+ALGO_CODES = {"auto": SSU_ALGO_AUTO, "monolith": SSU_ALGO_MONOLITH, "split": SSU_ALGO_SPLIT}
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+class SsuCache(ctypes.Structure):
+    _fields_ = [
+        ("num_slots", _I32), ("nheads", _I32), ("ngroups", _I32), ("headdim", _I32),
+        ("dstate", _I32), ("ring_len", _I32),
+        ("state_dtype", ctypes.c_int), ("io_dtype", ctypes.c_int),
+        ("state", _P), ("state_slot_stride", _I64),
+        ("state_scale", _P), ("scale_slot_stride", _I64),
+        ("x_cache", _P), ("x_slot_stride", _I64),
+        ("B_cache", _P), ("B_slot_stride", _I64),
+        ("dt_cache", _P), ("dt_slot_stride", _I64),
+        ("ring_start", _P), ("status", _P),
+    ]
+
+
+class SsuStep(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("max_seqlen", _I32),
+        ("slot_idx", _P), ("prev_num_accepted", _P), ("cu_seqlens", _P),
+        ("x", _P), ("B", _P), ("C", _P), ("dt", _P),
+        ("A", _P), ("D", _P), ("dt_bias", _P),
+        ("out", _P), ("out_dtype", ctypes.c_int),
+        ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("algo", ctypes.c_int),
+    ]
+
+
+_lib.ssu_workspace_size.restype = ctypes.c_size_t
+_lib.ssu_workspace_size.argtypes = [ctypes.POINTER(SsuCache), _I32, _I32]
+_lib.ssu_init_state.restype = ctypes.c_int
+_lib.ssu_init_state.argtypes = [ctypes.POINTER(SsuCache), _P, _I64, _P, _I32, _P]
+_lib.ssu_replay_step.restype = ctypes.c_int
+_lib.ssu_replay_step.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep), _P]
+_lib.ssu_flush.restype = ctypes.c_int
+_lib.ssu_flush.argtypes = [ctypes.POINTER(SsuCache), _P, _P, _P, _I32, _P]
+_lib.ssu_resolve_algo.restype = ctypes.c_int
+_lib.ssu_resolve_algo.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep)]
+_lib.ssu_get_split_threshold.restype = _I64
+_lib.ssu_get_split_threshold.argtypes = []
+_lib.ssu_set_split_threshold.restype = _I64
+_lib.ssu_set_split_threshold.argtypes = [_I64]
+_lib.ssu_last_error.restype = ctypes.c_char_p
+_lib.ssu_last_error.argtypes = []
+
+EXPORTED = ("ssu_workspace_size", "ssu_init_state", "ssu_replay_step", "ssu_flush",
+            "ssu_resolve_algo", "ssu_get_split_threshold", "ssu_set_split_threshold",
+            "ssu_last_error")
+
+
+class SsuError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("libssu error %d: %s" % (code, message))
+        self.code = code
+
+
+def ssu_last_error() -> str:
+    return (_lib.ssu_last_error() or b"").decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise SsuError(rc, ssu_last_error())
+    return rc
+
+
+# ---------------------------------------------------------------------------
+# raw C entry points (descriptor structs in, return code out)
+# ---------------------------------------------------------------------------
+
+def ssu_workspace_size(cache: SsuCache, batch: int, max_seqlen: int) -> int:
+    return int(_lib.ssu_workspace_size(ctypes.byref(cache), batch, max_seqlen))
+
+
+def ssu_init_state(cache: SsuCache, states: int, states_batch_stride: int, slot_idx: int, n: int,
+                   stream: int = 0) -> int:
+    return _lib.ssu_init_state(ctypes.byref(cache), states, states_batch_stride, slot_idx, n, stream)
+
+
+def ssu_replay_step(cache: SsuCache, step: SsuStep, stream: int = 0) -> int:
+    return _lib.ssu_replay_step(ctypes.byref(cache), ctypes.byref(step), stream)
+
+
+def ssu_flush(cache: SsuCache, slot_idx: int, num_fold: int, A: int, n: int, stream: int = 0) -> int:
+    return _lib.ssu_flush(ctypes.byref(cache), slot_idx, num_fold, A, n, stream)
+
+
+def ssu_resolve_algo(cache: SsuCache, step: SsuStep) -> int:
+    return _lib.ssu_resolve_algo(ctypes.byref(cache), ctypes.byref(step))
+
+
+def ssu_get_split_threshold() -> int:
+    return int(_lib.ssu_get_split_threshold())
+
+
+def ssu_set_split_threshold(work_units: int) -> int:
+    return int(_lib.ssu_set_split_threshold(work_units))
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor front end (argument marshalling only)
+# ---------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclasses.dataclass
+class DeviceCache:
+    """Device tensors of one cache in the ssu_cache layout.
+
+    Every per-slot tensor is a uint8 tensor [num_slots, slot_stride_bytes]
+    (the packed slot layout of include/ssu.h, plus optional padding);
+    ring_start is int32 [num_slots]; status is an optional int32 [1].
+    """
+    num_slots: int
+    nheads: int
+    ngroups: int
+    ring_len: int
+    state_dtype: str
+    state: object
+    scale: object
+    x_cache: object
+    B_cache: object
+    dt_cache: object
+    ring_start: object
+    status: object = None
+    headdim: int = 64
+    dstate: int = 128
+
+    def desc(self) -> SsuCache:
+        fp8 = self.state_dtype == "fp8"
+        return SsuCache(
+            self.num_slots, self.nheads, self.ngroups, self.headdim, self.dstate, self.ring_len,
+            DTYPE_CODES[self.state_dtype], SSU_BF16,
+            _ptr(self.state), self.state.stride(0),
+            _ptr(self.scale) if fp8 else None, self.scale.stride(0) if fp8 else 0,
+            _ptr(self.x_cache), self.x_cache.stride(0),
+            _ptr(self.B_cache), self.B_cache.stride(0),
+            _ptr(self.dt_cache), self.dt_cache.stride(0),
+            _ptr(self.ring_start), _ptr(self.status))
+
+
+def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
+                   out_dtype="bf16", workspace=None, algo="auto") -> SsuStep:
+    return SsuStep(
+        batch, max_seqlen, _ptr(slot_idx), _ptr(pnat), _ptr(cu_seqlens),
+        _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
+        _ptr(out), SSU_F32 if out_dtype == "f32" else SSU_BF16,
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        ALGO_CODES[algo])
+
+
+def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:
+    return ssu_workspace_size(cache.desc(), batch, max_seqlen)
+
+
+def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, stream=None):
+    """ssu_init_state with torch tensors (states f32 [n, H, 64, 128] on device)."""
+    n = slot_idx.numel()
+    if states_batch_stride is None:
+        states_batch_stride = states.stride(0) if n else 0
+    _check(ssu_init_state(cache.desc(), _ptr(states), states_batch_stride, _ptr(slot_idx), n,
+                          _stream(stream)))
+
+
+def replay_step(cache: DeviceCache, step: SsuStep, stream=None):
+    _check(ssu_replay_step(cache.desc(), step, _stream(stream)))
+
+
+def flush(cache: DeviceCache, slot_idx, num_fold, A, stream=None):
+    _check(ssu_flush(cache.desc(), _ptr(slot_idx), _ptr(num_fold), _ptr(A), slot_idx.numel(),
+                     _stream(stream)))

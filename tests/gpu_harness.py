@@ -1,0 +1,86 @@
+"""Helpers shared by the GPU tests: run the library on synth inputs and compare
+with the oracle.  Imported only by tests marked `gpu`."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import speculative_replay_state_amd as ssu
+import synth
+from synth import device as sd
+
+DEV = "cuda:0"
+
+
+def device_cache(spec: synth.CacheSpec, t: dict, with_status: bool = True) -> ssu.DeviceCache:
+    status = torch.zeros(1, dtype=torch.int32, device=DEV) if with_status else None
+    return ssu.DeviceCache(spec.num_slots, spec.nheads, spec.ngroups, spec.ring_len, spec.state_dtype,
+                           t["state"], t["scale"], t["x_cache"], t["B_cache"], t["dt_cache"],
+                           t["ring_start"], status, spec.headdim, spec.dstate)
+
+
+def out_tensor(step: synth.StepInputs, spec, out_dtype: str):
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    return torch.full((step.tokens, spec.nheads, spec.headdim), float("nan"), dtype=dt, device=DEV)
+
+
+def run_step(dc: ssu.DeviceCache, st: dict, step: synth.StepInputs, out, out_dtype: str, algo: str,
+             ws=None, stream=None):
+    if algo == "split" and ws is None:
+        nbytes = ssu.workspace_size(dc, step.batch, step.T)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=DEV)
+    desc = ssu.make_step_desc(step.batch, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"],
+                              st["x"], st["B"], st["C"], st["dt"], st["A"], st["D"], st["dt_bias"],
+                              out, out_dtype, ws, algo)
+    ssu.replay_step(dc, desc, stream)
+    return out
+
+
+def to_f64(out: torch.Tensor) -> np.ndarray:
+    return out.detach().to(torch.float64).cpu().numpy()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    if got.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+
+
+def tol_for(state_dtype: str, out_dtype: str) -> float:
+    """Parity bounds: 1e-4 (1 + |ref|) for fp32 state with fp32 output,
+    2e-2 (1 + |ref|) for bf16 / fp16 / fp8 state or bf16 output."""
+    return 1e-4 if (state_dtype == "f32" and out_dtype == "f32") else 2e-2
+
+
+def fp8_code_agreement(got: np.ndarray, ref: np.ndarray):
+    """(fraction equal, max distance in code steps) for e4m3fn codes; +-0 equal."""
+    g = got.astype(np.int32)
+    r = ref.astype(np.int32)
+
+    def ordinal(c):  # monotone index of the code value: sign-magnitude -> integer line
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+
+    og, orf = ordinal(g), ordinal(r)
+    same = og == orf
+    return float(same.mean()), int(np.max(np.abs(og - orf))) if og.size else 0
+
+
+def check_cache_after_step(spec, before: synth.CacheArrays, gpu: synth.CacheArrays,
+                           ref: synth.CacheArrays):
+    """Checkpoint untouched, x/B rings bit-exact with the oracle (appends are
+    copies), dt' appends within 1e-6 (1 + |ref|), everything else bit-exact,
+    including slot-padding canaries and ring_start."""
+    assert np.array_equal(gpu.state, before.state), "checkpoint modified by a replay step"
+    assert np.array_equal(gpu.scale, before.scale)
+    assert np.array_equal(gpu.x_cache, ref.x_cache), "x ring mismatch"
+    assert np.array_equal(gpu.B_cache, ref.B_cache), "B ring mismatch"
+    assert np.array_equal(gpu.ring_start, before.ring_start)
+    nb = spec.dt_bytes()
+    assert np.array_equal(gpu.dt_cache[:, nb:], ref.dt_cache[:, nb:])
+    g = gpu.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    r = ref.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    assert rel_err(g, r) <= 1e-6, "dt ring mismatch %g" % rel_err(g, r)
+    unchanged = ref.dt_cache[:, :nb].view(np.uint32) == before.dt_cache[:, :nb].view(np.uint32)
+    assert np.array_equal(gpu.dt_cache[:, :nb].view(np.uint32)[unchanged],
+                          before.dt_cache[:, :nb].view(np.uint32)[unchanged])
