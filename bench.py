@@ -1,0 +1,342 @@
+"""Benchmark of the ReplaySSM hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload fp8|prod|mtp|large|tiny]
+                    [--algo auto|monolith|split] [--batch B] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch: the replay step
+(dt' softplus, decay prefix, C.B, checkpoint replay and readout, ring appends)
+followed, for the fp8 workload, by the flush (fold of the accepted tokens,
+fp8 re-encode, ring_start advance).  The default workload is the quantised-
+checkpoint configuration: batch 256 of the cache's slots, 128 heads in 8
+groups, headdim 64, dstate 128, fp8 e4m3 checkpoint with fp32 row scales,
+T = 4 new tokens, a flush of k ~ U{1..4} tokens after every step.
+
+Inputs are synthetic, drawn on the GPU (synth package) and resident in HBM
+before timing.  To measure HBM rather than the 256 MB Infinity Cache the
+cache holds `--arenas` disjoint sets of `batch` slots (>= 2 GiB in total) and
+consecutive steps rotate through them.  The timed region replays a HIP graph
+of K steps between two stream synchronisations; per-kernel durations come
+from HIP events on the same stream.
+
+Prints one JSON line (metric, value = replayed tokens/s, roofline of the
+dominant kernel, CPU-oracle baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "replayed SSU tokens/sec and achieved HBM GB/s (% of MI355X peak) at 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+WORKLOADS = {
+    "fp8": dict(nheads=128, ngroups=8, state_dtype="fp8", batch=256, T=4, pnat_max=0, out="bf16",
+                flush=(1, 4), varlen=False, slot_pad=0,
+                desc="fp8 e4m3 checkpoint + f32 row scales, batch 256, H128 G8, P64 N128, T=4, "
+                     "replay step + flush k~U{1..4} every step, L=16"),
+    "prod": dict(nheads=128, ngroups=8, state_dtype="f16", batch=256, T=8, pnat_max=8, out="bf16",
+                 flush=None, varlen=False, slot_pad=0,
+                 desc="production MTP decode, fp16 checkpoint, H128 G8, P64 N128, T=8, pnat~U{0..8}, "
+                      "L=16, ring_start~U{0..15}"),
+    "mtp": dict(nheads=64, ngroups=8, state_dtype="bf16", batch=64, T=4, pnat_max=4, out="bf16",
+                flush=None, varlen=False, slot_pad=0,
+                desc="MTP decode, bf16 checkpoint, batch 64, H64 G8, P64 N128, T=4, pnat~U{0..4}, L=16"),
+    "large": dict(nheads=128, ngroups=8, state_dtype="bf16", batch=1024, T=8, pnat_max=8, out="bf16",
+                  flush=None, varlen=True, slot_pad=256,
+                  desc="large batch, bf16 checkpoint, 1024 active slots, H128 G8, P64 N128, varlen "
+                       "T_b~U{1..8}, pnat~U{0..8}, L=16, 256 B padding between slot pages"),
+    "tiny": dict(nheads=8, ngroups=1, state_dtype="f32", batch=2, T=1, pnat_max=8, out="f32",
+                 flush=None, varlen=False, slot_pad=0,
+                 desc="tiny reference, fp32 checkpoint, batch 2, H8 G1, T=1"),
+}
+
+ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
+
+
+def step_bytes(spec, H, G, pnat, Tb):
+    """Algorithmic HBM bytes of one replay step (sum over entries): checkpoint
+    (+ fp8 row scales) read, live-ring x/B/dt' read, new x/B/C/dt read, out
+    written, x/B/dt' appended.  Scratch traffic of the split is excluded."""
+    P, N = 64, 128
+    per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
+    tot = 0
+    for p, t in zip(pnat, Tb):
+        tot += per_state
+        tot += p * (H * P * 2 + G * N * 2 + H * 4)              # live ring reads
+        tot += t * (H * P * 2 + 2 * G * N * 2 + H * 4)          # new x, B, C, dt
+        tot += t * H * P * 2                                    # out (bf16)
+        tot += t * (H * P * 2 + G * N * 2 + H * 4)              # appends
+    return tot
+
+
+def flush_bytes(spec, H, G, k):
+    """Algorithmic bytes of one flush: checkpoint read + write and the k ring
+    tokens (x, B, dt') read, per entry with k > 0."""
+    P, N = 64, 128
+    per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
+    return int(sum(2 * per_state + kk * (H * P * 2 + G * N * 2 + H * 4) for kk in k if kk > 0))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--algo", default="auto", choices=["auto", "monolith", "split"])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--arenas", type=int, default=None, help="disjoint slot sets rotated per step")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--seed", type=int, default=1234)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ReplaySSM step has no cross-GPU exchange "
+              "(slots and heads shard without communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import speculative_replay_state_amd as ssu
+    import synth
+    from synth import device as sd
+
+    wl = dict(WORKLOADS[args.workload])
+    if args.batch:
+        wl["batch"] = args.batch
+    batch, H, G, T = wl["batch"], wl["nheads"], wl["ngroups"], wl["T"]
+    dev = "cuda:0"
+
+    # --- cache with rotating arenas (HBM, not the Infinity Cache) -----------
+    probe = synth.CacheSpec(num_slots=2, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
+                            slot_pad=wl["slot_pad"])
+    st_ = probe.strides()
+    slot_bytes = sum(st_.values())
+    if args.arenas is None:
+        arenas = max(1, math.ceil(2.2 * 2 ** 30 / (slot_bytes * batch)))
+        if args.workload == "large":
+            arenas = 2  # 2048 slots: 1024 active at a time, ~4.6 GB of checkpoints
+    else:
+        arenas = args.arenas
+    num_slots = arenas * batch + 1
+    spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
+                           slot_pad=wl["slot_pad"])
+    tcache = sd.make_cache_device(spec, args.seed, dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dc = ssu.DeviceCache(num_slots, H, G, spec.ring_len, spec.state_dtype, tcache["state"],
+                         tcache["scale"], tcache["x_cache"], tcache["B_cache"], tcache["dt_cache"],
+                         tcache["ring_start"], status)
+
+    rng = np.random.default_rng(args.seed)
+    perm = rng.permutation(np.arange(1, num_slots, dtype=np.int32))
+    steps_in, tsteps, flush_k, descs = [], [], [], []
+    out_dt = torch.float32 if wl["out"] == "f32" else torch.bfloat16
+    for a in range(arenas):
+        slots = np.sort(perm[a * batch:(a + 1) * batch]).astype(np.int32)
+        stp = synth.make_step(spec, batch, T, args.seed + 17 * a + 1, wl["pnat_max"], varlen=wl["varlen"],
+                              slots=slots, pnat_fixed=0 if wl["pnat_max"] == 0 else None)
+        steps_in.append(stp)
+        t = sd.upload_step(stp, dev)
+        t["out"] = torch.empty((stp.tokens, H, 64), dtype=out_dt, device=dev)
+        tsteps.append(t)
+        if wl["flush"]:
+            k = synth.flush_counts(batch, wl["flush"][0], wl["flush"][1], args.seed + 31 * a + 5)
+            flush_k.append(torch.from_numpy(k).to(dev))
+    ws = None
+    algo_used = args.algo
+    d0 = ssu.make_step_desc(batch, T, tsteps[0]["slot_idx"], tsteps[0]["pnat"], tsteps[0]["cu_seqlens"],
+                            tsteps[0]["x"], tsteps[0]["B"], tsteps[0]["C"], tsteps[0]["dt"],
+                            tsteps[0]["A"], tsteps[0]["D"], tsteps[0]["dt_bias"], tsteps[0]["out"],
+                            wl["out"], None, args.algo)
+    resolved = ssu.ssu_resolve_algo(dc.desc(), d0)
+    algo_used = {ssu.SSU_ALGO_MONOLITH: "monolith", ssu.SSU_ALGO_SPLIT: "split"}[resolved]
+    if algo_used == "split":
+        ws = torch.empty(ssu.workspace_size(dc, batch, T) // 4 + 1, dtype=torch.float32, device=dev)
+    for t in tsteps:
+        descs.append(ssu.make_step_desc(batch, T, t["slot_idx"], t["pnat"], t["cu_seqlens"], t["x"],
+                                        t["B"], t["C"], t["dt"], t["A"], t["D"], t["dt_bias"], t["out"],
+                                        wl["out"], ws, algo_used))
+    cdesc = dc.desc()
+
+    def one_step(i, ev=None):
+        stream = torch.cuda.current_stream()  # the capture stream inside torch.cuda.graph
+        sh = stream.cuda_stream
+        a = i % arenas
+        if ev is not None:
+            ev[0].record(stream)
+        rc = ssu.ssu_replay_step(cdesc, descs[a], sh)
+        if rc:
+            raise ssu.SsuError(rc, ssu.ssu_last_error())
+        if ev is not None:
+            ev[1].record(stream)
+        if wl["flush"]:
+            t = tsteps[a]
+            rc = ssu.ssu_flush(cdesc, t["slot_idx"].data_ptr(), flush_k[a].data_ptr(), t["A"].data_ptr(),
+                               batch, sh)
+            if rc:
+                raise ssu.SsuError(rc, ssu.ssu_last_error())
+            if ev is not None:
+                ev[2].record(stream)
+
+    # --- warmup (eager), then capture K steps in a graph --------------------
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d after warmup" % int(status.item()))
+
+    K = args.steps
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                one_step(args.warmup + i)
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            one_step(args.warmup + i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / K
+
+    # --- per-kernel durations (HIP events around each call, same stream) ----
+    nrep = min(K, 8 * arenas)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nrep)]
+    torch.cuda.synchronize()
+    for i in range(nrep):
+        one_step(i, evs[i])
+    torch.cuda.synchronize()
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    flush_ms = [e[1].elapsed_time(e[2]) for e in evs] if wl["flush"] else []
+
+    tokens_per_step = float(np.mean([s.tokens for s in steps_in]))
+    sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat if s.pnat is not None else [0] * batch,
+                                       np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch)
+                            for s in steps_in]))
+    fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy()) for k in flush_k])) if flush_k else 0.0
+    step_avg = float(np.mean(step_ms))
+    kernels = {"replay_step": {"algo": algo_used, "avg_us": 1e3 * step_avg, "bytes": sbytes,
+                               "GBps": sbytes / (step_avg * 1e6)}}
+    dominant = "replay_step"
+    if flush_ms:
+        fl_avg = float(np.mean(flush_ms))
+        kernels["flush"] = {"avg_us": 1e3 * fl_avg, "bytes": fbytes, "GBps": fbytes / (fl_avg * 1e6)}
+        if fl_avg > step_avg:
+            dominant = "flush"
+    dk = kernels[dominant]
+    achieved = dk["GBps"]
+    value = tokens_per_step * K / (ms_total * 1e-3)
+
+    # --- counter calibration copy (1 GiB), only when asked ------------------
+    if args.calib_copy:
+        src = torch.empty(2 ** 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # --- CPU oracle on a bounded sample of the same workload ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, wl, spec, tcache, steps_in, flush_k)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, drawn on the GPU; no dataset)",
+        "config": {
+            "workload": args.workload + ": " + wl["desc"],
+            "batch": batch, "nheads": H, "ngroups": G, "headdim": 64, "dstate": 128, "ring_len": 16,
+            "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "algo": algo_used,
+            "arenas": arenas, "cache_slots": num_slots, "graph": graph is not None,
+            "tokens_per_step": tokens_per_step,
+            "algorithmic_bytes_per_step": sbytes + fbytes,
+            "achieved_GBps_step": (sbytes + fbytes) / (ms_per_step * 1e6),
+            "wall_s_timed": wall1 - wall0,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
+    """The CPU oracle (as it stands) on a bounded sample: the first 64 entries
+    of the first arena, step (+ flush), repeated until --cpu-seconds of work."""
+    from oracle import ssu_oracle as O
+    from synth import device as sd
+
+    step = steps_in[0]
+    n = min(64, step.batch)
+    entries = list(range(n))
+    slots = [int(step.slot_idx[b]) for b in entries]
+    host, smap = sd.download_subset(spec, tcache, slots)
+    sub = sd.subset_step(step, entries, smap)
+    k = flush_k[0].cpu().numpy()[:n] if flush_k else None
+    tokens = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        c = host.copy()
+        O.replay_step(c, sub)
+        if k is not None:
+            O.flush(c, sub.slot_idx, k, sub.A)
+        tokens += sub.tokens
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or reps >= 1000:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d entries of the first batch, step%s, repeated %d times (%.1f s)" % (
+                n, step.batch, " + flush" if k is not None else "", reps, el)}
+
+
+if __name__ == "__main__":
+    main()
