@@ -71,6 +71,7 @@ def step_bytes(spec, H, G, pnat, Tb):
     per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
     tot = 0
     for p, t in zip(pnat, Tb):
+        p, t = int(p), int(t)
         tot += per_state
         tot += p * (H * P * 2 + G * N * 2 + H * 4)              # live ring reads
         tot += t * (H * P * 2 + 2 * G * N * 2 + H * 4)          # new x, B, C, dt
@@ -84,7 +85,7 @@ def flush_bytes(spec, H, G, k):
     tokens (x, B, dt') read, per entry with k > 0."""
     P, N = 64, 128
     per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
-    return int(sum(2 * per_state + kk * (H * P * 2 + G * N * 2 + H * 4) for kk in k if kk > 0))
+    return int(sum(2 * per_state + int(kk) * (H * P * 2 + G * N * 2 + H * 4) for kk in k if kk > 0))
 
 
 def main():

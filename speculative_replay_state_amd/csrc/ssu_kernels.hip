@@ -137,35 +137,6 @@ __device__ __forceinline__ float fp8_row_scale(float m) {
   return sc > 0.0f ? sc : 1.0f;
 }
 
-// fp32(v / sc) exactly as IEEE division rounds it.  y must be fp32(1 / sc).
-// For sc in [2^-60, 2^100] one residual step corrects the product v * y
-// (Markstein's correction theorem: y correctly rounded, v * y within one ulp);
-// outside that range the plain division is used.
-__device__ __forceinline__ float div_by_scale(float v, float sc, float y, bool fast) {
-  if (fast) {
-    float q0 = v * y;
-    float r = fmaf(-q0, sc, v);
-    return fmaf(r, y, q0);
-  }
-  return v / sc;
-}
-
-// Encode 8 fp32 values of one row into 8 e4m3fn codes: nearest of
-// clamp(v / sc, -448, 448).
-__device__ __forceinline__ u32x2 fp8_encode8(const float *v, float sc, float y) {
-  const bool fast = sc >= 0x1p-60f && sc <= 0x1p100f;
-  float qv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    qv[e] = __builtin_amdgcn_fmed3f(div_by_scale(v[e], sc, y, fast), -448.0f, 448.0f);
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-  u32x2 r = {(uint32_t)w0, (uint32_t)w1};
-  return r;
-}
-
 // Blocks are dispatched round-robin over the 8 XCDs; remap so that runs of
 // consecutive logical blocks (which share an entry's B/C rows) stay on one
 // XCD's L2.
@@ -221,15 +192,66 @@ __device__ __forceinline__ Entry load_entry(const KCache &c, const KStep &s, int
 }
 
 // ---------------------------------------------------------------------------
+// Combined-window geometry.  KW is the capacity of the combined window
+// (live ring tokens + new tokens, S <= L <= KW): 16 for rings up to 16
+// entries, else 32.  It is the K depth of the replay-term MFMA
+// (v_mfma_f32_16x16x16_bf16 or ..._16x16x32_bf16), so lane (i, q) holds the
+// coefficients of window positions s = kE q .. kE q + kE - 1.
+// ---------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int KW>
+struct Win;
+template <>
+struct Win<16> {
+  static constexpr int kE = 4;        // window positions per lane in the MFMA operands
+  static constexpr int kRounds = 2;   // 16-byte x loads per lane to cover the window
+  static constexpr int kXS = 20;      // LDS row stride (bf16) of the transposed window
+  static constexpr int kSigBits = 4;  // lane -> (s = l % 16, chunk = l / 16 + 4 jj)
+  typedef bf16x4 V;
+};
+template <>
+struct Win<32> {
+  static constexpr int kE = 8;
+  static constexpr int kRounds = 4;
+  static constexpr int kXS = 40;
+  static constexpr int kSigBits = 5;  // lane -> (s = l % 32, chunk = l / 32 + 2 jj)
+  typedef bf16x8 V;
+};
+
+template <int KW>
+__device__ __forceinline__ f32x4 mfma_win(typename Win<KW>::V a, typename Win<KW>::V b, f32x4 c) {
+  if constexpr (KW == 16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                      c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over lanes 0..KW-1 (Hillis-Steele).
+template <int KW>
+__device__ __forceinline__ float scan_win(float v, int lane) {
+#pragma unroll
+  for (int d = 1; d < KW; d <<= 1) {
+    const float t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
 // C.B of one (entry, group): CB[i][s] = sum_n C_i[n] B_s[n] for new token i
-// and combined index s (ring tokens, then new tokens), as two 16x16 MFMA
-// tiles.  Rows i >= T_b and columns s >= S come out zero.  On return lane l
+// and combined index s (ring tokens, then new tokens), as KW/16 MFMA tiles of
+// 16x16.  Rows i >= T_b and columns s >= S come out zero.  On return lane l
 // holds cb[nb][j] = CB[4*(l/16) + j][16*nb + l%16].  Optionally appends this
 // step's B rows to the group's ring (one writer per (entry, group)).
 // ---------------------------------------------------------------------------
 
+template <int KW>
 __device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, const Entry &e, int g,
-                                           bool append_B, int lane, f32x4 cb[2]) {
+                                           bool append_B, int lane, f32x4 cb[KW / 16]) {
   const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
   const bf16x8 zero8 = {};
   bf16x8 ca[4];
@@ -240,7 +262,7 @@ __device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, cons
   uint16_t *Bring = reinterpret_cast<uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
                     (int64_t)g * L * kDState;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < KW / 16; ++nb) {
     const int sig = nb * 16 + m;
     u32x4 bw[4] = {};
     if (sig < S) {
@@ -288,186 +310,6 @@ __device__ __forceinline__ void store_out(const KStep &s, int H, const Entry &e,
   }
 }
 
-// ---------------------------------------------------------------------------
-// The replay of one (entry, head) by one wave.  cb points at CB[0][0] of this
-// (entry, group) with row stride cbs floats (LDS in the monolith, the scratch
-// buffer in the split).  xT is this wave's LDS tile for the transposed x
-// window.
-// ---------------------------------------------------------------------------
-
-template <int ST, int OT>
-__device__ __forceinline__ void head_replay(const KCache &c, const KStep &s, const Entry &e, int h,
-                                            const float *cb, int cbs, uint16_t *xT, int lane) {
-  const int m = lane & 15, q = lane >> 4;
-  const int H = c.H, L = c.L, g = h / c.hpg, S = e.pnat + e.Tb;
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  constexpr int kRowBytes = kDState * kEB;
-  constexpr int NLD = kRowBytes / 64;  // 16-byte loads per lane per 16-row block
-  const uint8_t *hp =
-      c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
-
-  // 1. checkpoint tile (the bulk of the bytes): issued first.  Lane (m, q)
-  //    loads row 16 rb + m, bytes [64 u + 16 q, +16) of it.
-  u32x4 raw[4][NLD];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) raw[rb][u] = ld16(hp + (rb * 16 + m) * kRowBytes + u * 64 + q * 16);
-  f32x4 rscale[4];
-  if constexpr (ST == kFP8) {
-    const float *sp = reinterpret_cast<const float *>(c.scale + (int64_t)e.slot * c.scale_stride) +
-                      h * kHeadDim;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) rscale[rb] = *reinterpret_cast<const f32x4 *>(sp + rb * 16 + 4 * q);
-  }
-
-  // 2. C of token i = m, laid out to match the state tile's k order.
-  const bool tok_ok = m < e.Tb;
-  const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 craw[4];
-  float cf32[32];
-  if constexpr (ST == kBF16 || ST == kF16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) craw[u] = tok_ok ? ld16(Crow + 32 * u + 8 * q) : zero4;  // n = 32u + 8q + e
-  } else if constexpr (ST == kFP8) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)  // k step 2u + hh: n = 64u + 16q + 8hh + e
-        craw[2 * u + hh] = tok_ok ? ld16(Crow + 64 * u + 16 * q + 8 * hh) : zero4;
-  } else {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {  // k step 4u + e: n = 16u + 4q + e
-      u32x2 v = tok_ok ? ld8(Crow + 16 * u + 4 * q) : u32x2{0u, 0u};
-      cf32[4 * u + 0] = bf2f(v[0] & 0xFFFFu);
-      cf32[4 * u + 1] = bf2f(v[0] >> 16);
-      cf32[4 * u + 2] = bf2f(v[1] & 0xFFFFu);
-      cf32[4 * u + 3] = bf2f(v[1] >> 16);
-    }
-  }
-
-  // 3. dt' of the combined window, one position per lane; new positions are
-  //    appended to the dt ring.  Then the inclusive decay prefix.
-  float dtp = 0.f;
-  float *dtring = reinterpret_cast<float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
-  if (lane < S) {
-    const int pos = ring_pos(e.r, lane, L);
-    if (lane < e.pnat) {
-      dtp = dtring[pos];
-    } else {
-      const float v = s.dt[(int64_t)(e.bos + lane - e.pnat) * H + h] + s.dt_bias[h];
-      dtp = softplus_f(v);
-      dtring[pos] = dtp;
-    }
-  }
-  const float cum = scan32(s.A[h] * dtp, lane);
-
-  // 4. x window -> LDS, transposed to xT[p][s]; new tokens appended to the x
-  //    ring.  Positions s >= S are zero.
-  uint16_t *xring = reinterpret_cast<uint16_t *>(c.xc + (int64_t)e.slot * c.x_stride) +
-                    (int64_t)h * L * kHeadDim;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int sig = lane & 31, pc = 2 * jj + (lane >> 5);
-    u32x4 v = zero4;
-    if (sig < S) {
-      uint16_t *rp = xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8;
-      if (sig < e.pnat) {
-        v = ld16(rp);
-      } else {
-        v = ld16(s.x + ((int64_t)(e.bos + sig - e.pnat) * H + h) * kHeadDim + pc * 8);
-        st16(rp, v);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      xT[(pc * 8 + t) * kXS + sig] = (uint16_t)((t & 1) ? (v[t >> 1] >> 16) : (v[t >> 1] & 0xFFFFu));
-  }
-
-  // 5. replay coefficients W[i][s] for s = 8q + t (the B operand of the x
-  //    MFMA), and the checkpoint decay beta_i = exp(cumA_{pnat+i}).
-  const int ti = e.pnat + m;
-  const float ct = __shfl(cum, ti < 32 ? ti : 31, 64);
-  const float beta = tok_ok ? expf(ct) : 0.f;
-  f32x4 cb0 = {0.f, 0.f, 0.f, 0.f}, cb1 = cb0;
-  if (tok_ok) {
-    cb0 = *reinterpret_cast<const f32x4 *>(cb + m * cbs + 8 * q);
-    cb1 = *reinterpret_cast<const f32x4 *>(cb + m * cbs + 8 * q + 4);
-  }
-  const float Dh = s.D[h];
-  bf16x8 whi, wlo, wlo2;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int sig = 8 * q + t;
-    const float cs = __shfl(cum, sig, 64);
-    const float ds = __shfl(dtp, sig, 64);
-    const float cbv = t < 4 ? cb0[t] : cb1[t - 4];
-    float w = 0.f;
-    if (tok_ok && sig <= ti) w = expf(ct - cs) * ds * cbv;
-    if (tok_ok && sig == ti) w += Dh;
-    const __bf16 hi = (__bf16)w;
-    const float r1 = w - (float)hi;
-    const __bf16 lo = (__bf16)r1;
-    whi[t] = hi;
-    wlo[t] = lo;
-    if constexpr (ST == kF32) wlo2[t] = (__bf16)(r1 - (float)lo);
-  }
-  wave_sync();  // xT written by this wave -> read below
-
-  // 6. checkpoint readout: acc[rb][j] = sum_n h0[16 rb + 4 q + j][n] C_i[n]
-  f32x4 acc[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (ST == kBF16) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        a = mfma_bf16(__builtin_bit_cast(bf16x8, raw[rb][u]), __builtin_bit_cast(bf16x8, craw[u]), a);
-    } else if constexpr (ST == kF16) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        a = mfma_f16(__builtin_bit_cast(f16x8, raw[rb][u]), bf16x8_to_f16x8(craw[u]), a);
-    } else if constexpr (ST == kFP8) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x2 d0 = fp8x4_to_bf16(raw[rb][u][0]), d1 = fp8x4_to_bf16(raw[rb][u][1]);
-        const u32x2 d2 = fp8x4_to_bf16(raw[rb][u][2]), d3 = fp8x4_to_bf16(raw[rb][u][3]);
-        const u32x4 lo = {d0[0], d0[1], d1[0], d1[1]}, hi = {d2[0], d2[1], d3[0], d3[1]};
-        a = mfma_bf16(__builtin_bit_cast(bf16x8, lo), __builtin_bit_cast(bf16x8, craw[2 * u]), a);
-        a = mfma_bf16(__builtin_bit_cast(bf16x8, hi), __builtin_bit_cast(bf16x8, craw[2 * u + 1]), a);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a = mfma_f32(__uint_as_float(raw[rb][u][t]), cf32[4 * u + t], a);
-    }
-    acc[rb] = a;
-  }
-
-  // 7. epilogue: decay to the token (and fp8 row scale), then add the ring /
-  //    new-token replay terms through the x MFMA.
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (ST == kFP8)
-        acc[rb][j] = (acc[rb][j] * rscale[rb][j]) * beta;
-      else
-        acc[rb][j] = acc[rb][j] * beta;
-    }
-    const bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xT + (rb * 16 + m) * kXS + 8 * q);
-    acc[rb] = mfma_bf16(xa, whi, acc[rb]);
-    acc[rb] = mfma_bf16(xa, wlo, acc[rb]);
-    if constexpr (ST == kF32) acc[rb] = mfma_bf16(xa, wlo2, acc[rb]);
-  }
-  wave_sync();  // xT reads done before the tile is reused
-
-  // 8. output rows of the new tokens
-  store_out<OT>(s, H, e, h, lane, acc);
-}
-
 template <int OT>
 __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry &e, int h, int lane) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -476,97 +318,428 @@ __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry
 }
 
 // ---------------------------------------------------------------------------
-// MONOLITH: one workgroup per (entry, group, head tile).  Wave 0 forms C.B
-// for the group in LDS; every wave then replays heads of the tile.
+// The replay of one (entry, head) by one wave, in two phases so that a wave
+// can have the next head's loads in flight while this one computes:
+//   load_head  -- every global load of the head: the checkpoint tile (the
+//                 bulk of the bytes), C of the group's new tokens, the C.B row
+//                 of token i, the dt / x window and the fp8 row scales;
+//   head_compute -- softplus, decay prefix, appends, W, MFMAs, output.
 // ---------------------------------------------------------------------------
 
-template <int ST, int OT>
-__global__ __launch_bounds__(kWaves * 64) void replay_monolith_kernel(KCache c, KStep s, int nht) {
-  __shared__ float cb_lds[kMaxTokens * kCbLds];
-  __shared__ uint16_t xT_all[kWaves][kHeadDim * kXS];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int ht = bid % nht, bg = bid / nht;
-  const int g = bg % c.G, b = bg / c.G;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const Entry e = load_entry(c, s, b, g == 0 && ht == 0 && wave == 0);
-  if (e.mode == 0) return;  // uniform over the workgroup
-  const int HT = c.hpg / nht, hbase = g * c.hpg + ht * HT;
-  if (e.mode == 1) {
-    for (int hl = wave; hl < HT; hl += kWaves) zero_out_head<OT>(s, c.H, e, hbase + hl, lane);
-    return;
-  }
-  if (wave == 0) {
-    f32x4 cb[2];
-    compute_cb(c, s, e, g, ht == 0, lane, cb);
-    const int m = lane & 15, q = lane >> 4;
+// Per-head loads, prefetched one head ahead: the checkpoint tile (the bulk of
+// the bytes), the dt and x windows, and the fp8 row scales.
+template <int ST, int KW>
+struct HeadLoads {
+  static constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
+  static constexpr int kRowBytes = kDState * kEB;
+  static constexpr int kNLD = kRowBytes / 64;  // 16-byte checkpoint loads per lane per 16-row block
+  u32x4 raw[4][kNLD];                        // lane (m, q): bytes [64 u + 16 q, +16) of row 16 rb + m
+  u32x4 xw[Win<KW>::kRounds];                // x window chunks
+  f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
+  float dtv;                                 // lane s: stored dt' (s < pnat) or dt + dt_bias (new)
+};
+
+// Per-(entry, group) loads: C of the new tokens and the C.B row of token m.
+template <int ST, int KW>
+struct ItemLoads {
+  u32x4 craw[4];       // C of token m in the tile's k order (bf16 / f16 / fp8 state)
+  float cf32[32];      // C of token m for the fp32 tile
+  f32x4 cbr[KW / 16];  // C.B[m][kE q .. kE q + kE - 1]
+};
+
+template <int ST, int KW>
+__device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
+                                          HeadLoads<ST, KW> &ld) {
+  using T = HeadLoads<ST, KW>;
+  using WC = Win<KW>;
+  const int m = lane & 15, q = lane >> 4;
+  const int H = c.H, L = c.L, S = e.pnat + e.Tb;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * T::kEB);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cb_lds[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
+    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16(hp + (rb * 16 + m) * T::kRowBytes + u * 64 + q * 16);
+  if constexpr (ST == kFP8) {
+    const float *sp = reinterpret_cast<const float *>(c.scale + (int64_t)e.slot * c.scale_stride) +
+                      h * kHeadDim;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) ld.rscale[rb] = *reinterpret_cast<const f32x4 *>(sp + rb * 16 + 4 * q);
   }
-  __syncthreads();
-  for (int hl = wave; hl < HT; hl += kWaves)
-    head_replay<ST, OT>(c, s, e, hbase + hl, cb_lds, kCbLds, xT_all[wave], lane);
+  ld.dtv = 0.f;
+  if (lane < S) {
+    if (lane < e.pnat) {
+      const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
+      ld.dtv = dtring[ring_pos(e.r, lane, L)];
+    } else {
+      ld.dtv = s.dt[(int64_t)(e.bos + lane - e.pnat) * H + h] + s.dt_bias[h];
+    }
+  }
+  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)e.slot * c.x_stride) +
+                          (int64_t)h * L * kHeadDim;
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sig = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    ld.xw[jj] = zero4;
+    if (sig < S)
+      ld.xw[jj] = sig < e.pnat
+                      ? ld16(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8)
+                      : ld16(s.x + ((int64_t)(e.bos + sig - e.pnat) * H + h) * kHeadDim + pc * 8);
+  }
+}
+
+template <int ST, int KW>
+__device__ __forceinline__ void load_item_c(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
+                                            ItemLoads<ST, KW> &il) {
+  const int m = lane & 15, q = lane >> 4;
+  const bool tok_ok = m < e.Tb;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
+  if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) il.craw[u] = tok_ok ? ld16(Crow + 32 * u + 8 * q) : zero4;  // n = 32u + 8q + e
+  } else if constexpr (ST == kF16) {
+    // C as f16 (exact for |C| in the f16 normal range), converted once per item
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      il.craw[u] = __builtin_bit_cast(u32x4, bf16x8_to_f16x8(tok_ok ? ld16(Crow + 32 * u + 8 * q) : zero4));
+  } else if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)  // k step 2u + hh: n = 64u + 16q + 8hh + e
+        il.craw[2 * u + hh] = tok_ok ? ld16(Crow + 64 * u + 16 * q + 8 * hh) : zero4;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // k step 4u + e: n = 16u + 4q + e
+      const u32x2 v = tok_ok ? ld8(Crow + 16 * u + 4 * q) : u32x2{0u, 0u};
+      il.cf32[4 * u + 0] = bf2f(v[0] & 0xFFFFu);
+      il.cf32[4 * u + 1] = bf2f(v[0] >> 16);
+      il.cf32[4 * u + 2] = bf2f(v[1] & 0xFFFFu);
+      il.cf32[4 * u + 3] = bf2f(v[1] >> 16);
+    }
+  }
+}
+
+// The C.B row of token m from a [16][cbs] fp32 table (LDS or the scratch).
+template <int ST, int KW>
+__device__ __forceinline__ void load_cb_row(const Entry &e, const float *cb, int cbs, int lane,
+                                            ItemLoads<ST, KW> &il) {
+  const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int v = 0; v < KW / 16; ++v)
+    il.cbr[v] = m < e.Tb ? *reinterpret_cast<const f32x4 *>(cb + m * cbs + Win<KW>::kE * q + 4 * v)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int ST, int OT, int KW>
+__device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, const Entry &e, int h,
+                                             const HeadLoads<ST, KW> &ld, const ItemLoads<ST, KW> &il,
+                                             uint16_t *xT, int lane) {
+  using WC = Win<KW>;
+  using V = typename WC::V;
+  const int m = lane & 15, q = lane >> 4;
+  const int H = c.H, L = c.L, S = e.pnat + e.Tb;
+  const bool tok_ok = m < e.Tb;
+
+  // 1. dt' of the combined window (lane = combined index); new positions are
+  //    softplus'd and appended to the dt ring.  Then the inclusive decay prefix.
+  float dtp = ld.dtv;
+  if (lane >= e.pnat && lane < S) {
+    dtp = softplus_f(ld.dtv);
+    float *dtring = reinterpret_cast<float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
+    dtring[ring_pos(e.r, lane, L)] = dtp;
+  }
+  const float cum = scan_win<KW>(s.A[h] * dtp, lane);
+
+  // 2. x window -> LDS, transposed to xT[p][s]; new tokens appended to the x
+  //    ring.  Positions s >= S hold zeros.
+  uint16_t *xring = reinterpret_cast<uint16_t *>(c.xc + (int64_t)e.slot * c.x_stride) +
+                    (int64_t)h * L * kHeadDim;
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sig = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    const u32x4 v = ld.xw[jj];
+    if (sig >= e.pnat && sig < S) st16(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8, v);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      xT[(pc * 8 + tt) * WC::kXS + sig] = (uint16_t)((tt & 1) ? (v[tt >> 1] >> 16) : (v[tt >> 1] & 0xFFFFu));
+  }
+
+  // 3. replay coefficients W[i][s] for s = kE q + t (the B operand of the x
+  //    MFMA, split into bf16 hi + lo (+ lo2 for fp32 state) parts), and the
+  //    checkpoint decay beta_i = exp(cumA_{pnat+i}).
+  const int ti = e.pnat + m;
+  const float ct = __shfl(cum, ti < KW ? ti : KW - 1, 64);
+  const float beta = tok_ok ? expf(ct) : 0.f;
+  const float Dh = s.D[h];
+  V whi, wlo, wlo2;
+#pragma unroll
+  for (int tt = 0; tt < WC::kE; ++tt) {
+    const int sig = WC::kE * q + tt;
+    const float cs = __shfl(cum, sig, 64);
+    const float ds = __shfl(dtp, sig, 64);
+    const float cbv = il.cbr[tt >> 2][tt & 3];
+    float w = 0.f;
+    if (tok_ok && sig <= ti) w = expf(ct - cs) * ds * cbv;
+    if (tok_ok && sig == ti) w += Dh;
+    const __bf16 hi = (__bf16)w;
+    const float r1 = w - (float)hi;
+    const __bf16 lo = (__bf16)r1;
+    whi[tt] = hi;
+    wlo[tt] = lo;
+    if constexpr (ST == kF32) wlo2[tt] = (__bf16)(r1 - (float)lo);
+  }
+  wave_sync();  // xT written by this wave -> read below
+
+  // 4. checkpoint readout: acc[rb][j] = sum_n h0[16 rb + 4 q + j][n] C_i[n]
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ST == kBF16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        a = mfma_bf16(__builtin_bit_cast(bf16x8, ld.raw[rb][u]), __builtin_bit_cast(bf16x8, il.craw[u]), a);
+    } else if constexpr (ST == kF16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        a = mfma_f16(__builtin_bit_cast(f16x8, ld.raw[rb][u]), __builtin_bit_cast(f16x8, il.craw[u]), a);
+    } else if constexpr (ST == kFP8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x2 d0 = fp8x4_to_bf16(ld.raw[rb][u][0]), d1 = fp8x4_to_bf16(ld.raw[rb][u][1]);
+        const u32x2 d2 = fp8x4_to_bf16(ld.raw[rb][u][2]), d3 = fp8x4_to_bf16(ld.raw[rb][u][3]);
+        const u32x4 lo = {d0[0], d0[1], d1[0], d1[1]}, hi = {d2[0], d2[1], d3[0], d3[1]};
+        a = mfma_bf16(__builtin_bit_cast(bf16x8, lo), __builtin_bit_cast(bf16x8, il.craw[2 * u]), a);
+        a = mfma_bf16(__builtin_bit_cast(bf16x8, hi), __builtin_bit_cast(bf16x8, il.craw[2 * u + 1]), a);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) a = mfma_f32(__uint_as_float(ld.raw[rb][u][e4]), il.cf32[4 * u + e4], a);
+    }
+    acc[rb] = a;
+  }
+
+  // 5. epilogue: decay to the token (and fp8 row scale), then add the ring /
+  //    new-token replay terms through the x MFMA.
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (ST == kFP8)
+        acc[rb][j] = (acc[rb][j] * ld.rscale[rb][j]) * beta;
+      else
+        acc[rb][j] = acc[rb][j] * beta;
+    }
+    const V xa = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
+    acc[rb] = mfma_win<KW>(xa, whi, acc[rb]);
+    acc[rb] = mfma_win<KW>(xa, wlo, acc[rb]);
+    if constexpr (ST == kF32) acc[rb] = mfma_win<KW>(xa, wlo2, acc[rb]);
+  }
+  wave_sync();  // xT reads done before the tile is reused
+
+  // 6. output rows of the new tokens
+  store_out<OT>(s, H, e, h, lane, acc);
 }
 
 // ---------------------------------------------------------------------------
-// SPLIT: precompute (one wave per (entry, group)): C.B -> scratch, B append.
+// The replay kernel.  Persistent; a work item is (entry, group, chunk of nc
+// heads) and one wave runs one item at a time: it loads C and the C.B row of
+// the group once, then walks the item's heads, the loads of head j + 1 in
+// flight while head j computes (two register buffers alternate).
+//   SPLIT = false (monolith, one launch): the wave forms C.B itself (and the
+//     chunk-0 wave appends the group's B rows);
+//   SPLIT = true: C.B comes from the scratch written by precompute_kernel.
+// Both run identical arithmetic, so their outputs are bit-identical.
 // ---------------------------------------------------------------------------
 
+template <int ST, int OT, int KW, bool SPLIT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void replay_kernel(KCache c, KStep s, int d) {
+  __shared__ uint16_t xT_all[kWaves][kHeadDim * Win<KW>::kXS];
+  __shared__ float cbw_all[SPLIT ? 1 : kWaves][SPLIT ? 4 : kMaxTokens * kCbLds];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nc = c.hpg / d;
+  const int64_t nitems = (int64_t)s.batch * c.G * d;
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  uint16_t *xT = xT_all[wave];
+  for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += nw) {
+    const int chunk = (int)(item % d);
+    const int64_t bg = item / d;
+    const int g = (int)(bg % c.G), b = (int)(bg / c.G);
+    const int h0 = g * c.hpg + chunk * nc;
+    const Entry e = load_entry(c, s, b, g == 0 && chunk == 0);
+    if (e.mode == 0) continue;
+    if (e.mode == 1) {
+      for (int j = 0; j < nc; ++j) zero_out_head<OT>(s, c.H, e, h0 + j, lane);
+      continue;
+    }
+    HeadLoads<ST, KW> la, lb;
+    ItemLoads<ST, KW> il;
+    load_head<ST, KW>(c, s, e, h0, lane, la);
+    load_item_c<ST, KW>(c, s, e, g, lane, il);
+    if constexpr (SPLIT) {
+      load_cb_row<ST, KW>(e, s.cb + ((int64_t)b * c.G + g) * s.T * kCbStride, kCbStride, lane, il);
+    } else {
+      float *cbw = cbw_all[wave];
+      f32x4 cb[KW / 16];
+      compute_cb<KW>(c, s, e, g, chunk == 0, lane, cb);
+#pragma unroll
+      for (int nb = 0; nb < KW / 16; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cbw[(4 * (lane >> 4) + j) * kCbLds + nb * 16 + (lane & 15)] = cb[nb][j];
+      wave_sync();
+      load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
+      wave_sync();
+    }
+    if constexpr (ST == kF32) {  // a 32 KiB fp32 tile per head: no room for a second buffer
+      for (int j = 0; j < nc; ++j) {
+        if (j > 0) load_head<ST, KW>(c, s, e, h0 + j, lane, la);
+        head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+      }
+      continue;
+    }
+    int j = 0;
+    for (; j + 2 < nc; j += 2) {  // heads j + 1 and j + 2 exist: prefetch unconditionally
+      load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
+      __builtin_amdgcn_sched_barrier(0);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+      load_head<ST, KW>(c, s, e, h0 + j + 2, lane, la);
+      __builtin_amdgcn_sched_barrier(0);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, lane);
+    }
+    if (j + 1 < nc) {  // two heads left
+      load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
+      __builtin_amdgcn_sched_barrier(0);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, lane);
+    } else {  // one head left
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SPLIT precompute (one wave per (entry, group)): C.B -> scratch, B append.
+// ---------------------------------------------------------------------------
+
+template <int KW>
 __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep s) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int item = blockIdx.x * kWaves + wave;
   if (item >= s.batch * c.G) return;
   const int b = item / c.G, g = item - b * c.G;
   const Entry e = load_entry(c, s, b, false);
   if (e.mode != 2) return;
-  f32x4 cb[2];
-  compute_cb(c, s, e, g, true, lane, cb);
+  f32x4 cb[KW / 16];
+  compute_cb<KW>(c, s, e, g, true, lane, cb);
   const int m = lane & 15, q = lane >> 4;
   float *dst = s.cb + ((int64_t)b * c.G + g) * s.T * kCbStride;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * q + j;
     if (i < s.T) {
-      dst[i * kCbStride + m] = cb[0][j];
-      dst[i * kCbStride + 16 + m] = cb[1][j];
+#pragma unroll
+      for (int nb = 0; nb < KW / 16; ++nb) dst[i * kCbStride + nb * 16 + m] = cb[nb][j];
     }
-  }
-}
-
-// SPLIT main: persistent grid-stride over (entry, head) items, one per wave.
-template <int ST, int OT>
-__global__ __launch_bounds__(kWaves * 64) void replay_main_kernel(KCache c, KStep s) {
-  __shared__ uint16_t xT_all[kWaves][kHeadDim * kXS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nitems = s.batch * c.H;
-  const int stride = gridDim.x * kWaves;
-  for (int it = blockIdx.x * kWaves + wave; it < nitems; it += stride) {
-    const int b = it / c.H, h = it - b * c.H;
-    const Entry e = load_entry(c, s, b, h == 0);
-    if (e.mode == 0) continue;
-    if (e.mode == 1) {
-      zero_out_head<OT>(s, c.H, e, h, lane);
-      continue;
-    }
-    const float *cb = s.cb + ((int64_t)b * c.G + h / c.hpg) * s.T * kCbStride;
-    head_replay<ST, OT>(c, s, e, h, cb, kCbStride, xT_all[wave], lane);
   }
 }
 
 // ---------------------------------------------------------------------------
 // FLUSH: fold the first k live ring tokens into the checkpoint (fp32) and
 // re-encode it.  One wave per (entry, head); lane (c = l%16, r = l/16) owns
-// elements n = 8c..8c+7 of rows p = 4 t + r, t = 0..15.
+// elements n = 8c..8c+7 of rows p = 4 t + r, t = 0..15.  All loads (the
+// checkpoint and the k ring tokens' dt', x and B) are issued before any
+// arithmetic.
 // ---------------------------------------------------------------------------
+
+// fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448):
+// the quotient v / sc, correctly rounded, is taken from y = fp32(1 / sc) with
+// one residual step (Markstein's correction: y correctly rounded and v * y
+// within one ulp give the correctly rounded quotient; valid for sc in
+// [2^-60, 2^100]).  No clamp is needed: |v| <= max|row| bounds |v / sc| by
+// 448 (1 + 2^-23), which the round-to-nearest conversion maps to 448.
+__device__ __forceinline__ u32x2 fp8_encode8_fast(const float *v, float sc, float y) {
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q0 = v[e] * y;
+    const float r = fmaf(-q0, sc, v[e]);
+    qv[e] = fmaf(r, y, q0);
+  }
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+// Same with the plain IEEE division (scales outside that range).
+__device__ __forceinline__ u32x2 fp8_encode8_div(const float *v, float sc) {
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = __builtin_amdgcn_fmed3f(v[e] / sc, -448.0f, 448.0f);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+__device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && sc <= 0x1p100f; }
+
+__device__ __forceinline__ float max8_abs(const float *v) {
+  const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  const float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
+}
+
+// LDS bytes of one flush wave for ring length L.
+__host__ __device__ constexpr int flush_lds_bytes(int L) {
+  return (kHeadDim + 32) * 4 + L * (kHeadDim + kDState) * 2;
+}
+
+// B chunk (8 values of lane column c) and fold coefficient of the ring tokens
+// s0 .. s0 + 3 (zero past k).
+__device__ __forceinline__ void load_fold_chunk(const uint16_t *bs, int s0, int k, int cl, float coef,
+                                                float bc[4][8], float cf[4]) {
+#pragma unroll
+  for (int ss = 0; ss < 4; ++ss) {
+    const int sg = s0 + ss < k ? s0 + ss : s0;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(bs + sg * kDState + cl * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bc[ss][e] = bf2f((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
+    cf[ss] = s0 + ss < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(coef), s0 + ss)) : 0.f;
+  }
+}
+
+// acc[tq][e] += (coef_s x_s[p]) B_s[n] for the 4 passes of quarter Q.
+__device__ __forceinline__ void fold_chunk(float acc[4][8], const float bc[4][8], const float cf[4],
+                                           const uint16_t *xs, int s0, int k, int Q, int rsub) {
+#pragma unroll
+  for (int ss = 0; ss < 4; ++ss) {
+    if (s0 + ss < k) {
+#pragma unroll
+      for (int tq = 0; tq < 4; ++tq) {
+        const float uu = cf[ss] * bf2f(xs[(s0 + ss) * kHeadDim + 16 * Q + 4 * tq + rsub]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tq][e] = fmaf(uu, bc[ss][e], acc[tq][e]);
+      }
+    }
+  }
+}
 
 template <int ST>
 __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
-  __shared__ float u_all[kWaves][kMaxRing * kHeadDim];  // u[s][p] = coef_s x_s[p]
-  __shared__ float rs_all[kWaves][3 * kHeadDim];          // old scale | row max / new scale | 1/scale
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Dynamic LDS, per wave (flush_lds_bytes): old scales | row max, new scale,
+  // 1/scale (96 floats), then x [L][64] and B [L][128] of the ring tokens.
+  extern __shared__ __align__(16) uint8_t flush_smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
   const int h = (blockIdx.x - j * htiles) * kWaves + wave;
   if (h >= c.H) return;
@@ -583,13 +756,18 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
     return;
   }
   const int g = h / c.hpg, cl = lane & 15, rsub = lane >> 4;
-  float *u_s = u_all[wave];
-  float *rs = rs_all[wave];
+  uint8_t *wsm = flush_smem + wave * flush_lds_bytes(L);
+  float *rs = reinterpret_cast<float *>(wsm);
+  uint16_t *xs = reinterpret_cast<uint16_t *>(wsm + (kHeadDim + 32) * 4);
+  uint16_t *bs = xs + L * kHeadDim;
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   constexpr int kRowBytes = kDState * kEB;
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
 
-  // 1. checkpoint loads (8 elements per lane per pass)
+  // 1. loads, all issued before any arithmetic: the checkpoint (lane (c, r)
+  //    owns elements 8c..8c+7 of rows p = 4 t + r), the old fp8 row scale,
+  //    dt' (lane s), and the first ring tokens' x (lane l: token l/8, chunk
+  //    l%8) and B (lane l: token l/16, chunk l%16).
   u32x4 raw16[16];
   u32x4 raw32[16][2];
   u32x2 raw8[16];
@@ -606,123 +784,125 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
     }
   }
   float *scp = nullptr;
+  float old_scale = 1.f;
   if constexpr (ST == kFP8) {
     scp = reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
-    rs[lane] = scp[lane];
+    old_scale = scp[lane];
   }
-
-  // 2. dt', decay prefix, fold coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s
   const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)slot * c.dt_stride) + h * L;
   const float dtp = lane < k ? dtring[ring_pos(r, lane, L)] : 0.f;
+  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
+                          (int64_t)h * L * kHeadDim;
+  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
+                          (int64_t)g * L * kDState;
+  u32x4 xr = {0u, 0u, 0u, 0u}, br = {0u, 0u, 0u, 0u};
+  if ((lane >> 3) < k) xr = ld16(xring + ring_pos(r, lane >> 3, L) * kHeadDim + (lane & 7) * 8);
+  if ((lane >> 4) < k) br = ld16(Bring + ring_pos(r, lane >> 4, L) * kDState + (lane & 15) * 8);
+
+  // 2. decay prefix and fold coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s;
+  //    ring tokens -> LDS (tokens past the first 8 / 4 are loaded here)
   const float cum = scan32(A[h] * dtp, lane);
   const float ctot = __shfl(cum, k - 1, 64);
   const float coef = lane < k ? expf(ctot - cum) * dtp : 0.f;
   const float D0 = expf(ctot);
-
-  // 3. u[s][p] = coef_s x_s[p], lane = p
-  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
-                          (int64_t)h * L * kHeadDim;
-  for (int sg = 0; sg < k; ++sg) {
-    const float cf = __shfl(coef, sg, 64);
-    u_s[sg * kHeadDim + lane] = cf * bf2f(xring[ring_pos(r, sg, L) * kHeadDim + lane]);
+  if constexpr (ST == kFP8) rs[lane] = old_scale;
+  if ((lane >> 3) < k) st16(xs + (lane >> 3) * kHeadDim + (lane & 7) * 8, xr);
+  if ((lane >> 4) < k) st16(bs + (lane >> 4) * kDState + (lane & 15) * 8, br);
+  for (int s0 = 8; s0 < k; s0 += 8) {
+    const int sg = s0 + (lane >> 3);
+    if (sg < k) st16(xs + sg * kHeadDim + (lane & 7) * 8, ld16(xring + ring_pos(r, sg, L) * kHeadDim + (lane & 7) * 8));
+  }
+  for (int s0 = 4; s0 < k; s0 += 4) {
+    const int sg = s0 + (lane >> 4);
+    if (sg < k) st16(bs + sg * kDState + (lane & 15) * 8, ld16(Bring + ring_pos(r, sg, L) * kDState + (lane & 15) * 8));
   }
   wave_sync();
 
-  // 4. decode and decay: acc = exp(cumA_{k-1}) h0
-  float acc[16][8];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    if constexpr (ST == kFP8) {
-      const float f = D0 * rs[4 * t + rsub];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], false);
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], true);
-        acc[t][4 * w + 0] = f * a[0];
-        acc[t][4 * w + 1] = f * a[1];
-        acc[t][4 * w + 2] = f * b[0];
-        acc[t][4 * w + 3] = f * b[1];
-      }
-    } else if constexpr (ST == kF32) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[t][e] = D0 * __uint_as_float(raw32[t][e >> 2][e & 3]);
-    } else if constexpr (ST == kBF16) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc[t][e] = D0 * bf2f((e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu);
-        acc[t][e] = D0 * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-      }
-    }
-  }
+  float bc0[4][8], cf0[4];
+  load_fold_chunk(bs, 0, k, cl, coef, bc0, cf0);
 
-  // 5. rank-k update: acc[p][n] += sum_s u[s][p] B_s[n], four ring tokens at a time
-  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
-                          (int64_t)g * L * kDState;
-  for (int s0 = 0; s0 < k; s0 += 4) {
-    float bc[4][8];
+  // 3. quarter by quarter (16 rows): decode and decay, rank-k update, encode
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (s0 + ss < k) v = ld16(Bring + ring_pos(r, s0 + ss, L) * kDState + cl * 8);
+  for (int Q = 0; Q < 4; ++Q) {
+    float acc[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bc[ss][e] = bf2f((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
-    }
+    for (int tq = 0; tq < 4; ++tq) {
+      const int t = 4 * Q + tq;
+      if constexpr (ST == kFP8) {
+        const float f = D0 * rs[4 * t + rsub];
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      if (s0 + ss < k) {
+        for (int w = 0; w < 2; ++w) {
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], false);
+          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], true);
+          acc[tq][4 * w + 0] = f * a[0];
+          acc[tq][4 * w + 1] = f * a[1];
+          acc[tq][4 * w + 2] = f * b[0];
+          acc[tq][4 * w + 3] = f * b[1];
+        }
+      } else if constexpr (ST == kF32) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const float uu = u_s[(s0 + ss) * kHeadDim + 4 * t + rsub];
+        for (int e = 0; e < 8; ++e) acc[tq][e] = D0 * __uint_as_float(raw32[t][e >> 2][e & 3]);
+      } else if constexpr (ST == kBF16) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(uu, bc[ss][e], acc[t][e]);
+        for (int e = 0; e < 8; ++e)
+          acc[tq][e] = D0 * bf2f((e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu);
+          acc[tq][e] = D0 * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
         }
       }
     }
-  }
+    fold_chunk(acc, bc0, cf0, xs, 0, k, Q, rsub);
+    for (int s0 = 4; s0 < k; s0 += 4) {
+      float bc[4][8], cf[4];
+      load_fold_chunk(bs, s0, k, cl, coef, bc, cf);
+      fold_chunk(acc, bc, cf, xs, s0, k, Q, rsub);
+    }
 
-  // 6. encode and store
-  if constexpr (ST == kFP8) {
+    if constexpr (ST == kFP8) {
+      // row max -> one lane per row computes scale and 1/scale -> every lane
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float mx = 0.f;
+      for (int tq = 0; tq < 4; ++tq) {
+        const float mx = row16_max(max8_abs(acc[tq]));
+        if (cl == 0) rs[kHeadDim + 4 * tq + rsub] = mx;
+      }
+      wave_sync();
+      bool fast = true;
+      if (lane < 16) {
+        const float sc = fp8_row_scale(rs[kHeadDim + lane]);
+        const float y = 1.0f / sc;
+        scp[16 * Q + lane] = sc;
+        rs[kHeadDim + lane] = sc;
+        rs[kHeadDim + 16 + lane] = y;
+        fast = scale_fast(sc);
+      }
+      const bool all_fast = __all(fast);
+      wave_sync();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(acc[t][e]));
-      mx = row16_max(mx);
-      if (cl == 0) rs[kHeadDim + 4 * t + rsub] = mx;
-    }
-    wave_sync();
-    {
-      const float sc = fp8_row_scale(rs[kHeadDim + lane]);
-      const float y = 1.0f / sc;
-      scp[lane] = sc;
-      rs[kHeadDim + lane] = sc;
-      rs[2 * kHeadDim + lane] = y;
-    }
-    wave_sync();
+      for (int tq = 0; tq < 4; ++tq) {
+        const int p = 16 * Q + 4 * tq + rsub;
+        const float sc = rs[kHeadDim + 4 * tq + rsub], y = rs[kHeadDim + 16 + 4 * tq + rsub];
+        st8(hp + p * kRowBytes + cl * 8, all_fast ? fp8_encode8_fast(acc[tq], sc, y) : fp8_encode8_div(acc[tq], sc));
+      }
+      wave_sync();
+    } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float sc = rs[kHeadDim + 4 * t + rsub], y = rs[2 * kHeadDim + 4 * t + rsub];
-      st8(hp + (4 * t + rsub) * kRowBytes + cl * 8, fp8_encode8(acc[t], sc, y));
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      uint8_t *rowp = hp + (4 * t + rsub) * kRowBytes + cl * 8 * kEB;
-      if constexpr (ST == kF32) {
-        st16(rowp, u32x4{__float_as_uint(acc[t][0]), __float_as_uint(acc[t][1]),
-                         __float_as_uint(acc[t][2]), __float_as_uint(acc[t][3])});
-        st16(rowp + 16, u32x4{__float_as_uint(acc[t][4]), __float_as_uint(acc[t][5]),
-                              __float_as_uint(acc[t][6]), __float_as_uint(acc[t][7])});
-      } else if constexpr (ST == kBF16) {
-        st16(rowp, u32x4{pack_bf16(acc[t][0], acc[t][1]), pack_bf16(acc[t][2], acc[t][3]),
-                         pack_bf16(acc[t][4], acc[t][5]), pack_bf16(acc[t][6], acc[t][7])});
-      } else {
-        st16(rowp, u32x4{pack_f16(acc[t][0], acc[t][1]), pack_f16(acc[t][2], acc[t][3]),
-                         pack_f16(acc[t][4], acc[t][5]), pack_f16(acc[t][6], acc[t][7])});
+      for (int tq = 0; tq < 4; ++tq) {
+        uint8_t *rowp = hp + (16 * Q + 4 * tq + rsub) * kRowBytes + cl * 8 * kEB;
+        if constexpr (ST == kF32) {
+          st16(rowp, u32x4{__float_as_uint(acc[tq][0]), __float_as_uint(acc[tq][1]),
+                           __float_as_uint(acc[tq][2]), __float_as_uint(acc[tq][3])});
+          st16(rowp + 16, u32x4{__float_as_uint(acc[tq][4]), __float_as_uint(acc[tq][5]),
+                                __float_as_uint(acc[tq][6]), __float_as_uint(acc[tq][7])});
+        } else if constexpr (ST == kBF16) {
+          st16(rowp, u32x4{pack_bf16(acc[tq][0], acc[tq][1]), pack_bf16(acc[tq][2], acc[tq][3]),
+                           pack_bf16(acc[tq][4], acc[tq][5]), pack_bf16(acc[tq][6], acc[tq][7])});
+        } else {
+          st16(rowp, u32x4{pack_f16(acc[tq][0], acc[tq][1]), pack_f16(acc[tq][2], acc[tq][3]),
+                           pack_f16(acc[tq][4], acc[tq][5]), pack_f16(acc[tq][6], acc[tq][7])});
+        }
       }
     }
   }
@@ -764,13 +944,12 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
     float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     uint8_t *rowp = hp + p * kRowBytes + cl * 8 * kEB;
     if constexpr (ST == kFP8) {
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
-      mx = row16_max(mx);
-      const float sc = fp8_row_scale(mx);
+      const float sc = fp8_row_scale(row16_max(max8_abs(v)));
       const float y = 1.0f / sc;
-      st8(rowp, fp8_encode8(v, sc, y));
+      if (__all(scale_fast(sc)))
+        st8(rowp, fp8_encode8_fast(v, sc, y));
+      else
+        st8(rowp, fp8_encode8_div(v, sc));
       if (cl == 0)
         reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + p] = sc;
     } else if constexpr (ST == kF32) {
@@ -810,13 +989,6 @@ __global__ __launch_bounds__(256) void init_clear_kernel(KCache c, const int32_t
 
 namespace {
 
-// Heads per monolith workgroup: up to one per wave, dividing the group.
-int monolith_head_tile(int hpg) {
-  for (int ht = kWaves; ht > 1; --ht)
-    if (hpg % ht == 0) return ht;
-  return 1;
-}
-
 template <typename K>
 int resident_blocks(K kernel, int lds_dynamic) {
   int dev = 0, cus = 0, per_cu = 0;
@@ -829,37 +1001,50 @@ int resident_blocks(K kernel, int lds_dynamic) {
   return cus * per_cu;
 }
 
-template <int ST, int OT>
-hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
-  const int ht = monolith_head_tile(c.hpg), nht = c.hpg / ht;
-  const int64_t blocks = (int64_t)s.batch * c.G * nht;
-  if (blocks <= 0) return hipSuccess;
-  replay_monolith_kernel<ST, OT><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s, nht);
+// Heads per work item: the whole group unless that leaves fewer items than
+// the GPU runs waves at once, then the group is split into d chunks.
+int chunks_per_group(int64_t batch, int G, int hpg, int64_t resident_waves) {
+  for (int d = 1; d <= hpg; ++d)
+    if (hpg % d == 0 && batch * G * d >= resident_waves) return d;
+  return hpg;
+}
+
+template <int ST, int OT, int KW, bool SPLIT>
+hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
+  static int resident = 0;  // blocks resident on the device (per template instance)
+  if (resident == 0) resident = resident_blocks(replay_kernel<ST, OT, KW, SPLIT>, 0);
+  if (SPLIT) {
+    const int64_t pre_items = (int64_t)s.batch * c.G;
+    precompute_kernel<KW><<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int d = chunks_per_group(s.batch, c.G, c.hpg, (int64_t)resident * kWaves);
+  const int64_t items = (int64_t)s.batch * c.G * d;
+  const int64_t need = (items + kWaves - 1) / kWaves;
+  const int64_t blocks = need < resident ? need : resident;
+  replay_kernel<ST, OT, KW, SPLIT><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s, d);
   return hipGetLastError();
 }
 
 template <int ST, int OT>
+hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
+  if (s.batch <= 0) return hipSuccess;
+  return c.L <= 16 ? replay_kw<ST, OT, 16, false>(c, s, st) : replay_kw<ST, OT, 32, false>(c, s, st);
+}
+
+template <int ST, int OT>
 hipError_t split_t(const KCache &c, const KStep &s, hipStream_t st) {
-  const int64_t pre_items = (int64_t)s.batch * c.G;
-  if (pre_items <= 0) return hipSuccess;
-  precompute_kernel<<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  static int resident = 0;  // per template instance; the same on every gfx950 device
-  if (resident == 0) resident = resident_blocks(replay_main_kernel<ST, OT>, 0);
-  const int64_t items = (int64_t)s.batch * c.H;
-  const int64_t need = (items + kWaves - 1) / kWaves;
-  const int64_t blocks = need < resident ? need : resident;
-  replay_main_kernel<ST, OT><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s);
-  return hipGetLastError();
+  if (s.batch <= 0) return hipSuccess;
+  return c.L <= 16 ? replay_kw<ST, OT, 16, true>(c, s, st) : replay_kw<ST, OT, 32, true>(c, s, st);
 }
 
 template <int ST>
 hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                    int n, hipStream_t st) {
   const int htiles = (c.H + kWaves - 1) / kWaves;
-  flush_kernel<ST><<<dim3((unsigned)((int64_t)n * htiles)), dim3(kWaves * 64), 0, st>>>(
-      c, slot_idx, num_fold, A, htiles);
+  flush_kernel<ST><<<dim3((unsigned)((int64_t)n * htiles)), dim3(kWaves * 64), kWaves * flush_lds_bytes(c.L),
+                     st>>>(c, slot_idx, num_fold, A, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   ring_advance_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);
