@@ -91,7 +91,7 @@ enum {
  * The per-slot cache [FI item 2; VD].  Inside one slot page every tensor is
  * packed; *_slot_stride is the distance in BYTES between slot pages (it may
  * include padding).  Layouts:
- *   state       [slot][nheads][headdim][dstate]  state_dtype
+ *   state       [slot][nheads][64 * 128]         state_dtype, MFMA-tiled (below)
  *   state_scale [slot][nheads][headdim]          f32, fp8 state only: the row's
  *                                                value is code * scale
  *   x_cache     [slot][nheads][ring_len][headdim] io_dtype
@@ -100,6 +100,15 @@ enum {
  *   ring_start  [slot]                            i32, in [0, ring_len)
  * Live token j (j < pnat) of a slot is ring entry (ring_start + j) mod L; new
  * token i is appended at (ring_start + pnat + i) mod L.
+ * Checkpoint tiling: element h[p][n] of one head (eb bytes per element) sits
+ * at byte offset
+ *     rb * 2048 * eb + (u * 64 + l) * 16 + (t % (16 / eb)) * eb
+ * with p = 16 rb + m, n = 32 q + t, l = 16 q + m, u = t / (16 / eb).  Each
+ * row is cut into four quarters of 32 values; quarter q of row 16 rb + m is
+ * lane l's share of a 64-lane wave, stored as 16-byte chunks u with chunk u of
+ * all 64 lanes side by side, so every 16-byte-per-lane load or store of a
+ * row block is 1 KiB contiguous.  ssu_init_state writes this layout from
+ * plain row-major fp32 [headdim][dstate] states.
  * Requirements: headdim == 64, dstate == 128, nheads % ngroups == 0,
  * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer and slot stride
  * 16-byte aligned.  status may be NULL.

@@ -52,7 +52,8 @@
  *
  * Layouts (all byte strides between slots are arguments; inside a slot the
  * layout is packed):
- *   state     [slot][H][P][N]  element type = state dtype
+ *   state     [slot][H][P][N]  element type = state dtype, each head either
+ *                              row-major or in the tiled order (elem_offset)
  *   scale     [slot][H][P]     f32 (fp8 state only)
  *   x_cache   [slot][H][L][P]  bf16 bits
  *   B_cache   [slot][G][L][N]  bf16 bits
@@ -186,6 +187,7 @@ double or_softplus(double v) { return v > 20.0 ? v : log1p(exp(v)); }
 typedef struct {
   int num_slots, nheads, ngroups, headdim, dstate, ring_len;
   int state_dtype;
+  int state_layout; /* 0: row-major [P][N]; 1: tiled (P = 64, N = 128) */
   uint8_t *state;
   int64_t state_stride; /* bytes between slots */
   uint8_t *scale;
@@ -209,6 +211,21 @@ static int state_elem_bytes(int dt) {
   }
 }
 
+/* Byte offset of element (p, n) inside one head's checkpoint.
+ * Row-major: (p N + n) eb.
+ * Tiled (P = 64, N = 128; the layout the library documents): rows come in
+ * blocks of 16 (rb = p / 16, m = p % 16) and each row in four quarters of 32
+ * values (q = n / 32, t = n % 32).  Quarter q of row p is owned by lane
+ * l = 16 q + m; its 32 values are cut into 16-byte chunks of ce = 16 / eb
+ * values, and chunk u = t / ce of lane l is stored at byte
+ * rb * 2048 eb + (64 u + l) * 16, value t % ce of it at + (t % ce) eb. */
+static int64_t elem_offset(const or_cache *c, int eb, int p, int n) {
+  if (c->state_layout == 0) return ((int64_t)p * c->dstate + n) * eb;
+  const int rb = p / 16, m = p % 16, q = n / 32, t = n % 32, ce = 16 / eb;
+  const int l = 16 * q + m, u = t / ce;
+  return (int64_t)rb * 2048 * eb + ((int64_t)u * 64 + l) * 16 + (int64_t)(t % ce) * eb;
+}
+
 /* Decode the checkpoint of (slot, head) into h[P*N] (fp64). */
 static void decode_state(const or_cache *c, int slot, int head, double *h) {
   const int P = c->headdim, N = c->dstate, eb = state_elem_bytes(c->state_dtype);
@@ -223,7 +240,7 @@ static void decode_state(const or_cache *c, int slot, int head, double *h) {
       sc = (double)f;
     }
     for (int n = 0; n < N; ++n) {
-      const uint8_t *e = base + ((int64_t)p * N + n) * eb;
+      const uint8_t *e = base + elem_offset(c, eb, p, n);
       double v;
       switch (c->state_dtype) {
       case OR_F32: { float f; memcpy(&f, e, 4); v = f; } break;
@@ -241,8 +258,7 @@ static void decode_state(const or_cache *c, int slot, int head, double *h) {
 static void encode_row(const or_cache *c, int slot, int head, int p,
                        const float *row) {
   const int P = c->headdim, N = c->dstate, eb = state_elem_bytes(c->state_dtype);
-  uint8_t *base = c->state + (int64_t)slot * c->state_stride +
-                  ((int64_t)head * P * N + (int64_t)p * N) * eb;
+  uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * P * N * eb;
   if (c->state_dtype == OR_FP8) {
     float m = 0.0f;
     for (int n = 0; n < N; ++n)
@@ -253,12 +269,12 @@ static void encode_row(const or_cache *c, int slot, int head, int p,
            &scale, 4);
     for (int n = 0; n < N; ++n) {
       float q = row[n] / scale;
-      base[n] = or_enc_e4m3_sat((double)q);
+      base[elem_offset(c, eb, p, n)] = or_enc_e4m3_sat((double)q);
     }
     return;
   }
   for (int n = 0; n < N; ++n) {
-    uint8_t *e = base + (int64_t)n * eb;
+    uint8_t *e = base + elem_offset(c, eb, p, n);
     switch (c->state_dtype) {
     case OR_F32: memcpy(e, &row[n], 4); break;
     case OR_BF16: { uint16_t u = or_enc_bf16((double)row[n]); memcpy(e, &u, 2); } break;
@@ -268,7 +284,7 @@ static void encode_row(const or_cache *c, int slot, int head, int p,
   }
 }
 
-/* fp64 state mode (test only): store without rounding. */
+/* fp64 state mode (test only, row-major): store without rounding. */
 static void store_state_f64(const or_cache *c, int slot, int head, const double *h) {
   const int PN = c->headdim * c->dstate;
   uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * PN * 8;

@@ -47,7 +47,7 @@ class _OrCache(ctypes.Structure):
     _fields_ = [
         ("num_slots", ctypes.c_int), ("nheads", ctypes.c_int), ("ngroups", ctypes.c_int),
         ("headdim", ctypes.c_int), ("dstate", ctypes.c_int), ("ring_len", ctypes.c_int),
-        ("state_dtype", ctypes.c_int),
+        ("state_dtype", ctypes.c_int), ("state_layout", ctypes.c_int),
         ("state", ctypes.c_void_p), ("state_stride", ctypes.c_int64),
         ("scale", ctypes.c_void_p), ("scale_stride", ctypes.c_int64),
         ("x_cache", ctypes.c_void_p), ("x_stride", ctypes.c_int64),
@@ -98,7 +98,7 @@ def _as_orcache(cache) -> _OrCache:
     assert cache.ring_start.dtype == np.int32
     return _OrCache(
         s.num_slots, s.nheads, s.ngroups, s.headdim, s.dstate, s.ring_len,
-        _DTYPE_CODE[s.state_dtype],
+        _DTYPE_CODE[s.state_dtype], {"rowmajor": 0, "tiled": 1}[s.state_layout],
         cache.state.ctypes.data, cache.state.shape[1],
         cache.scale.ctypes.data, cache.scale.shape[1],
         cache.x_cache.ctypes.data, cache.x_cache.shape[1],
@@ -191,7 +191,7 @@ def softplus(v):
 def decode_state(cache, slot):
     """fp64 [H, P, N] value of one slot's checkpoint (decode rule of the oracle)."""
     s = cache.spec
-    raw = cache.state_view(slot)
+    raw = cache.state_logical(slot)
     if s.state_dtype in ("f32", "f64"):
         return raw.astype(np.float64)
     if s.state_dtype == "bf16":

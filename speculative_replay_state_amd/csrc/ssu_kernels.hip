@@ -60,21 +60,15 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 // Streaming (non-temporal) forms for data touched once per call whose every
-// instruction covers whole cache lines (the flush's row-linear checkpoint
-// tiles, the x windows).  On MI355X they lift a line-contiguous read stream
-// from ~5.7 to ~6.1 TB/s and a read + write stream from ~5.4 to ~6.2 TB/s;
-// on half-line access patterns they do not help or hurt.
+// wave instruction covers whole cache lines (the tiled checkpoint, whose
+// chunk u of a row block is 1 KiB contiguous over the wave, and the x
+// windows).  On MI355X they lift a line-contiguous read stream from ~5.7 to
+// ~6.1 TB/s and a read + write stream from ~5.4 to ~6.2 TB/s.
 __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
-__device__ __forceinline__ u32x2 ld8_nt(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-}
 __device__ __forceinline__ void st16_nt(void *p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-__device__ __forceinline__ void st8_nt(void *p, u32x2 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -95,25 +89,6 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(expf(v)); }
-
-// Inclusive prefix sum over lanes 0..31 (Hillis-Steele; lanes >= 32 unused).
-__device__ __forceinline__ float scan32(float v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) {
-    float t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
-
-// Max over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
-  return v;
-}
 
 __device__ __forceinline__ int ring_pos(int r, int s, int L) {
   int p = r + s;
@@ -152,6 +127,16 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
 __device__ __forceinline__ float fp8_row_scale(float m) {
   float sc = m / 448.0f;
   return sc > 0.0f ? sc : 1.0f;
+}
+
+// Byte offset, inside one head's checkpoint, of 16-byte chunk u of lane l in
+// row block rb.  The checkpoint is stored MFMA-tiled: row p = 16 rb + m is cut
+// into four quarters of 32 values (q = n / 32); quarter q of row p belongs to
+// lane l = 16 q + m and is stored as 16-byte chunks, chunk u of every lane of
+// a row block side by side, so one wave load instruction reads 1 KiB
+// contiguous that is directly the lanes' MFMA operand.
+__device__ __forceinline__ int tile_chunk(int rb, int u, int lane, int eb) {
+  return rb * 2048 * eb + (u * 64 + lane) * 16;
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs; remap so that runs of
@@ -348,9 +333,8 @@ __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry
 template <int ST, int KW>
 struct HeadLoads {
   static constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  static constexpr int kRowBytes = kDState * kEB;
-  static constexpr int kNLD = kRowBytes / 64;  // 16-byte checkpoint loads per lane per 16-row block
-  u32x4 raw[4][kNLD];                        // lane (m, q): bytes [64 u + 16 q, +16) of row 16 rb + m
+  static constexpr int kNLD = 2 * kEB;  // 16-byte chunks per lane per 16-row block
+  u32x4 raw[4][kNLD];                   // lane l = 16 q + m: chunk u of quarter q of row 16 rb + m
   u32x4 xw[Win<KW>::kRounds];                // x window chunks
   f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
   float dtv;                                 // lane s: stored dt' (s < pnat) or dt + dt_bias (new)
@@ -376,7 +360,7 @@ __device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16(hp + (rb * 16 + m) * T::kRowBytes + u * 64 + q * 16);
+    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, T::kEB));
   if constexpr (ST == kFP8) {
     const float *sp = reinterpret_cast<const float *>(c.scale + (int64_t)e.slot * c.scale_stride) +
                       h * kHeadDim;
@@ -411,25 +395,21 @@ __device__ __forceinline__ void load_item_c(const KCache &c, const KStep &s, con
   const int m = lane & 15, q = lane >> 4;
   const bool tok_ok = m < e.Tb;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
-  if constexpr (ST == kBF16) {
+  // k step kk of the readout takes values t = 8 kk .. 8 kk + 7 of the lane's
+  // quarter q, i.e. n = 32 q + 8 kk + e (fp32 tile: k step t, n = 32 q + t).
+  const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState + 32 * q;
+  if constexpr (ST == kBF16 || ST == kFP8) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) il.craw[u] = tok_ok ? ld16(Crow + 32 * u + 8 * q) : zero4;  // n = 32u + 8q + e
+    for (int u = 0; u < 4; ++u) il.craw[u] = tok_ok ? ld16(Crow + 8 * u) : zero4;
   } else if constexpr (ST == kF16) {
     // C as f16 (exact for |C| in the f16 normal range), converted once per item
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      il.craw[u] = __builtin_bit_cast(u32x4, bf16x8_to_f16x8(tok_ok ? ld16(Crow + 32 * u + 8 * q) : zero4));
-  } else if constexpr (ST == kFP8) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)  // k step 2u + hh: n = 64u + 16q + 8hh + e
-        il.craw[2 * u + hh] = tok_ok ? ld16(Crow + 64 * u + 16 * q + 8 * hh) : zero4;
+      il.craw[u] = __builtin_bit_cast(u32x4, bf16x8_to_f16x8(tok_ok ? ld16(Crow + 8 * u) : zero4));
   } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // k step 4u + e: n = 16u + 4q + e
-      const u32x2 v = tok_ok ? ld8(Crow + 16 * u + 4 * q) : u32x2{0u, 0u};
+    for (int u = 0; u < 8; ++u) {
+      const u32x2 v = tok_ok ? ld8(Crow + 4 * u) : u32x2{0u, 0u};
       il.cf32[4 * u + 0] = bf2f(v[0] & 0xFFFFu);
       il.cf32[4 * u + 1] = bf2f(v[0] >> 16);
       il.cf32[4 * u + 2] = bf2f(v[1] & 0xFFFFu);
@@ -666,11 +646,18 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
 }
 
 // ---------------------------------------------------------------------------
-// FLUSH: fold the first k live ring tokens into the checkpoint (fp32) and
-// re-encode it.  One wave per (entry, head); lane (c = l%16, r = l/16) owns
-// elements n = 8c..8c+7 of rows p = 4 t + r, t = 0..15.  All loads (the
-// checkpoint and the k ring tokens' dt', x and B) are issued before any
-// arithmetic.
+// FLUSH: fold the first k live ring tokens into the checkpoint and re-encode
+// it.  One wave per (entry, head).  With coef_s = exp(cumA_{k-1} - cumA_s) dt'_s
+// and D0 = exp(cumA_{k-1}) the new checkpoint is D0 h0 + sum_{s<k} coef_s x_s B_s^T.
+// The rank-k update runs on MFMA in transposed form: for row block rb and
+// tile nb (0..7),
+//   acc_nb[r][c] += sum_s (coef_s B_s[n(r, nb)]) x_s[16 rb + c],
+//   n(r, nb) = 32 (r / 4) + 8 (r % 4) + nb,
+// so lane l = 16 q + m ends up holding values t = 8 j + nb (j = 0..3,
+// nb = 0..7) of quarter q of row 16 rb + m: exactly its own chunks of the
+// tiled checkpoint, and decode, update, row max and encode stay in registers.
+// coef_s B_s is split into bf16 hi + lo (+ lo2 for fp32 state) parts; x is
+// bf16 and exact.  The A operands do not depend on rb and are built once.
 // ---------------------------------------------------------------------------
 
 // fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448):
@@ -708,54 +695,100 @@ __device__ __forceinline__ u32x2 fp8_encode8_div(const float *v, float sc) {
 
 __device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && sc <= 0x1p100f; }
 
-__device__ __forceinline__ float max8_abs(const float *v) {
-  const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-  const float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
-  return fmaxf(fmaxf(a, b), fmaxf(fabsf(v[6]), fabsf(v[7])));
-}
-
-// LDS bytes of one flush wave for ring length L.
-__host__ __device__ constexpr int flush_lds_bytes(int L) {
-  return (kHeadDim + 32) * 4 + L * (kHeadDim + kDState) * 2;
-}
-
-// B chunk (8 values of lane column c) and fold coefficient of the ring tokens
-// s0 .. s0 + 3 (zero past k).
-__device__ __forceinline__ void load_fold_chunk(const uint16_t *bs, int s0, int k, int cl, float coef,
-                                                float bc[4][8], float cf[4]) {
+// Max |v| over the 32 values t of a lane's quarter row, then over the four
+// lanes (q = 0..3) that hold the same row.
+__device__ __forceinline__ float quarter_row_max(const float *v) {
+  float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int ss = 0; ss < 4; ++ss) {
-    const int sg = s0 + ss < k ? s0 + ss : s0;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(bs + sg * kDState + cl * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bc[ss][e] = bf2f((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu));
-    cf[ss] = s0 + ss < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(coef), s0 + ss)) : 0.f;
+  for (int t = 0; t < 32; t += 2) {
+    a = fmaxf(a, fabsf(v[t]));
+    b = fmaxf(b, fabsf(v[t + 1]));
   }
+  float mx = fmaxf(a, b);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
 }
 
-// acc[tq][e] += (coef_s x_s[p]) B_s[n] for the 4 passes of quarter Q.
-__device__ __forceinline__ void fold_chunk(float acc[4][8], const float bc[4][8], const float cf[4],
-                                           const uint16_t *xs, int s0, int k, int Q, int rsub) {
-#pragma unroll
-  for (int ss = 0; ss < 4; ++ss) {
-    if (s0 + ss < k) {
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) {
-        const float uu = cf[ss] * bf2f(xs[(s0 + ss) * kHeadDim + 16 * Q + 4 * tq + rsub]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[tq][e] = fmaf(uu, bc[ss][e], acc[tq][e]);
-      }
-    }
-  }
-}
-
+// Encodes the 32 values of one quarter row (value t in v[t]) into the lane's
+// chunks of row block rb, and returns nothing; fp8 also needs the row scale.
 template <int ST>
+__device__ __forceinline__ void store_quarter(uint8_t *hp, int rb, int lane, const float *v, float sc, float y,
+                                              bool fast) {
+  if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const u32x2 lo = fast ? fp8_encode8_fast(v + 16 * u, sc, y) : fp8_encode8_div(v + 16 * u, sc);
+      const u32x2 hi = fast ? fp8_encode8_fast(v + 16 * u + 8, sc, y) : fp8_encode8_div(v + 16 * u + 8, sc);
+      st16_nt(hp + tile_chunk(rb, u, lane, 1), u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+  } else if constexpr (ST == kF32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      st16_nt(hp + tile_chunk(rb, u, lane, 4),
+              u32x4{__float_as_uint(v[4 * u]), __float_as_uint(v[4 * u + 1]), __float_as_uint(v[4 * u + 2]),
+                    __float_as_uint(v[4 * u + 3])});
+  } else if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st16_nt(hp + tile_chunk(rb, u, lane, 2),
+              u32x4{pack_bf16(v[8 * u], v[8 * u + 1]), pack_bf16(v[8 * u + 2], v[8 * u + 3]),
+                    pack_bf16(v[8 * u + 4], v[8 * u + 5]), pack_bf16(v[8 * u + 6], v[8 * u + 7])});
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st16_nt(hp + tile_chunk(rb, u, lane, 2),
+              u32x4{pack_f16(v[8 * u], v[8 * u + 1]), pack_f16(v[8 * u + 2], v[8 * u + 3]),
+                    pack_f16(v[8 * u + 4], v[8 * u + 5]), pack_f16(v[8 * u + 6], v[8 * u + 7])});
+  }
+}
+
+// Decodes one lane's chunks of a row block into v[t] (t = 0..31), times f.
+template <int ST>
+__device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, float *v) {
+  if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], true);
+        v[16 * u + 4 * w + 0] = f * a[0];
+        v[16 * u + 4 * w + 1] = f * a[1];
+        v[16 * u + 4 * w + 2] = f * b[0];
+        v[16 * u + 4 * w + 3] = f * b[1];
+      }
+  } else if constexpr (ST == kF32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * u + e] = f * __uint_as_float(raw[u][e]);
+  } else if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[8 * u + e] = f * bf2f((e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu);
+        v[8 * u + e] = f * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+      }
+  }
+}
+
+template <int ST, int KW>
 __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
-  // Dynamic LDS, per wave (flush_lds_bytes): old scales | row max, new scale,
-  // 1/scale (96 floats), then x [L][64] and B [L][128] of the ring tokens.
-  extern __shared__ __align__(16) uint8_t flush_smem[];
+  using WC = Win<KW>;
+  using V = typename WC::V;
+  constexpr int kE = WC::kE;
+  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
+  constexpr int kNLD = 2 * kEB;
+  __shared__ uint16_t xT_all[kWaves][kHeadDim * WC::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
   const int h = (blockIdx.x - j * htiles) * kWaves + wave;
@@ -772,156 +805,114 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
     if (h == 0 && lane == 0 && c.status) atomicOr(c.status, SSU_STATUS_BAD_RING);
     return;
   }
-  const int g = h / c.hpg, cl = lane & 15, rsub = lane >> 4;
-  uint8_t *wsm = flush_smem + wave * flush_lds_bytes(L);
-  float *rs = reinterpret_cast<float *>(wsm);
-  uint16_t *xs = reinterpret_cast<uint16_t *>(wsm + (kHeadDim + 32) * 4);
-  uint16_t *bs = xs + L * kHeadDim;
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  constexpr int kRowBytes = kDState * kEB;
+  const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
+  uint16_t *xT = xT_all[wave];
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // 1. loads, all issued before any arithmetic: the checkpoint (lane (c, r)
-  //    owns elements 8c..8c+7 of rows p = 4 t + r), the old fp8 row scale,
-  //    dt' (lane s), and the first ring tokens' x (lane l: token l/8, chunk
-  //    l%8) and B (lane l: token l/16, chunk l%16).
-  u32x4 raw16[16];
-  u32x4 raw32[16][2];
-  u32x2 raw8[16];
+  // 1. loads, issued before any arithmetic: the checkpoint (fp32: per row
+  //    block, below), the old fp8 row scales of rows 16 rb + m, dt' (lane s),
+  //    the B values of the lane's A operand (tokens s = kE q + e, values
+  //    n = 32 (m / 4) + 8 (m % 4) + 0..7) and the x window.
+  u32x4 raw[ST == kF32 ? 1 : 4][kNLD];
+  if constexpr (ST != kF32) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const uint8_t *rowp = hp + (4 * t + rsub) * kRowBytes + cl * 8 * kEB;
-    if constexpr (ST == kFP8) {
-      raw8[t] = ld8_nt(rowp);
-    } else if constexpr (ST == kF32) {
-      raw32[t][0] = ld16_nt(rowp);
-      raw32[t][1] = ld16_nt(rowp + 16);
-    } else {
-      raw16[t] = ld16_nt(rowp);
-    }
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int u = 0; u < kNLD; ++u) raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
   }
   float *scp = nullptr;
-  float old_scale = 1.f;
+  float osc[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (ST == kFP8) {
     scp = reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
-    old_scale = scp[lane];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) osc[rb] = scp[16 * rb + m];
   }
   const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)slot * c.dt_stride) + h * L;
   const float dtp = lane < k ? dtring[ring_pos(r, lane, L)] : 0.f;
-  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
-                          (int64_t)h * L * kHeadDim;
   const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
                           (int64_t)g * L * kDState;
-  u32x4 xr = {0u, 0u, 0u, 0u}, br = {0u, 0u, 0u, 0u};
-  if ((lane >> 3) < k) xr = ld16(xring + ring_pos(r, lane >> 3, L) * kHeadDim + (lane & 7) * 8);
-  if ((lane >> 4) < k) br = ld16(Bring + ring_pos(r, lane >> 4, L) * kDState + (lane & 15) * 8);
+  u32x4 bw[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    const int sg = kE * q + e;
+    bw[e] = sg < k ? ld16(Bring + ring_pos(r, sg, L) * kDState + 32 * (m >> 2) + 8 * (m & 3)) : zero4;
+  }
+  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
+                          (int64_t)h * L * kHeadDim;
+  u32x4 xw[WC::kRounds];
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    xw[jj] = sg < k ? ld16(xring + ring_pos(r, sg, L) * kHeadDim + pc * 8) : zero4;
+  }
 
-  // 2. decay prefix and fold coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s;
-  //    ring tokens -> LDS (tokens past the first 8 / 4 are loaded here)
-  const float cum = scan32(A[h] * dtp, lane);
+  // 2. decay prefix, fold coefficients, x window -> LDS transposed to
+  //    xT[p][s] (zero for s >= k)
+  const float cum = scan_win<KW>(A[h] * dtp, lane);
   const float ctot = __shfl(cum, k - 1, 64);
   const float coef = lane < k ? expf(ctot - cum) * dtp : 0.f;
   const float D0 = expf(ctot);
-  if constexpr (ST == kFP8) rs[lane] = old_scale;
-  if ((lane >> 3) < k) st16(xs + (lane >> 3) * kHeadDim + (lane & 7) * 8, xr);
-  if ((lane >> 4) < k) st16(bs + (lane >> 4) * kDState + (lane & 15) * 8, br);
-  for (int s0 = 8; s0 < k; s0 += 8) {
-    const int sg = s0 + (lane >> 3);
-    if (sg < k) st16(xs + sg * kHeadDim + (lane & 7) * 8, ld16(xring + ring_pos(r, sg, L) * kHeadDim + (lane & 7) * 8));
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      xT[(pc * 8 + tt) * WC::kXS + sg] =
+          (uint16_t)((tt & 1) ? (xw[jj][tt >> 1] >> 16) : (xw[jj][tt >> 1] & 0xFFFFu));
   }
-  for (int s0 = 4; s0 < k; s0 += 4) {
-    const int sg = s0 + (lane >> 4);
-    if (sg < k) st16(bs + sg * kDState + (lane & 15) * 8, ld16(Bring + ring_pos(r, sg, L) * kDState + (lane & 15) * 8));
+
+  // 3. A operands of the 8 tiles: ahi[nb][e] + alo[nb][e] (+ alo2) =
+  //    coef_s B_s[32 (m / 4) + 8 (m % 4) + nb], s = kE q + e
+  V ahi[8], alo[8], alo2[ST == kF32 ? 8 : 1];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    const float cf = __shfl(coef, kE * q + e, 64);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const float w = cf * bf2f((nb & 1) ? (bw[e][nb >> 1] >> 16) : (bw[e][nb >> 1] & 0xFFFFu));
+      const __bf16 hi = (__bf16)w;
+      const float r1 = w - (float)hi;
+      const __bf16 lo = (__bf16)r1;
+      ahi[nb][e] = hi;
+      alo[nb][e] = lo;
+      if constexpr (ST == kF32) alo2[nb][e] = (__bf16)(r1 - (float)lo);
+    }
   }
-  wave_sync();
+  wave_sync();  // xT written by this wave -> read below
 
-  float bc0[4][8], cf0[4];
-  load_fold_chunk(bs, 0, k, cl, coef, bc0, cf0);
-
-  // 3. quarter by quarter (16 rows): decode and decay, rank-k update, encode
+  // 4. row block by row block: decode and decay, rank-k update, encode
 #pragma unroll
-  for (int Q = 0; Q < 4; ++Q) {
-    float acc[4][8];
+  for (int rb = 0; rb < 4; ++rb) {
+    u32x4 rr[kNLD];
 #pragma unroll
-    for (int tq = 0; tq < 4; ++tq) {
-      const int t = 4 * Q + tq;
-      if constexpr (ST == kFP8) {
-        const float f = D0 * rs[4 * t + rsub];
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], false);
-          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw8[t][w], true);
-          acc[tq][4 * w + 0] = f * a[0];
-          acc[tq][4 * w + 1] = f * a[1];
-          acc[tq][4 * w + 2] = f * b[0];
-          acc[tq][4 * w + 3] = f * b[1];
-        }
-      } else if constexpr (ST == kF32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[tq][e] = D0 * __uint_as_float(raw32[t][e >> 2][e & 3]);
-      } else if constexpr (ST == kBF16) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[tq][e] = D0 * bf2f((e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? (raw16[t][e >> 1] >> 16) : (raw16[t][e >> 1] & 0xFFFFu);
-          acc[tq][e] = D0 * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-        }
-      }
+    for (int u = 0; u < kNLD; ++u) {
+      if constexpr (ST == kF32)
+        rr[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
+      else
+        rr[u] = raw[rb][u];
     }
-    fold_chunk(acc, bc0, cf0, xs, 0, k, Q, rsub);
-    for (int s0 = 4; s0 < k; s0 += 4) {
-      float bc[4][8], cf[4];
-      load_fold_chunk(bs, s0, k, cl, coef, bc, cf);
-      fold_chunk(acc, bc, cf, xs, s0, k, Q, rsub);
+    float v[32];
+    decode_quarter<ST>(rr, ST == kFP8 ? D0 * osc[rb] : D0, v);
+    const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + kE * q);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      f32x4 a = {v[nb], v[8 + nb], v[16 + nb], v[24 + nb]};
+      a = mfma_win<KW>(ahi[nb], xb, a);
+      a = mfma_win<KW>(alo[nb], xb, a);
+      if constexpr (ST == kF32) a = mfma_win<KW>(alo2[nb], xb, a);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[8 * jj + nb] = a[jj];
     }
-
+    float sc = 1.f, y = 1.f;
+    bool fast = true;
     if constexpr (ST == kFP8) {
-      // row max -> one lane per row computes scale and 1/scale -> every lane
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) {
-        const float mx = row16_max(max8_abs(acc[tq]));
-        if (cl == 0) rs[kHeadDim + 4 * tq + rsub] = mx;
-      }
-      wave_sync();
-      bool fast = true;
-      if (lane < 16) {
-        const float sc = fp8_row_scale(rs[kHeadDim + lane]);
-        const float y = 1.0f / sc;
-        scp[16 * Q + lane] = sc;
-        rs[kHeadDim + lane] = sc;
-        rs[kHeadDim + 16 + lane] = y;
-        fast = scale_fast(sc);
-      }
-      const bool all_fast = __all(fast);
-      wave_sync();
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) {
-        const int p = 16 * Q + 4 * tq + rsub;
-        const float sc = rs[kHeadDim + 4 * tq + rsub], y = rs[kHeadDim + 16 + 4 * tq + rsub];
-        st8_nt(hp + p * kRowBytes + cl * 8, all_fast ? fp8_encode8_fast(acc[tq], sc, y) : fp8_encode8_div(acc[tq], sc));
-      }
-      wave_sync();
-    } else {
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) {
-        uint8_t *rowp = hp + (16 * Q + 4 * tq + rsub) * kRowBytes + cl * 8 * kEB;
-        if constexpr (ST == kF32) {
-          st16_nt(rowp, u32x4{__float_as_uint(acc[tq][0]), __float_as_uint(acc[tq][1]),
-                              __float_as_uint(acc[tq][2]), __float_as_uint(acc[tq][3])});
-          st16_nt(rowp + 16, u32x4{__float_as_uint(acc[tq][4]), __float_as_uint(acc[tq][5]),
-                                   __float_as_uint(acc[tq][6]), __float_as_uint(acc[tq][7])});
-        } else if constexpr (ST == kBF16) {
-          st16_nt(rowp, u32x4{pack_bf16(acc[tq][0], acc[tq][1]), pack_bf16(acc[tq][2], acc[tq][3]),
-                              pack_bf16(acc[tq][4], acc[tq][5]), pack_bf16(acc[tq][6], acc[tq][7])});
-        } else {
-          st16_nt(rowp, u32x4{pack_f16(acc[tq][0], acc[tq][1]), pack_f16(acc[tq][2], acc[tq][3]),
-                              pack_f16(acc[tq][4], acc[tq][5]), pack_f16(acc[tq][6], acc[tq][7])});
-        }
-      }
+      sc = fp8_row_scale(quarter_row_max(v));
+      y = 1.0f / sc;
+      fast = __all(scale_fast(sc));
+      if (q == 0) scp[16 * rb + m] = sc;
     }
+    store_quarter<ST>(hp, rb, lane, v, sc, y, fast);
   }
 }
 
@@ -937,49 +928,40 @@ __global__ void ring_advance_kernel(KCache c, const int32_t *slot_idx, const int
 }
 
 // ---------------------------------------------------------------------------
-// INIT: encode fp32 prefill states (one workgroup per (entry, head), 16 rows
-// per wave) and clear the slot's rings.
+// INIT: encode fp32 prefill states (one workgroup per (entry, head), row
+// block w per wave: lane 16 q + m encodes quarter q of row 16 w + m) and
+// clear the slot's rings.
 // ---------------------------------------------------------------------------
 
 template <int ST>
 __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const float *states,
                                                                 int64_t states_stride,
                                                                 const int32_t *slot_idx) {
+  static_assert(kWaves == 4, "one row block per wave");
   const int j = blockIdx.x / c.H, h = blockIdx.x - j * c.H;
   const int slot = slot_idx[j];
   if (slot <= 0 || slot >= c.num_slots) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, cl = lane & 15, rsub = lane >> 4;
+  const int rb = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  constexpr int kRowBytes = kDState * kEB;
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
-  const float *src = states + (int64_t)j * states_stride + (int64_t)h * kHeadElems;
+  const float *src = states + (int64_t)j * states_stride + (int64_t)h * kHeadElems +
+                     (16 * rb + m) * kDState + 32 * q;
+  float v[32];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int p = wave * 16 + 4 * t + rsub;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(src + p * kDState + 8 * cl);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(src + p * kDState + 8 * cl + 4);
-    float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    uint8_t *rowp = hp + p * kRowBytes + cl * 8 * kEB;
-    if constexpr (ST == kFP8) {
-      const float sc = fp8_row_scale(row16_max(max8_abs(v)));
-      const float y = 1.0f / sc;
-      if (__all(scale_fast(sc)))
-        st8(rowp, fp8_encode8_fast(v, sc, y));
-      else
-        st8(rowp, fp8_encode8_div(v, sc));
-      if (cl == 0)
-        reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + p] = sc;
-    } else if constexpr (ST == kF32) {
-      st16(rowp, __builtin_bit_cast(u32x4, a));
-      st16(rowp + 16, __builtin_bit_cast(u32x4, b));
-    } else if constexpr (ST == kBF16) {
-      st16(rowp, u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
-                       pack_bf16(v[6], v[7])});
-    } else {
-      st16(rowp, u32x4{pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),
-                       pack_f16(v[6], v[7])});
-    }
+  for (int u = 0; u < 8; ++u) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 4 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * u + e] = a[e];
   }
+  float sc = 1.f, y = 1.f;
+  bool fast = true;
+  if constexpr (ST == kFP8) {
+    sc = fp8_row_scale(quarter_row_max(v));
+    y = 1.0f / sc;
+    fast = __all(scale_fast(sc));
+    if (q == 0) reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + 16 * rb + m] = sc;
+  }
+  store_quarter<ST>(hp, rb, lane, v, sc, y, fast);
 }
 
 __device__ __forceinline__ void zero_bytes(uint8_t *p, int64_t nbytes, int tid, int nthreads) {
@@ -1060,8 +1042,11 @@ template <int ST>
 hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                    int n, hipStream_t st) {
   const int htiles = (c.H + kWaves - 1) / kWaves;
-  flush_kernel<ST><<<dim3((unsigned)((int64_t)n * htiles)), dim3(kWaves * 64), kWaves * flush_lds_bytes(c.L),
-                     st>>>(c, slot_idx, num_fold, A, htiles);
+  const dim3 grid((unsigned)((int64_t)n * htiles)), block(kWaves * 64);
+  if (c.L <= 16)
+    flush_kernel<ST, 16><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+  else
+    flush_kernel<ST, 32><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   ring_advance_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);

@@ -58,10 +58,15 @@ class CacheSpec:
     ring_len: int = 16
     state_dtype: str = "bf16"
     slot_pad: int = 0  # bytes appended to every per-slot stride
+    state_layout: str = ""  # "tiled" (the library's layout, 64 x 128 heads) or "rowmajor"
 
     def __post_init__(self):
         assert self.state_dtype in DTYPES
         assert self.nheads % self.ngroups == 0
+        if not self.state_layout:
+            tiled_ok = (self.headdim, self.dstate) == (64, 128) and self.state_dtype != "f64"
+            self.state_layout = "tiled" if tiled_ok else "rowmajor"
+        assert self.state_layout in ("tiled", "rowmajor")
 
     # packed per-slot byte sizes
     def state_bytes(self):
@@ -91,6 +96,23 @@ class CacheSpec:
         )
 
 
+def tiled_index(eb: int) -> np.ndarray:
+    """Storage element index of each logical element (p, n) of a 64 x 128 head
+    in the tiled layout, as an array [64, 128].
+
+    Rows come in blocks of 16 (rb = p // 16, m = p % 16), each row in four
+    quarters of 32 values (q = n // 32, t = n % 32); quarter q of row p belongs
+    to lane l = 16 q + m and is cut into 16-byte chunks of ce = 16 // eb values;
+    chunk u = t // ce of lane l is the (64 u + l)-th chunk of the row block.
+    """
+    ce = 16 // eb
+    p = np.arange(64)[:, None]
+    n = np.arange(128)[None, :]
+    rb, m, q, t = p // 16, p % 16, n // 32, n % 32
+    lane = 16 * q + m
+    return rb * 2048 + (t // ce) * (64 * ce) + lane * ce + t % ce
+
+
 @dataclasses.dataclass
 class CacheArrays:
     spec: CacheSpec
@@ -107,12 +129,33 @@ class CacheArrays:
             self.ring_start)))
 
     # typed views of the packed part of one slot (for tests)
+    def _state_np_dtype(self):
+        return {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16,
+                "fp8": np.uint8, "f64": np.float64}[self.spec.state_dtype]
+
     def state_view(self, slot):
+        """Checkpoint elements of one slot in storage order, [H, P * N] (a view)."""
         s = self.spec
-        dt = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16,
-              "fp8": np.uint8, "f64": np.float64}[s.state_dtype]
         raw = self.state[slot, : s.state_bytes()]
-        return raw.view(dt).reshape(s.nheads, s.headdim, s.dstate)
+        return raw.view(self._state_np_dtype()).reshape(s.nheads, s.headdim * s.dstate)
+
+    def state_logical(self, slot):
+        """Checkpoint elements of one slot as [H, P, N] (a copy, logical order)."""
+        s = self.spec
+        v = self.state_view(slot)
+        if s.state_layout == "rowmajor":
+            return v.reshape(s.nheads, s.headdim, s.dstate).copy()
+        return v[:, tiled_index(ELEM_BYTES[s.state_dtype])]
+
+    def set_state_logical(self, slot, values):
+        """Write [H, P, N] logical elements into one slot's storage."""
+        s = self.spec
+        v = self.state_view(slot)
+        values = np.asarray(values, self._state_np_dtype()).reshape(s.nheads, s.headdim, s.dstate)
+        if s.state_layout == "rowmajor":
+            v[:] = values.reshape(s.nheads, -1)
+        else:
+            v[:, tiled_index(ELEM_BYTES[s.state_dtype])] = values
 
     def scale_view(self, slot):
         s = self.spec

@@ -30,7 +30,7 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
 def state_f64(cache, slot) -> np.ndarray:
     """Checkpoint value [H, P, N] decoded through torch's dtypes."""
     s = cache.spec
-    raw = cache.state_view(slot)
+    raw = cache.state_logical(slot)
     if s.state_dtype in ("f32", "f64"):
         return raw.astype(np.float64)
     if s.state_dtype == "bf16":

@@ -137,7 +137,7 @@ def test_init_state_encodes_and_clears(oracle, state_dtype, broadcast):
         if slot <= 0 or slot >= spec.num_slots:
             continue
         src = states[0] if broadcast else states[j]
-        raw = cache.state_view(slot)
+        raw = cache.state_logical(slot)
         if state_dtype == "f32":
             assert np.array_equal(raw, src)
         elif state_dtype == "bf16":

@@ -180,8 +180,9 @@ def test_dt_zero_identity(oracle, state_dtype):
     cache, step = _zero_dt(cache, step)
     if state_dtype == "fp8":
         for s_ in range(spec.num_slots):
-            v = cache.state_view(s_)
+            v = cache.state_logical(s_)
             v[:, :, 0] = 0x7E  # +448 in every row
+            cache.set_state_logical(s_, v)
     before = cache.copy()
     out, st = oracle.replay_step(cache, step)
     assert st == 0
@@ -232,7 +233,7 @@ def test_A_zero_h0_zero_is_causal_linear_attention(oracle):
     spec, cache, step = _small_case("f64", seed=61, pnat_max=5, T=3)
     step.A[:] = 0.0
     for s_ in range(spec.num_slots):
-        cache.state_view(s_)[:] = 0.0
+        cache.state_view(s_)[:] = 0.0  # zero in any layout
     before = cache.copy()
     out, _ = oracle.replay_step(cache, step)
     for b in range(step.batch):
