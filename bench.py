@@ -24,9 +24,11 @@ dominant kernel, CPU-oracle baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -118,6 +120,7 @@ def main():
     from synth import device as sd
 
     wl = dict(WORKLOADS[args.workload])
+    wl_batch = wl["batch"]
     if args.batch:
         wl["batch"] = args.batch
     batch, H, G, T = wl["batch"], wl["nheads"], wl["ngroups"], wl["T"]
@@ -299,7 +302,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(dominant, args.workload) if batch == wl_batch else None,
         },
         "kernels": kernels,
         "cpu_baseline": cpu,
@@ -309,7 +312,8 @@ def main():
 
 def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
     """The CPU oracle (as it stands) on a bounded sample: the first 64 entries
-    of the first arena, step (+ flush), repeated until --cpu-seconds of work."""
+    of the first arena, step (+ flush), repeated until --cpu-seconds of work,
+    once with every OpenMP thread the host offers and once with one thread."""
     from oracle import ssu_oracle as O
     from synth import device as sd
 
@@ -320,23 +324,61 @@ def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
     host, smap = sd.download_subset(spec, tcache, slots)
     sub = sd.subset_step(step, entries, smap)
     k = flush_k[0].cpu().numpy()[:n] if flush_k else None
-    tokens = 0
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        c = host.copy()
-        O.replay_step(c, sub)
-        if k is not None:
-            O.flush(c, sub.slot_idx, k, sub.A)
-        tokens += sub.tokens
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or reps >= 1000:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+
+    def timed(seconds):
+        tokens = reps = 0
+        t0 = time.perf_counter()
+        while True:
+            c = host.copy()
+            O.replay_step(c, sub)
+            if k is not None:
+                O.flush(c, sub.slot_idx, k, sub.A)
+            tokens += sub.tokens
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                return tokens / el, reps, el
+
+    threads = O.max_threads()
+    v_all, reps, el = timed(args.cpu_seconds)
+    O.set_threads(1)
+    v_one, reps1, el1 = timed(args.cpu_seconds / 2)
+    O.set_threads(threads)
+    return {"value": v_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d entries of the first batch, step%s, repeated %d times (%.1f s)" % (
-                n, step.batch, " + flush" if k is not None else "", reps, el)}
+                n, step.batch, " + flush" if k is not None else "", reps, el),
+            "single_thread": {"value": v_one, "cores": 1, "repeats": reps1, "seconds": el1},
+            "host": {"os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_hbm_traffic.md, or None when that summary is
+    missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (kernel, workload))
+    src = os.path.join(ROOT, "speculative_replay_state_amd", "csrc", "ssu_kernels.hip")
+    try:
+        text = open(path).read()
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_val or m_sha.group(1) != sha:
+        return None
+    return float(m_val.group(1))
 
 
 if __name__ == "__main__":

@@ -217,7 +217,9 @@ int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *nu
 int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step);
 
 /* Work-unit threshold (batch * nheads) at or above which AUTO picks SPLIT.
- * Process-wide; set_ returns the previous value. */
+ * Process-wide; set_ returns the previous value.  The default is INT64_MAX
+ * (AUTO = monolith): on MI355X the split never overtook the monolith between
+ * 128 and 65536 work units. */
 int64_t ssu_get_split_threshold(void);
 int64_t ssu_set_split_threshold(int64_t work_units);
 

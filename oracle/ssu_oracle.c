@@ -68,6 +68,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_FP8 = 3, OR_F64 = 4 };
 
@@ -153,6 +154,11 @@ static void build_tables(void) {
 }
 
 void or_init_tables(void) { build_tables(); }
+
+/* Thread control for timing runs: the parallel loops over (entry, head) use
+ * at most this many OpenMP threads. */
+void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int or_max_threads(void) { return omp_get_max_threads(); }
 
 uint16_t or_enc_bf16(double v) {
   build_tables();

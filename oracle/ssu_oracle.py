@@ -76,6 +76,10 @@ def lib():
                 f = getattr(L, name)
                 f.restype = None
                 f.argtypes = [P, P, I64]
+            L.or_set_threads.restype = None
+            L.or_set_threads.argtypes = [I]
+            L.or_max_threads.restype = I
+            L.or_max_threads.argtypes = []
             L.or_init_tables()
             _lib = L
     return _lib
@@ -151,6 +155,15 @@ def init_state(cache, states, slot_idx, states_stride=None):
         states_stride = s.nheads * s.headdim * s.dstate
     lib().or_init_state(ctypes.byref(oc), states.ctypes.data, int(states_stride), _ptr(slots),
                         slots.shape[0])
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads the oracle's loops use from now on."""
+    lib().or_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().or_max_threads())
 
 
 def _arr(fn, a, in_dtype, out_dtype):
