@@ -111,8 +111,23 @@ def _as_orcache(cache) -> _OrCache:
         cache.ring_start.ctypes.data)
 
 
-def replay_step(cache, step):
-    """Replay step (see or_replay_step).  Returns (out fp64 [tokens, H, P], status)."""
+_STATUS_BAD_FOLD = 2
+
+
+def replay_step(cache, step, num_fold=None):
+    """Replay step (see or_replay_step).  Returns (out fp64 [tokens, H, P], status).
+
+    With num_fold ([batch] ints) the step is the fused flush-in-step: for each
+    entry the step would process (valid slot, 0 <= pnat, pnat + T_b <= L, a
+    valid ring_start and T_b within max_seqlen) and k = num_fold[b] in
+    [0, pnat], the first k live tokens are flushed into the checkpoint and the
+    step then runs with pnat - k live tokens from the new ring start; an entry
+    with k outside [0, pnat] is skipped like padding (zero output rows, cache
+    untouched) and reported with status bit 2.  This is by definition the
+    composition of flush and replay_step below.
+    """
+    if num_fold is not None:
+        return _fused_step(cache, step, np.asarray(num_fold, np.int32))
     s = cache.spec
     oc = _as_orcache(cache)
     ntok = step.tokens
@@ -132,6 +147,47 @@ def replay_step(cache, step):
                               _ptr(pnat), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
                               _ptr(D), _ptr(db), out.ctypes.data)
     return out, st
+
+
+def _fused_step(cache, step, k):
+    s = cache.spec
+    assert k.shape == (step.batch,)
+    if step.cu_seqlens is not None:
+        tb = np.diff(np.asarray(step.cu_seqlens, np.int64))
+    else:
+        tb = np.full(step.batch, step.T, np.int64)
+    slots = np.asarray(step.slot_idx, np.int32).copy()
+    pnat = np.asarray(step.pnat, np.int32).copy()
+    status = 0
+    fold_slots, fold_k = [], []
+    for b in range(step.batch):
+        sl, p = int(slots[b]), int(pnat[b])
+        if not (0 <= tb[b] <= step.T) or not (0 < sl < s.num_slots):
+            continue
+        if p < 0 or p + tb[b] > s.ring_len:
+            continue
+        if not (0 <= int(cache.ring_start[sl]) < s.ring_len):
+            continue
+        kb = int(k[b])
+        if kb < 0 or kb > p:
+            status |= _STATUS_BAD_FOLD
+            slots[b] = 0  # skipped like a padding entry
+            continue
+        if kb > 0:
+            fold_slots.append(sl)
+            fold_k.append(kb)
+            pnat[b] = p - kb
+    if fold_slots:
+        st = flush(cache, np.array(fold_slots, np.int32), np.array(fold_k, np.int32), step.A)
+        assert st == 0
+    sub = _replace(step, slot_idx=slots, pnat=pnat)
+    out, st = replay_step(cache, sub)
+    return out, st | status
+
+
+def _replace(step, **kw):
+    import dataclasses
+    return dataclasses.replace(step, **kw)
 
 
 def flush(cache, slot_idx, num_fold, A):

@@ -160,6 +160,51 @@ def test_flush_then_step_invariance(oracle):
     assert np.array_equal(out2, ref_out)
 
 
+def test_fused_flush_in_step_f64(oracle):
+    """The fused call (fold k <= pnat live tokens, then step) reads out exactly
+    what the plain step reads out (fp64 state), leaves the checkpoint at the
+    closed-form state after the k folded tokens, and advances ring_start by k."""
+    spec, cache, step = _small_case("f64", seed=37, pnat_max=5, T=3, batch=4, num_slots=8)
+    rng = np.random.default_rng(3)
+    k = np.array([rng.integers(0, int(p) + 1) for p in step.pnat], np.int32)
+    k[int(np.argmax(step.pnat))] = int(np.max(step.pnat))  # one entry folds its whole prefix
+    ref_out, _ = oracle.replay_step(cache.copy(), step)
+    c2 = cache.copy()
+    out2, st = oracle.replay_step(c2, step, num_fold=k)
+    assert st == 0
+    assert np.array_equal(out2, ref_out)
+    L = spec.ring_len
+    for b in range(step.batch):
+        slot, kb = int(step.slot_idx[b]), int(k[b])
+        assert int(c2.ring_start[slot]) == (int(cache.ring_start[slot]) + kb) % L
+        h0 = R.state_f64(cache, slot)
+        got = R.state_f64(c2, slot)
+        for h in range(spec.nheads):
+            seq = R.sequence(cache, step, b, h)
+            want = R.closed_form_state(h0[h], float(step.A[h]), seq["dtp"][:kb], seq["x"][:kb],
+                                       seq["B"][:kb])
+            assert _rel_err(got[h], want) <= 1e-12
+
+
+def test_fused_invalid_fold_is_skipped(oracle):
+    spec, cache, step = _small_case("f32", seed=41, pnat_max=4, T=2, batch=4, num_slots=8)
+    step.pnat[:] = [2, 3, 1, 0]
+    k = np.array([1, 4, -1, 0], np.int32)  # entries 1 (k > pnat) and 2 (k < 0) are invalid
+    before = cache.copy()
+    out, st = oracle.replay_step(cache, step, num_fold=k)
+    assert st == 2
+    T = step.T
+    assert np.all(out[1 * T:3 * T] == 0.0)
+    for b in (1, 2):
+        slot = int(step.slot_idx[b])
+        assert np.array_equal(cache.state[slot], before.state[slot])
+        assert np.array_equal(cache.x_cache[slot], before.x_cache[slot])
+        assert int(cache.ring_start[slot]) == int(before.ring_start[slot])
+    s0 = int(step.slot_idx[0])
+    assert int(cache.ring_start[s0]) == (int(before.ring_start[s0]) + 1) % spec.ring_len
+    assert not np.array_equal(cache.state[s0], before.state[s0])
+
+
 # --------------------------------------------------------------------------
 # special cases
 # --------------------------------------------------------------------------
