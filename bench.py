@@ -5,11 +5,15 @@
 
 One step = one pass of the whole hot path over one batch: the replay step
 (dt' softplus, decay prefix, C.B, checkpoint replay and readout, ring appends)
-followed, for the fp8 workload, by the flush (fold of the accepted tokens,
-fp8 re-encode, ring_start advance).  The default workload is the quantised-
+and, for the fp8 workload, the flush (fold of the accepted tokens, fp8
+re-encode, ring_start advance).  The default workload is the quantised-
 checkpoint configuration: batch 256 of the cache's slots, 128 heads in 8
 groups, headdim 64, dstate 128, fp8 e4m3 checkpoint with fp32 row scales,
-T = 4 new tokens, a flush of k ~ U{1..4} tokens after every step.
+T = 4 new tokens, k ~ U{1..4} accepted tokens flushed every step.  By
+default the flush is fused into the step: each call folds the k tokens the
+previous step accepted (pnat = num_fold = k) and then replays the 4 new ones,
+reading each checkpoint once; --no-fuse times the step with pnat = 0 followed
+by a separate ssu_flush of k tokens instead.
 
 Inputs are synthetic, drawn on the GPU (synth package) and resident in HBM
 before timing.  To measure HBM rather than the 256 MB Infinity Cache the
@@ -65,7 +69,7 @@ WORKLOADS = {
 ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
 
 
-def step_bytes(spec, H, G, pnat, Tb):
+def step_bytes(spec, H, G, pnat, Tb, out_bytes=2):
     """Algorithmic HBM bytes of one replay step (sum over entries): checkpoint
     (+ fp8 row scales) read, live-ring x/B/dt' read, new x/B/C/dt read, out
     written, x/B/dt' appended.  Scratch traffic of the split is excluded."""
@@ -77,9 +81,22 @@ def step_bytes(spec, H, G, pnat, Tb):
         tot += per_state
         tot += p * (H * P * 2 + G * N * 2 + H * 4)              # live ring reads
         tot += t * (H * P * 2 + 2 * G * N * 2 + H * 4)          # new x, B, C, dt
-        tot += t * H * P * 2                                    # out (bf16)
+        tot += t * H * P * out_bytes                            # out
         tot += t * (H * P * 2 + G * N * 2 + H * 4)              # appends
     return tot
+
+
+def state_bytes(spec, H):
+    """Checkpoint (+ fp8 row scales) bytes of one slot."""
+    return H * 64 * 128 * ELEM[spec.state_dtype] + (H * 64 * 4 if spec.state_dtype == "fp8" else 0)
+
+
+def fused_bytes(spec, H, G, k, Tb, out_bytes=2):
+    """Algorithmic bytes of one fused flush-in-step with pnat = k = num_fold:
+    a flush of k tokens and a step with no live tokens, minus the checkpoint
+    read the fusion saves for every entry that folds."""
+    saved = sum(state_bytes(spec, H) for kk in k if kk > 0)
+    return step_bytes(spec, H, G, [0] * len(k), Tb, out_bytes) + flush_bytes(spec, H, G, k) - saved
 
 
 def flush_bytes(spec, H, G, k):
@@ -105,6 +122,9 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--fuse", action=argparse.BooleanOptionalAction, default=True,
+                    help="flush workloads: fold the accepted tokens inside the replay step (one "
+                         "ssu_replay_step with num_fold) instead of a separate ssu_flush call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -121,6 +141,7 @@ def main():
 
     wl = dict(WORKLOADS[args.workload])
     wl_batch = wl["batch"]
+    fused = bool(wl["flush"]) and args.fuse
     if args.batch:
         wl["batch"] = args.batch
     batch, H, G, T = wl["batch"], wl["nheads"], wl["ngroups"], wl["T"]
@@ -154,27 +175,29 @@ def main():
         slots = np.sort(perm[a * batch:(a + 1) * batch]).astype(np.int32)
         stp = synth.make_step(spec, batch, T, args.seed + 17 * a + 1, wl["pnat_max"], varlen=wl["varlen"],
                               slots=slots, pnat_fixed=0 if wl["pnat_max"] == 0 else None)
+        if wl["flush"]:
+            k = synth.flush_counts(batch, wl["flush"][0], wl["flush"][1], args.seed + 31 * a + 5)
+            flush_k.append(torch.from_numpy(k).to(dev))
+            if fused:  # the k accepted tokens of the previous step are the live prefix, folded first
+                stp.pnat[:] = k
         steps_in.append(stp)
         t = sd.upload_step(stp, dev)
         t["out"] = torch.empty((stp.tokens, H, 64), dtype=out_dt, device=dev)
         tsteps.append(t)
-        if wl["flush"]:
-            k = synth.flush_counts(batch, wl["flush"][0], wl["flush"][1], args.seed + 31 * a + 5)
-            flush_k.append(torch.from_numpy(k).to(dev))
     ws = None
     algo_used = args.algo
     d0 = ssu.make_step_desc(batch, T, tsteps[0]["slot_idx"], tsteps[0]["pnat"], tsteps[0]["cu_seqlens"],
                             tsteps[0]["x"], tsteps[0]["B"], tsteps[0]["C"], tsteps[0]["dt"],
                             tsteps[0]["A"], tsteps[0]["D"], tsteps[0]["dt_bias"], tsteps[0]["out"],
-                            wl["out"], None, args.algo)
+                            wl["out"], None, args.algo, flush_k[0] if fused else None)
     resolved = ssu.ssu_resolve_algo(dc.desc(), d0)
     algo_used = {ssu.SSU_ALGO_MONOLITH: "monolith", ssu.SSU_ALGO_SPLIT: "split"}[resolved]
     if algo_used == "split":
         ws = torch.empty(ssu.workspace_size(dc, batch, T) // 4 + 1, dtype=torch.float32, device=dev)
-    for t in tsteps:
+    for a, t in enumerate(tsteps):
         descs.append(ssu.make_step_desc(batch, T, t["slot_idx"], t["pnat"], t["cu_seqlens"], t["x"],
                                         t["B"], t["C"], t["dt"], t["A"], t["D"], t["dt_bias"], t["out"],
-                                        wl["out"], ws, algo_used))
+                                        wl["out"], ws, algo_used, flush_k[a] if fused else None))
     cdesc = dc.desc()
 
     def one_step(i, ev=None):
@@ -188,7 +211,7 @@ def main():
             raise ssu.SsuError(rc, ssu.ssu_last_error())
         if ev is not None:
             ev[1].record(stream)
-        if wl["flush"]:
+        if wl["flush"] and not fused:
             t = tsteps[a]
             rc = ssu.ssu_flush(cdesc, t["slot_idx"].data_ptr(), flush_k[a].data_ptr(), t["A"].data_ptr(),
                                batch, sh)
@@ -238,16 +261,21 @@ def main():
         one_step(i, evs[i])
     torch.cuda.synchronize()
     step_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    flush_ms = [e[1].elapsed_time(e[2]) for e in evs] if wl["flush"] else []
+    flush_ms = [e[1].elapsed_time(e[2]) for e in evs] if (wl["flush"] and not fused) else []
 
     tokens_per_step = float(np.mean([s.tokens for s in steps_in]))
-    sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat if s.pnat is not None else [0] * batch,
-                                       np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch)
-                            for s in steps_in]))
-    fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy()) for k in flush_k])) if flush_k else 0.0
+    ob = 4 if wl["out"] == "f32" else 2
+    tbs = [np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch for s in steps_in]
+    if fused:
+        sbytes = float(np.mean([fused_bytes(spec, H, G, k.cpu().numpy(), tb, ob)
+                                for k, tb in zip(flush_k, tbs)]))
+        fbytes = 0.0
+    else:
+        sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat, tb, ob) for s, tb in zip(steps_in, tbs)]))
+        fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy()) for k in flush_k])) if flush_k else 0.0
     step_avg = float(np.mean(step_ms))
-    kernels = {"replay_step": {"algo": algo_used, "avg_us": 1e3 * step_avg, "bytes": sbytes,
-                               "GBps": sbytes / (step_avg * 1e6)}}
+    kernels = {"replay_step": {"algo": algo_used, "fused_flush": fused, "avg_us": 1e3 * step_avg,
+                               "bytes": sbytes, "GBps": sbytes / (step_avg * 1e6)}}
     dominant = "replay_step"
     if flush_ms:
         fl_avg = float(np.mean(flush_ms))
@@ -270,7 +298,7 @@ def main():
     # --- CPU oracle on a bounded sample of the same workload ----------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, spec, tcache, steps_in, flush_k)
+        cpu = cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused)
 
     line = {
         "metric": METRIC,
@@ -289,6 +317,9 @@ def main():
             "workload": args.workload + ": " + wl["desc"],
             "batch": batch, "nheads": H, "ngroups": G, "headdim": 64, "dstate": 128, "ring_len": 16,
             "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "algo": algo_used,
+            "flush": (None if not wl["flush"] else
+                      "fused into the replay step (ssu_replay_step with num_fold = pnat = k)" if fused
+                      else "separate ssu_flush after the step"),
             "arenas": arenas, "cache_slots": num_slots, "graph": graph is not None,
             "tokens_per_step": tokens_per_step,
             "algorithmic_bytes_per_step": sbytes + fbytes,
@@ -302,7 +333,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(dominant, args.workload) if batch == wl_batch else None,
+            "traffic": (measured_traffic(dominant, args.workload + ("_fused" if fused else ""))
+                        if batch == wl_batch else None),
         },
         "kernels": kernels,
         "cpu_baseline": cpu,
@@ -310,7 +342,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
+def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused):
     """The CPU oracle (as it stands) on a bounded sample: the first 64 entries
     of the first arena, step (+ flush), repeated until --cpu-seconds of work,
     once with every OpenMP thread the host offers and once with one thread."""
@@ -330,9 +362,12 @@ def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
         t0 = time.perf_counter()
         while True:
             c = host.copy()
-            O.replay_step(c, sub)
-            if k is not None:
-                O.flush(c, sub.slot_idx, k, sub.A)
+            if fused:
+                O.replay_step(c, sub, num_fold=k)
+            else:
+                O.replay_step(c, sub)
+                if k is not None:
+                    O.flush(c, sub.slot_idx, k, sub.A)
             tokens += sub.tokens
             reps += 1
             el = time.perf_counter() - t0
@@ -346,7 +381,8 @@ def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k):
     O.set_threads(threads)
     return {"value": v_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d entries of the first batch, step%s, repeated %d times (%.1f s)" % (
-                n, step.batch, " + flush" if k is not None else "", reps, el),
+                n, step.batch, (" with fused flush" if fused else " + flush") if k is not None else "",
+                reps, el),
             "single_thread": {"value": v_one, "cores": 1, "repeats": reps1, "seconds": el1},
             "host": {"os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}}
 

@@ -146,6 +146,9 @@ typedef struct ssu_cache {
  *   workspace / workspace_bytes: scratch for SPLIT, at least
  *               ssu_workspace_size(cache, batch, max_seqlen) bytes, 16-byte
  *               aligned; may be NULL for MONOLITH.
+ *   num_fold    [batch] i32 or NULL: fused flush-in-step (see ssu_replay_step).
+ *               Runs in the monolith: AUTO resolves to MONOLITH, an explicit
+ *               SPLIT returns SSU_ERR_UNSUPPORTED.
  * Requirements: 1 <= max_seqlen <= min(16, ring_len); pointers 16-byte
  * aligned (dt, A, D, dt_bias: 4-byte).  Active slots must be unique.
  */
@@ -166,6 +169,7 @@ typedef struct ssu_step {
   void *workspace;
   size_t workspace_bytes;
   ssu_algo algo;
+  const int32_t *num_fold;
 } ssu_step;
 
 /* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen):
@@ -196,6 +200,18 @@ int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_b
  * appended to the ring.  The checkpoint and ring_start are not modified, so
  * repeating a step with the same inputs gives the same result.
  * Requires pnat + T_b <= ring_len per entry (else SSU_STATUS_BAD_PNAT).
+ *
+ * Fused flush-in-step [FI, the checkpoint write path inside the replay
+ * kernel; Reviewer Notes]: with step->num_fold non-NULL, an entry with
+ * k = num_fold[b] in [1, pnat] first folds its first k live ring tokens into
+ * the checkpoint exactly as ssu_flush does (fp32 fold, re-encode, new fp8
+ * row scales), then reads out from the new checkpoint with the remaining
+ * pnat - k live tokens; after the call ring_start[slot] has advanced by k.
+ * The result equals ssu_flush(k) followed by this step with pnat - k, but the
+ * checkpoint is read once instead of twice.  k == 0 is a plain step; k < 0 or
+ * k > pnat skips the entry like padding (zero output rows, cache untouched)
+ * and sets SSU_STATUS_BAD_FOLD.  A fused step is not repeatable (it changes
+ * the checkpoint and ring_start).
  */
 int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t stream);
 

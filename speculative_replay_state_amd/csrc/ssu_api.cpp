@@ -154,11 +154,15 @@ int check_step(const ssu_cache *c, const ssu_step *s) {
     return fail(SSU_ERR_INVALID, "dt, A, D, dt_bias and the index arrays must be 4-byte aligned");
   if (s->algo != SSU_ALGO_AUTO && s->algo != SSU_ALGO_MONOLITH && s->algo != SSU_ALGO_SPLIT)
     return fail(SSU_ERR_INVALID, "unknown algo %d", (int)s->algo);
+  if (s->num_fold && !aligned4(s->num_fold)) return fail(SSU_ERR_INVALID, "num_fold must be 4-byte aligned");
+  if (s->num_fold && s->algo == SSU_ALGO_SPLIT)
+    return fail(SSU_ERR_UNSUPPORTED, "the fused flush (num_fold) runs in the monolith only; use AUTO or MONOLITH");
   return SSU_OK;
 }
 
 int resolve(const ssu_cache *c, const ssu_step *s) {
   if (s->algo == SSU_ALGO_MONOLITH || s->algo == SSU_ALGO_SPLIT) return s->algo;
+  if (s->num_fold) return SSU_ALGO_MONOLITH;
   const int64_t units = (int64_t)s->batch * c->nheads;
   return units >= g_split_threshold.load(std::memory_order_relaxed) ? SSU_ALGO_SPLIT : SSU_ALGO_MONOLITH;
 }
@@ -199,6 +203,7 @@ int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t st
   k.slot_idx = step->slot_idx;
   k.pnat = step->prev_num_accepted;
   k.cu = step->cu_seqlens;
+  k.fold = step->num_fold;
   k.x = static_cast<const uint16_t *>(step->x);
   k.B = static_cast<const uint16_t *>(step->B);
   k.C = static_cast<const uint16_t *>(step->C);

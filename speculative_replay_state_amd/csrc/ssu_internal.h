@@ -42,6 +42,7 @@ struct KStep {
   const int32_t *slot_idx;
   const int32_t *pnat;
   const int32_t *cu;  // NULL unless varlen
+  const int32_t *fold;  // NULL, or tokens to fold per entry before the readout (monolith only)
   const uint16_t *x;  // bf16 bits
   const uint16_t *B;
   const uint16_t *C;

@@ -152,8 +152,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // per-entry metadata and device-side contract checks
 // ---------------------------------------------------------------------------
 
+// pnat and r describe the replay window.  With a fused fold of k tokens they
+// are the values after the fold (pnat - k live tokens from ring_start + k);
+// r0 is the ring start the fold reads from.
 struct Entry {
   int slot, pnat, r, Tb, bos;
+  int k, r0;
   int mode;  // 0: skip entirely, 1: zero the output rows only, 2: replay
 };
 
@@ -169,6 +173,8 @@ __device__ __forceinline__ Entry load_entry(const KCache &c, const KStep &s, int
   e.slot = s.slot_idx[b];
   e.pnat = 0;
   e.r = 0;
+  e.k = 0;
+  e.r0 = 0;
   e.mode = 2;
   int bit = 0;
   if (e.Tb < 0 || e.Tb > s.T) {
@@ -183,9 +189,20 @@ __device__ __forceinline__ Entry load_entry(const KCache &c, const KStep &s, int
       bit = SSU_STATUS_BAD_PNAT;
     } else {
       e.r = c.ring_start[e.slot];
+      e.r0 = e.r;
       if (e.r < 0 || e.r >= c.L) {
         e.mode = 1;
         bit = SSU_STATUS_BAD_RING;
+      } else if (s.fold) {
+        const int k = s.fold[b];
+        if (k < 0 || k > e.pnat) {
+          e.mode = 1;
+          bit = SSU_STATUS_BAD_FOLD;
+        } else {
+          e.k = k;
+          e.r = ring_pos(e.r0, k, c.L);
+          e.pnat -= k;
+        }
       }
     }
   }
@@ -251,42 +268,74 @@ __device__ __forceinline__ float scan_win(float v, int lane) {
 // step's B rows to the group's ring (one writer per (entry, group)).
 // ---------------------------------------------------------------------------
 
+// Operands of the C.B MFMA tiles: C of new token m (k order n = 32 u + 8 q + e)
+// and B of combined index s = 16 nb + m (ring or new token).
 template <int KW>
-__device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, const Entry &e, int g,
-                                           bool append_B, int lane, f32x4 cb[KW / 16]) {
+struct CbLoads {
+  bf16x8 ca[4];
+  u32x4 bw[KW / 16][4];
+};
+
+template <int KW>
+__device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
+                                        CbLoads<KW> &cl) {
   const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
   const bf16x8 zero8 = {};
-  bf16x8 ca[4];
   const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + 32 * u + 8 * q)) : zero8;
-  uint16_t *Bring = reinterpret_cast<uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
-                    (int64_t)g * L * kDState;
+    cl.ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + 32 * u + 8 * q)) : zero8;
+  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
+                          (int64_t)g * L * kDState;
 #pragma unroll
   for (int nb = 0; nb < KW / 16; ++nb) {
     const int sig = nb * 16 + m;
-    u32x4 bw[4] = {};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cl.bw[nb][u] = u32x4{0u, 0u, 0u, 0u};
     if (sig < S) {
-      uint16_t *rp = Bring + ring_pos(e.r, sig, L) * kDState;
-      if (sig < e.pnat) {
+      const uint16_t *rp = sig < e.pnat ? Bring + ring_pos(e.r, sig, L) * kDState
+                                        : s.B + ((int64_t)(e.bos + sig - e.pnat) * c.G + g) * kDState;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) bw[u] = ld16(rp + 32 * u + 8 * q);
-      } else {
-        const uint16_t *ip = s.B + ((int64_t)(e.bos + sig - e.pnat) * c.G + g) * kDState;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) bw[u] = ld16(ip + 32 * u + 8 * q);
-        if (append_B) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) st16(rp + 32 * u + 8 * q, bw[u]);
-        }
-      }
+      for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + 32 * u + 8 * q);
     }
+  }
+}
+
+// This step's B rows -> the group's ring (one writer per (entry, group)).
+template <int KW>
+__device__ __forceinline__ void append_B_rows(const KCache &c, const Entry &e, int g, int lane,
+                                              const CbLoads<KW> &cl) {
+  const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
+  uint16_t *Bring = reinterpret_cast<uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) + (int64_t)g * L * kDState;
+#pragma unroll
+  for (int nb = 0; nb < KW / 16; ++nb) {
+    const int sig = nb * 16 + m;
+    if (sig >= e.pnat && sig < S) {
+      uint16_t *rp = Bring + ring_pos(e.r, sig, L) * kDState;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st16(rp + 32 * u + 8 * q, cl.bw[nb][u]);
+    }
+  }
+}
+
+template <int KW>
+__device__ __forceinline__ void cb_tiles(const CbLoads<KW> &cl, f32x4 cb[KW / 16]) {
+#pragma unroll
+  for (int nb = 0; nb < KW / 16; ++nb) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a = mfma_bf16(ca[u], __builtin_bit_cast(bf16x8, bw[u]), a);
+    for (int u = 0; u < 4; ++u) a = mfma_bf16(cl.ca[u], __builtin_bit_cast(bf16x8, cl.bw[nb][u]), a);
     cb[nb] = a;
   }
+}
+
+template <int KW>
+__device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, const Entry &e, int g,
+                                           bool append_B, int lane, f32x4 cb[KW / 16]) {
+  CbLoads<KW> cl;
+  load_cb<KW>(c, s, e, g, lane, cl);
+  if (append_B) append_B_rows<KW>(c, e, g, lane, cl);
+  cb_tiles<KW>(cl, cb);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,6 +369,278 @@ __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry
 }
 
 // ---------------------------------------------------------------------------
+// FLUSH: fold the first k live ring tokens into the checkpoint and re-encode
+// it.  One wave per (entry, head).  With coef_s = exp(cumA_{k-1} - cumA_s) dt'_s
+// and D0 = exp(cumA_{k-1}) the new checkpoint is D0 h0 + sum_{s<k} coef_s x_s B_s^T.
+// The rank-k update runs on MFMA in transposed form: for row block rb and
+// tile nb (0..7),
+//   acc_nb[r][c] += sum_s (coef_s B_s[n(r, nb)]) x_s[16 rb + c],
+//   n(r, nb) = 32 (r / 4) + 8 (r % 4) + nb,
+// so lane l = 16 q + m ends up holding values t = 8 j + nb (j = 0..3,
+// nb = 0..7) of quarter q of row 16 rb + m: exactly its own chunks of the
+// tiled checkpoint, and decode, update, row max and encode stay in registers.
+// coef_s B_s is split into bf16 hi + lo (+ lo2 for fp32 state) parts; x is
+// bf16 and exact.  The A operands do not depend on rb and are built once.
+// ---------------------------------------------------------------------------
+
+// fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448):
+// the quotient v / sc, correctly rounded, is taken from y = fp32(1 / sc) with
+// one residual step (Markstein's correction: y correctly rounded and v * y
+// within one ulp give the correctly rounded quotient; valid for sc in
+// [2^-60, 2^100]).  No clamp is needed: |v| <= max|row| bounds |v / sc| by
+// 448 (1 + 2^-23), which the round-to-nearest conversion maps to 448.
+__device__ __forceinline__ u32x2 fp8_encode8_fast(const float *v, float sc, float y) {
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q0 = v[e] * y;
+    const float r = fmaf(-q0, sc, v[e]);
+    qv[e] = fmaf(r, y, q0);
+  }
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+// Same with the plain IEEE division (scales outside that range).
+__device__ __forceinline__ u32x2 fp8_encode8_div(const float *v, float sc) {
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = __builtin_amdgcn_fmed3f(v[e] / sc, -448.0f, 448.0f);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+__device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && sc <= 0x1p100f; }
+
+// Max |v| over the 32 values t of a lane's quarter row, then over the four
+// lanes (q = 0..3) that hold the same row.
+__device__ __forceinline__ float quarter_row_max(const float *v) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int t = 0; t < 32; t += 2) {
+    a = fmaxf(a, fabsf(v[t]));
+    b = fmaxf(b, fabsf(v[t + 1]));
+  }
+  float mx = fmaxf(a, b);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+// Encodes the 32 values of one quarter row (value t in v[t]) into the lane's
+// 16-byte chunks of a row block (2 * element bytes of them); fp8 uses the
+// row scale sc and y = fp32(1 / sc) (fast: Markstein quotient valid).
+template <int ST>
+__device__ __forceinline__ void encode_quarter(const float *v, float sc, float y, bool fast, u32x4 *ch) {
+  if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const u32x2 lo = fast ? fp8_encode8_fast(v + 16 * u, sc, y) : fp8_encode8_div(v + 16 * u, sc);
+      const u32x2 hi = fast ? fp8_encode8_fast(v + 16 * u + 8, sc, y) : fp8_encode8_div(v + 16 * u + 8, sc);
+      ch[u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  } else if constexpr (ST == kF32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      ch[u] = u32x4{__float_as_uint(v[4 * u]), __float_as_uint(v[4 * u + 1]), __float_as_uint(v[4 * u + 2]),
+                    __float_as_uint(v[4 * u + 3])};
+  } else if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      ch[u] = u32x4{pack_bf16(v[8 * u], v[8 * u + 1]), pack_bf16(v[8 * u + 2], v[8 * u + 3]),
+                    pack_bf16(v[8 * u + 4], v[8 * u + 5]), pack_bf16(v[8 * u + 6], v[8 * u + 7])};
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      ch[u] = u32x4{pack_f16(v[8 * u], v[8 * u + 1]), pack_f16(v[8 * u + 2], v[8 * u + 3]),
+                    pack_f16(v[8 * u + 4], v[8 * u + 5]), pack_f16(v[8 * u + 6], v[8 * u + 7])};
+  }
+}
+
+template <int ST>
+__device__ __forceinline__ void store_chunks(uint8_t *hp, int rb, int lane, const u32x4 *ch) {
+  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
+#pragma unroll
+  for (int u = 0; u < 2 * kEB; ++u) st16_nt(hp + tile_chunk(rb, u, lane, kEB), ch[u]);
+}
+
+// Decodes one lane's chunks of a row block into v[t] (t = 0..31), times f.
+template <int ST>
+__device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, float *v) {
+  if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], true);
+        v[16 * u + 4 * w + 0] = f * a[0];
+        v[16 * u + 4 * w + 1] = f * a[1];
+        v[16 * u + 4 * w + 2] = f * b[0];
+        v[16 * u + 4 * w + 3] = f * b[1];
+      }
+  } else if constexpr (ST == kF32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * u + e] = f * __uint_as_float(raw[u][e]);
+  } else if constexpr (ST == kBF16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[8 * u + e] = f * bf2f((e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu);
+        v[8 * u + e] = f * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+      }
+  }
+}
+
+// What the fold of one (slot, head) reads besides the checkpoint, in two
+// parts.  Per head: dt' of ring token s in lane s < k, the x window of the k
+// tokens and, for fp8, the old scales of rows 16 rb + m.  Per group: the B
+// values of the lane's A operands (tokens s = kE q + e, values
+// n = 32 (m / 4) + 8 (m % 4) + 0..7).
+template <int ST, int KW>
+struct FoldHeadLoads {
+  float dtp;
+  u32x4 xw[Win<KW>::kRounds];
+  float osc[4];
+};
+
+template <int KW>
+struct FoldBLoads {
+  u32x4 bw[Win<KW>::kE];
+};
+
+template <int ST, int KW>
+__device__ __forceinline__ void load_fold_head(const KCache &c, int slot, int h, int r, int k, int lane,
+                                               FoldHeadLoads<ST, KW> &fl) {
+  using WC = Win<KW>;
+  const int m = lane & 15, L = c.L;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = 1.f;
+  if constexpr (ST == kFP8) {
+    const float *scp = reinterpret_cast<const float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = scp[16 * rb + m];
+  }
+  const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)slot * c.dt_stride) + h * L;
+  fl.dtp = lane < k ? dtring[ring_pos(r, lane, L)] : 0.f;
+  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
+                          (int64_t)h * L * kHeadDim;
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    fl.xw[jj] = sg < k ? ld16(xring + ring_pos(r, sg, L) * kHeadDim + pc * 8) : zero4;
+  }
+}
+
+template <int KW>
+__device__ __forceinline__ void load_fold_B(const KCache &c, int slot, int g, int r, int k, int lane,
+                                            FoldBLoads<KW> &fb) {
+  using WC = Win<KW>;
+  const int m = lane & 15, q = lane >> 4, L = c.L;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
+                          (int64_t)g * L * kDState;
+#pragma unroll
+  for (int e = 0; e < WC::kE; ++e) {
+    const int sg = WC::kE * q + e;
+    fb.bw[e] = sg < k ? ld16(Bring + ring_pos(r, sg, L) * kDState + 32 * (m >> 2) + 8 * (m & 3)) : zero4;
+  }
+}
+
+// The fold's operands: A operands of the 8 tiles, ahi[nb][e] + alo[nb][e]
+// (+ alo2) = coef_s B_s[32 (m / 4) + 8 (m % 4) + nb] for s = kE q + e, and the
+// checkpoint decay D0.
+template <int ST, int KW>
+struct FoldOps {
+  typename Win<KW>::V ahi[8], alo[8], alo2[ST == kF32 ? 8 : 1];
+  float D0;
+};
+
+// Decay prefix and coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s,
+// D0 = exp(cumA_{k-1}); the x window goes to LDS transposed, xT[p][s] (zero
+// for s >= k).  The caller orders the LDS writes before the MFMA reads.
+template <int ST, int KW>
+__device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<ST, KW> &fl,
+                                           const FoldBLoads<KW> &fb, uint16_t *xT, int lane, FoldOps<ST, KW> &fo) {
+  using WC = Win<KW>;
+  constexpr int kE = WC::kE;
+  const int q = lane >> 4;
+  const float cum = scan_win<KW>(Ah * fl.dtp, lane);
+  const float ctot = __shfl(cum, k - 1, 64);
+  const float coef = lane < k ? expf(ctot - cum) * fl.dtp : 0.f;
+  fo.D0 = expf(ctot);
+#pragma unroll
+  for (int jj = 0; jj < WC::kRounds; ++jj) {
+    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      xT[(pc * 8 + tt) * WC::kXS + sg] =
+          (uint16_t)((tt & 1) ? (fl.xw[jj][tt >> 1] >> 16) : (fl.xw[jj][tt >> 1] & 0xFFFFu));
+  }
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    const float cf = __shfl(coef, kE * q + e, 64);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const float w = cf * bf2f((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu));
+      const __bf16 hi = (__bf16)w;
+      const float r1 = w - (float)hi;
+      const __bf16 lo = (__bf16)r1;
+      fo.ahi[nb][e] = hi;
+      fo.alo[nb][e] = lo;
+      if constexpr (ST == kF32) fo.alo2[nb][e] = (__bf16)(r1 - (float)lo);
+    }
+  }
+}
+
+// One row block of the fold: decode and decay the lane's chunks ch (old
+// checkpoint), add the rank-k update, re-encode into ch (new checkpoint) and
+// return the fp8 row scale of row 16 rb + m (1 for other dtypes).
+template <int ST, int KW>
+__device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb, int lane,
+                                               float old_scale, u32x4 *ch) {
+  using WC = Win<KW>;
+  using V = typename WC::V;
+  const int m = lane & 15, q = lane >> 4;
+  float v[32];
+  decode_quarter<ST>(ch, ST == kFP8 ? fo.D0 * old_scale : fo.D0, v);
+  const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    f32x4 a = {v[nb], v[8 + nb], v[16 + nb], v[24 + nb]};
+    a = mfma_win<KW>(fo.ahi[nb], xb, a);
+    a = mfma_win<KW>(fo.alo[nb], xb, a);
+    if constexpr (ST == kF32) a = mfma_win<KW>(fo.alo2[nb], xb, a);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v[8 * jj + nb] = a[jj];
+  }
+  float sc = 1.f, y = 1.f;
+  bool fast = true;
+  if constexpr (ST == kFP8) {
+    sc = fp8_row_scale(quarter_row_max(v));
+    y = 1.0f / sc;
+    fast = __all(scale_fast(sc));
+  }
+  encode_quarter<ST>(v, sc, y, fast, ch);
+  return sc;
+}
+
+// ---------------------------------------------------------------------------
 // The replay of one (entry, head) by one wave, in two phases so that a wave
 // can have the next head's loads in flight while this one computes:
 //   load_head  -- every global load of the head: the checkpoint tile (the
@@ -348,25 +669,26 @@ struct ItemLoads {
   f32x4 cbr[KW / 16];  // C.B[m][kE q .. kE q + kE - 1]
 };
 
+// The checkpoint tile of (slot, h): 16-byte chunks, 1 KiB contiguous per wave
+// instruction, streamed (non-temporal).
 template <int ST, int KW>
-__device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
-                                          HeadLoads<ST, KW> &ld) {
+__device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int lane, HeadLoads<ST, KW> &ld) {
   using T = HeadLoads<ST, KW>;
-  using WC = Win<KW>;
-  const int m = lane & 15, q = lane >> 4;
-  const int H = c.H, L = c.L, S = e.pnat + e.Tb;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * T::kEB);
+  const uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * T::kEB);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, T::kEB));
-  if constexpr (ST == kFP8) {
-    const float *sp = reinterpret_cast<const float *>(c.scale + (int64_t)e.slot * c.scale_stride) +
-                      h * kHeadDim;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) ld.rscale[rb] = *reinterpret_cast<const f32x4 *>(sp + rb * 16 + 4 * q);
-  }
+}
+
+// The readout window of (entry, h): dt (ring dt' or raw dt + dt_bias) in lane
+// s and the x chunks of the combined window.
+template <int ST, int KW>
+__device__ __forceinline__ void load_window(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
+                                            HeadLoads<ST, KW> &ld) {
+  using WC = Win<KW>;
+  const int H = c.H, L = c.L, S = e.pnat + e.Tb;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   ld.dtv = 0.f;
   if (lane < S) {
     if (lane < e.pnat) {
@@ -387,6 +709,22 @@ __device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const
                       ? ld16_nt(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8)
                       : ld16_nt(s.x + ((int64_t)(e.bos + sig - e.pnat) * H + h) * kHeadDim + pc * 8);
   }
+}
+
+// Every per-head load of the replay: checkpoint, fp8 row scales of rows
+// 16 rb + 4 q + j, and the window.
+template <int ST, int KW>
+__device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
+                                          HeadLoads<ST, KW> &ld) {
+  const int q = lane >> 4;
+  load_state<ST, KW>(c, e.slot, h, lane, ld);
+  if constexpr (ST == kFP8) {
+    const float *sp = reinterpret_cast<const float *>(c.scale + (int64_t)e.slot * c.scale_stride) +
+                      h * kHeadDim;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) ld.rscale[rb] = *reinterpret_cast<const f32x4 *>(sp + rb * 16 + 4 * q);
+  }
+  load_window<ST, KW>(c, s, e, h, lane, ld);
 }
 
 template <int ST, int KW>
@@ -645,147 +983,11 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
   }
 }
 
-// ---------------------------------------------------------------------------
-// FLUSH: fold the first k live ring tokens into the checkpoint and re-encode
-// it.  One wave per (entry, head).  With coef_s = exp(cumA_{k-1} - cumA_s) dt'_s
-// and D0 = exp(cumA_{k-1}) the new checkpoint is D0 h0 + sum_{s<k} coef_s x_s B_s^T.
-// The rank-k update runs on MFMA in transposed form: for row block rb and
-// tile nb (0..7),
-//   acc_nb[r][c] += sum_s (coef_s B_s[n(r, nb)]) x_s[16 rb + c],
-//   n(r, nb) = 32 (r / 4) + 8 (r % 4) + nb,
-// so lane l = 16 q + m ends up holding values t = 8 j + nb (j = 0..3,
-// nb = 0..7) of quarter q of row 16 rb + m: exactly its own chunks of the
-// tiled checkpoint, and decode, update, row max and encode stay in registers.
-// coef_s B_s is split into bf16 hi + lo (+ lo2 for fp32 state) parts; x is
-// bf16 and exact.  The A operands do not depend on rb and are built once.
-// ---------------------------------------------------------------------------
-
-// fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448):
-// the quotient v / sc, correctly rounded, is taken from y = fp32(1 / sc) with
-// one residual step (Markstein's correction: y correctly rounded and v * y
-// within one ulp give the correctly rounded quotient; valid for sc in
-// [2^-60, 2^100]).  No clamp is needed: |v| <= max|row| bounds |v / sc| by
-// 448 (1 + 2^-23), which the round-to-nearest conversion maps to 448.
-__device__ __forceinline__ u32x2 fp8_encode8_fast(const float *v, float sc, float y) {
-  float qv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float q0 = v[e] * y;
-    const float r = fmaf(-q0, sc, v[e]);
-    qv[e] = fmaf(r, y, q0);
-  }
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-  return u32x2{(uint32_t)w0, (uint32_t)w1};
-}
-
-// Same with the plain IEEE division (scales outside that range).
-__device__ __forceinline__ u32x2 fp8_encode8_div(const float *v, float sc) {
-  float qv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qv[e] = __builtin_amdgcn_fmed3f(v[e] / sc, -448.0f, 448.0f);
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-  return u32x2{(uint32_t)w0, (uint32_t)w1};
-}
-
-__device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && sc <= 0x1p100f; }
-
-// Max |v| over the 32 values t of a lane's quarter row, then over the four
-// lanes (q = 0..3) that hold the same row.
-__device__ __forceinline__ float quarter_row_max(const float *v) {
-  float a = 0.f, b = 0.f;
-#pragma unroll
-  for (int t = 0; t < 32; t += 2) {
-    a = fmaxf(a, fabsf(v[t]));
-    b = fmaxf(b, fabsf(v[t + 1]));
-  }
-  float mx = fmaxf(a, b);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  return fmaxf(mx, __shfl_xor(mx, 32, 64));
-}
-
-// Encodes the 32 values of one quarter row (value t in v[t]) into the lane's
-// chunks of row block rb, and returns nothing; fp8 also needs the row scale.
-template <int ST>
-__device__ __forceinline__ void store_quarter(uint8_t *hp, int rb, int lane, const float *v, float sc, float y,
-                                              bool fast) {
-  if constexpr (ST == kFP8) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const u32x2 lo = fast ? fp8_encode8_fast(v + 16 * u, sc, y) : fp8_encode8_div(v + 16 * u, sc);
-      const u32x2 hi = fast ? fp8_encode8_fast(v + 16 * u + 8, sc, y) : fp8_encode8_div(v + 16 * u + 8, sc);
-      st16_nt(hp + tile_chunk(rb, u, lane, 1), u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-  } else if constexpr (ST == kF32) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      st16_nt(hp + tile_chunk(rb, u, lane, 4),
-              u32x4{__float_as_uint(v[4 * u]), __float_as_uint(v[4 * u + 1]), __float_as_uint(v[4 * u + 2]),
-                    __float_as_uint(v[4 * u + 3])});
-  } else if constexpr (ST == kBF16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st16_nt(hp + tile_chunk(rb, u, lane, 2),
-              u32x4{pack_bf16(v[8 * u], v[8 * u + 1]), pack_bf16(v[8 * u + 2], v[8 * u + 3]),
-                    pack_bf16(v[8 * u + 4], v[8 * u + 5]), pack_bf16(v[8 * u + 6], v[8 * u + 7])});
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st16_nt(hp + tile_chunk(rb, u, lane, 2),
-              u32x4{pack_f16(v[8 * u], v[8 * u + 1]), pack_f16(v[8 * u + 2], v[8 * u + 3]),
-                    pack_f16(v[8 * u + 4], v[8 * u + 5]), pack_f16(v[8 * u + 6], v[8 * u + 7])});
-  }
-}
-
-// Decodes one lane's chunks of a row block into v[t] (t = 0..31), times f.
-template <int ST>
-__device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, float *v) {
-  if constexpr (ST == kFP8) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], false);
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], true);
-        v[16 * u + 4 * w + 0] = f * a[0];
-        v[16 * u + 4 * w + 1] = f * a[1];
-        v[16 * u + 4 * w + 2] = f * b[0];
-        v[16 * u + 4 * w + 3] = f * b[1];
-      }
-  } else if constexpr (ST == kF32) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * u + e] = f * __uint_as_float(raw[u][e]);
-  } else if constexpr (ST == kBF16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[8 * u + e] = f * bf2f((e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu));
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu);
-        v[8 * u + e] = f * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-      }
-  }
-}
-
 template <int ST, int KW>
 __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
   using WC = Win<KW>;
-  using V = typename WC::V;
-  constexpr int kE = WC::kE;
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   constexpr int kNLD = 2 * kEB;
   __shared__ uint16_t xT_all[kWaves][kHeadDim * WC::kXS];
@@ -805,15 +1007,12 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
     if (h == 0 && lane == 0 && c.status) atomicOr(c.status, SSU_STATUS_BAD_RING);
     return;
   }
-  const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
+  const int m = lane & 15, q = lane >> 4;
   uint16_t *xT = xT_all[wave];
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // 1. loads, issued before any arithmetic: the checkpoint (fp32: per row
-  //    block, below), the old fp8 row scales of rows 16 rb + m, dt' (lane s),
-  //    the B values of the lane's A operand (tokens s = kE q + e, values
-  //    n = 32 (m / 4) + 8 (m % 4) + 0..7) and the x window.
+  // 1. loads, issued before any arithmetic (fp32: the checkpoint per row
+  //    block, below)
   u32x4 raw[ST == kF32 ? 1 : 4][kNLD];
   if constexpr (ST != kF32) {
 #pragma unroll
@@ -821,99 +1020,143 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
 #pragma unroll
       for (int u = 0; u < kNLD; ++u) raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
   }
-  float *scp = nullptr;
-  float osc[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (ST == kFP8) {
-    scp = reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) osc[rb] = scp[16 * rb + m];
-  }
-  const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)slot * c.dt_stride) + h * L;
-  const float dtp = lane < k ? dtring[ring_pos(r, lane, L)] : 0.f;
-  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
-                          (int64_t)g * L * kDState;
-  u32x4 bw[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) {
-    const int sg = kE * q + e;
-    bw[e] = sg < k ? ld16(Bring + ring_pos(r, sg, L) * kDState + 32 * (m >> 2) + 8 * (m & 3)) : zero4;
-  }
-  const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
-                          (int64_t)h * L * kHeadDim;
-  u32x4 xw[WC::kRounds];
-#pragma unroll
-  for (int jj = 0; jj < WC::kRounds; ++jj) {
-    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
-    xw[jj] = sg < k ? ld16(xring + ring_pos(r, sg, L) * kHeadDim + pc * 8) : zero4;
-  }
+  FoldHeadLoads<ST, KW> fl;
+  FoldBLoads<KW> fb;
+  load_fold_head<ST, KW>(c, slot, h, r, k, lane, fl);
+  load_fold_B<KW>(c, slot, h / c.hpg, r, k, lane, fb);
 
-  // 2. decay prefix, fold coefficients, x window -> LDS transposed to
-  //    xT[p][s] (zero for s >= k)
-  const float cum = scan_win<KW>(A[h] * dtp, lane);
-  const float ctot = __shfl(cum, k - 1, 64);
-  const float coef = lane < k ? expf(ctot - cum) * dtp : 0.f;
-  const float D0 = expf(ctot);
-#pragma unroll
-  for (int jj = 0; jj < WC::kRounds; ++jj) {
-    const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-      xT[(pc * 8 + tt) * WC::kXS + sg] =
-          (uint16_t)((tt & 1) ? (xw[jj][tt >> 1] >> 16) : (xw[jj][tt >> 1] & 0xFFFFu));
-  }
-
-  // 3. A operands of the 8 tiles: ahi[nb][e] + alo[nb][e] (+ alo2) =
-  //    coef_s B_s[32 (m / 4) + 8 (m % 4) + nb], s = kE q + e
-  V ahi[8], alo[8], alo2[ST == kF32 ? 8 : 1];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) {
-    const float cf = __shfl(coef, kE * q + e, 64);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const float w = cf * bf2f((nb & 1) ? (bw[e][nb >> 1] >> 16) : (bw[e][nb >> 1] & 0xFFFFu));
-      const __bf16 hi = (__bf16)w;
-      const float r1 = w - (float)hi;
-      const __bf16 lo = (__bf16)r1;
-      ahi[nb][e] = hi;
-      alo[nb][e] = lo;
-      if constexpr (ST == kF32) alo2[nb][e] = (__bf16)(r1 - (float)lo);
-    }
-  }
+  // 2. coefficients, xT, A operands
+  FoldOps<ST, KW> fo;
+  fold_setup<ST, KW>(A[h], k, fl, fb, xT, lane, fo);
   wave_sync();  // xT written by this wave -> read below
 
-  // 4. row block by row block: decode and decay, rank-k update, encode
+  // 3. row block by row block: decode and decay, rank-k update, encode, store
+  float *scp = reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    u32x4 rr[kNLD];
+    u32x4 ch[kNLD];
 #pragma unroll
     for (int u = 0; u < kNLD; ++u) {
       if constexpr (ST == kF32)
-        rr[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
+        ch[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
       else
-        rr[u] = raw[rb][u];
+        ch[u] = raw[rb][u];
     }
-    float v[32];
-    decode_quarter<ST>(rr, ST == kFP8 ? D0 * osc[rb] : D0, v);
-    const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + kE * q);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      f32x4 a = {v[nb], v[8 + nb], v[16 + nb], v[24 + nb]};
-      a = mfma_win<KW>(ahi[nb], xb, a);
-      a = mfma_win<KW>(alo[nb], xb, a);
-      if constexpr (ST == kF32) a = mfma_win<KW>(alo2[nb], xb, a);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[8 * jj + nb] = a[jj];
-    }
-    float sc = 1.f, y = 1.f;
-    bool fast = true;
-    if constexpr (ST == kFP8) {
-      sc = fp8_row_scale(quarter_row_max(v));
-      y = 1.0f / sc;
-      fast = __all(scale_fast(sc));
+    const float sc = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ch);
+    if constexpr (ST == kFP8)
       if (q == 0) scp[16 * rb + m] = sc;
-    }
-    store_quarter<ST>(hp, rb, lane, v, sc, y, fast);
+    store_chunks<ST>(hp, rb, lane, ch);
   }
+}
+
+// ---------------------------------------------------------------------------
+// FUSED flush-in-step: one wave per (entry, head).  An entry with k = fold[b]
+// > 0 first folds its first k live ring tokens into the checkpoint with the
+// flush's own device functions and keeps the re-encoded tile in registers;
+// the readout then replays the remaining pnat - k live tokens and the new
+// tokens from those very codes.  The result is that of a flush followed by
+// a step, with one read of the checkpoint instead of two.
+// The phases run in sequence (checkpoint loads issued as soon as the slot is
+// known, the fold, the readout's loads, the new tile's stores, the readout)
+// so that their registers do not add up and the kernel keeps three waves per
+// SIMD; those waves, not a prefetch buffer, keep the memory system busy, and
+// the tile's writes drain while the readout computes.  Each wave forms its
+// group's C.B itself (a few MFMAs); the wave of the group's first head
+// appends the group's B rows.
+// ---------------------------------------------------------------------------
+
+template <int ST, int OT, int KW>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : 3)))
+void fused_kernel(KCache c, KStep s, int htiles) {
+  __shared__ uint16_t xT_all[kWaves][kHeadDim * Win<KW>::kXS];
+  __shared__ float cbw_all[kWaves][kMaxTokens * kCbLds];
+  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int b = blockIdx.x / htiles;
+  const int h = (blockIdx.x - b * htiles) * kWaves + wave;
+  if (h >= c.H) return;
+  const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
+  uint16_t *xT = xT_all[wave];
+  float *cbw = cbw_all[wave];
+
+  // 1. the checkpoint as soon as the slot is known (in bounds for any valid
+  //    slot; discarded if the entry turns out to be skipped)
+  HeadLoads<ST, KW> ld;
+  {
+    const int slot = s.slot_idx[b];
+    if (slot > 0 && slot < c.num_slots) load_state<ST, KW>(c, slot, h, lane, ld);
+  }
+  const Entry e = load_entry(c, s, b, h == 0);
+  if (e.mode == 0) return;
+  if (e.mode == 1) {
+    zero_out_head<OT>(s, c.H, e, h, lane);
+    return;
+  }
+
+  // 2. fold the first k live tokens: the new tile replaces ld.raw, the new
+  //    fp8 row scales of rows 16 rb + m replace fl.osc
+  FoldHeadLoads<ST, KW> fl;  // fp8: the old scales even when k == 0
+  load_fold_head<ST, KW>(c, e.slot, h, e.r0, e.k, lane, fl);
+  if (e.k > 0) {
+    FoldBLoads<KW> fb;
+    load_fold_B<KW>(c, e.slot, g, e.r0, e.k, lane, fb);
+    FoldOps<ST, KW> fo;
+    fold_setup<ST, KW>(s.A[h], e.k, fl, fb, xT, lane, fo);
+    wave_sync();  // xT written by this wave -> read below
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+    wave_sync();  // the fold's xT reads done before the readout rewrites xT
+  }
+
+  // 3. the readout's loads, then the new tile's stores (in this order: one
+  //    counter tracks a wave's loads and stores in issue order, so loads
+  //    issued after the stores would wait for the writes)
+  load_window<ST, KW>(c, s, e, h, lane, ld);
+  ItemLoads<ST, KW> il;
+  load_item_c<ST, KW>(c, s, e, g, lane, il);
+  CbLoads<KW> cl;
+  load_cb<KW>(c, s, e, g, lane, cl);
+  if (e.k > 0) {
+    uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) store_chunks<ST>(hp, rb, lane, ld.raw[rb]);
+    if constexpr (ST == kFP8) {
+      float *scp = reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim;
+      if (q == 0) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) scp[16 * rb + m] = fl.osc[rb];
+      }
+    }
+  }
+  if constexpr (ST == kFP8) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ld.rscale[rb][j] = __shfl(fl.osc[rb], 4 * q + j, 64);  // row 16 rb + 4 q + j
+  }
+
+  // 4. C.B of the group, then the replay of the head from the (new) tile
+  if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl);
+  {
+    f32x4 cb[KW / 16];
+    cb_tiles<KW>(cl, cb);
+#pragma unroll
+    for (int nb = 0; nb < KW / 16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cbw[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
+    wave_sync();
+    load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
+  }
+  head_compute<ST, OT, KW>(c, s, e, h, ld, il, xT, lane);
+}
+
+// Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
+// entry the step folded (same validity rules as the step itself).
+__global__ void step_ring_advance_kernel(KCache c, KStep s) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= s.batch) return;
+  const Entry e = load_entry(c, s, b, false);
+  if (e.mode == 2 && e.k > 0) c.ring_start[e.slot] = e.r;
 }
 
 // Ring bookkeeping after a flush: ring_start <- (ring_start + k) mod L.
@@ -961,7 +1204,9 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
     fast = __all(scale_fast(sc));
     if (q == 0) reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + 16 * rb + m] = sc;
   }
-  store_quarter<ST>(hp, rb, lane, v, sc, y, fast);
+  u32x4 ch[2 * kEB];
+  encode_quarter<ST>(v, sc, y, fast, ch);
+  store_chunks<ST>(hp, rb, lane, ch);
 }
 
 __device__ __forceinline__ void zero_bytes(uint8_t *p, int64_t nbytes, int tid, int nthreads) {
@@ -1027,8 +1272,23 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
 }
 
 template <int ST, int OT>
+hipError_t fused_t(const KCache &c, const KStep &s, hipStream_t st) {
+  const int htiles = (c.H + kWaves - 1) / kWaves;
+  const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kWaves * 64);
+  if (c.L <= 16)
+    fused_kernel<ST, OT, 16><<<grid, block, 0, st>>>(c, s, htiles);
+  else
+    fused_kernel<ST, OT, 32><<<grid, block, 0, st>>>(c, s, htiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  step_ring_advance_kernel<<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
+  return hipGetLastError();
+}
+
+template <int ST, int OT>
 hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
+  if (s.fold) return fused_t<ST, OT>(c, s, st);
   return c.L <= 16 ? replay_kw<ST, OT, 16, false>(c, s, st) : replay_kw<ST, OT, 32, false>(c, s, st);
 }
 

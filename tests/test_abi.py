@@ -105,6 +105,8 @@ STEP_ERRORS = [
     (dict(algo=9), -1, "algo"),
     (dict(workspace=None), -4, "workspace"),
     (dict(workspace=FAKE, workspace_bytes=16), -4, "workspace"),
+    (dict(num_fold=FAKE), -2, "monolith only"),
+    (dict(num_fold=FAKE + 2, algo=0), -1, "num_fold"),
 ]
 
 
@@ -133,8 +135,16 @@ def test_workspace_size_and_algo_resolution(ssu):
         assert ssu.ssu_resolve_algo(c, s) == ssu.SSU_ALGO_MONOLITH
         s = _step(ssu, algo=ssu.SSU_ALGO_MONOLITH, batch=400)
         assert ssu.ssu_resolve_algo(c, s) == ssu.SSU_ALGO_MONOLITH
+        s = _step(ssu, algo=ssu.SSU_ALGO_AUTO, batch=400, num_fold=FAKE)  # fused: monolith
+        assert ssu.ssu_resolve_algo(c, s) == ssu.SSU_ALGO_MONOLITH
     finally:
         ssu.ssu_set_split_threshold(old)
+
+
+def test_auto_defaults_to_monolith(ssu):
+    c = _cache(ssu)
+    s = _step(ssu, algo=ssu.SSU_ALGO_AUTO, batch=100000)
+    assert ssu.ssu_resolve_algo(c, s) == ssu.SSU_ALGO_MONOLITH
 
 
 def test_empty_calls_are_noops(ssu):

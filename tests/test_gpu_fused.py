@@ -1,0 +1,190 @@
+"""GPU parity of the fused flush-in-step (replay step with num_fold).
+
+The oracle defines the fused call as a flush of the first k live tokens
+followed by the step with pnat - k.  Checked here on the GPU through the C
+ABI: outputs and cache against that oracle composition (bounds as for the
+step and the flush), the GPU's own flush-then-step bit for bit, k = 0 against
+the plain monolith step bit for bit, and invalid k reported and skipped.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import device as sd
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import gpu_harness as gh
+    import speculative_replay_state_amd as ssu
+from oracle import ssu_oracle as O
+from tests.test_gpu_replay import CASES, _setup
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _fold_counts(step, seed):
+    """k ~ U{0..pnat}, with the entry of largest pnat folding its whole prefix."""
+    rng = np.random.default_rng(seed)
+    k = np.array([rng.integers(0, int(p) + 1) for p in step.pnat], np.int32)
+    k[int(np.argmax(step.pnat))] = int(np.max(step.pnat))
+    return k
+
+
+def _run_fused(spec, cache, step, out_dtype, k, algo="auto"):
+    t = sd.upload_cache(cache, gh.DEV)
+    st = sd.upload_step(step, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    out = gh.out_tensor(step, spec, out_dtype)
+    kt = torch.from_numpy(np.asarray(k, np.int32)).to(gh.DEV)
+    desc = ssu.make_step_desc(step.batch, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"],
+                              st["B"], st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, out_dtype,
+                              None, algo, num_fold=kt)
+    ssu.replay_step(dc, desc)
+    torch.cuda.synchronize()
+    return out, sd.download_cache(spec, t), int(dc.status.item())
+
+
+def _check_state(spec, gpu, ref, before, touched):
+    untouched = [s for s in range(spec.num_slots) if s not in touched]
+    assert np.array_equal(gpu.state[untouched], before.state[untouched])
+    assert np.array_equal(gpu.state[:, spec.state_bytes():], before.state[:, spec.state_bytes():])
+    if not touched:
+        return
+    if spec.state_dtype == "fp8":
+        g = np.stack([gpu.state_view(s) for s in touched])
+        r = np.stack([ref.state_view(s) for s in touched])
+        frac, dist = gh.fp8_code_agreement(g, r)
+        assert frac >= 0.999 and dist <= 1, (frac, dist)
+        gs = np.stack([gpu.scale_view(s) for s in touched]).astype(np.float64)
+        rs = np.stack([ref.scale_view(s) for s in touched]).astype(np.float64)
+        assert np.max(np.abs(gs - rs) / rs) <= 1e-5
+    else:
+        g = np.stack([O.decode_state(gpu, s) for s in touched])
+        r = np.stack([O.decode_state(ref, s) for s in touched])
+        assert gh.rel_err(g, r) <= (1e-4 if spec.state_dtype == "f32" else 2e-2)
+
+
+def _state_propagation_bound(spec, step, k, gpu, ref_cache):
+    """Per output element, the most the readout can move between the GPU's
+    re-encoded checkpoint and the oracle's: the readout of token i is
+    beta_i C_i.h with beta_i = exp(cumA) <= 1 (A < 0, dt' >= 0), so the two
+    differ by at most sum_n |C_i[n]| |h_gpu[p, n] - h_ref[p, n]|.  The state
+    check bounds those differences (fp8: one code in at most 0.1 % of the
+    elements), and this lets the output check accept the readout of any
+    checkpoint that passes it."""
+    extra = np.zeros((step.tokens, spec.nheads, spec.headdim))
+    hpg = spec.nheads // spec.ngroups
+    C = R_bf16(step.C)
+    for b in range(step.batch):
+        slot = int(step.slot_idx[b])
+        if k[b] <= 0 or not 0 < slot < spec.num_slots:
+            continue
+        bos = int(step.cu_seqlens[b]) if step.cu_seqlens is not None else b * step.T
+        tb = (int(step.cu_seqlens[b + 1]) - bos) if step.cu_seqlens is not None else step.T
+        dh = np.abs(O.decode_state(gpu, slot) - O.decode_state(ref_cache, slot))  # [H, P, N]
+        for h in range(spec.nheads):
+            extra[bos:bos + tb, h, :] = np.abs(C[bos:bos + tb, h // hpg]) @ dh[h].T
+    return extra
+
+
+def R_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_fused_step_parity(case):
+    spec, cache, step, out_dtype = _setup(case, 3000 + len(case))
+    k = _fold_counts(step, 7 + len(case))
+    print("case", case, "k", k[:8], flush=True)
+    out, gpu, status = _run_fused(spec, cache, step, out_dtype, k)
+    assert status == 0
+    ref_cache = cache.copy()
+    ref, st = O.replay_step(ref_cache, step, num_fold=k)
+    assert st == 0
+    got = gh.to_f64(out)
+    extra = _state_propagation_bound(spec, step, k, gpu, ref_cache)
+    excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, out_dtype) * (1.0 + np.abs(ref)) - extra
+    assert np.all(excess <= 1e-12), "max excess %g (plain rel err %g)" % (np.max(excess), gh.rel_err(got, ref))
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
+    assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
+    assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
+    nb = spec.dt_bytes()
+    gd = gpu.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    rd = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    assert gh.rel_err(gd, rd) <= 1e-6
+    touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
+    _check_state(spec, gpu, ref_cache, cache, touched)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_fused_equals_gpu_flush_then_step(case):
+    """One fused pass gives the same bits as the flush kernel then the step."""
+    spec, cache, step, out_dtype = _setup(case, 4000 + len(case))
+    k = _fold_counts(step, 11 + len(case))
+    out_f, gpu_f, st_f = _run_fused(spec, cache, step, out_dtype, k)
+    assert st_f == 0
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    st = sd.upload_step(step, gh.DEV)
+    ssu.flush(dc, st["slot_idx"], torch.from_numpy(k).to(gh.DEV), st["A"])
+    step2 = synth.StepInputs(**{**step.__dict__, "pnat": (step.pnat - k).astype(np.int32)})
+    st2 = sd.upload_step(step2, gh.DEV)
+    out_s = gh.out_tensor(step, spec, out_dtype)
+    gh.run_step(dc, st2, step2, out_s, out_dtype, "monolith")
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == 0
+    gpu_s = sd.download_cache(spec, t)
+    view = torch.int32 if out_f.dtype == torch.float32 else torch.int16
+    assert torch.equal(out_f.view(view), out_s.view(view))
+    for f in sd.CACHE_FIELDS:
+        assert np.array_equal(getattr(gpu_f, f), getattr(gpu_s, f)), f
+
+
+@pytest.mark.parametrize("case", ["mtp_bf16", "fp8", "f32_T16_L32"])
+def test_fused_k0_equals_plain_step(case):
+    spec, cache, step, out_dtype = _setup(case, 5000 + len(case))
+    k = np.zeros(step.batch, np.int32)
+    out_f, gpu_f, st_f = _run_fused(spec, cache, step, out_dtype, k)
+    assert st_f == 0
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    st = sd.upload_step(step, gh.DEV)
+    out_s = gh.out_tensor(step, spec, out_dtype)
+    gh.run_step(dc, st, step, out_s, out_dtype, "monolith")
+    torch.cuda.synchronize()
+    view = torch.int32 if out_f.dtype == torch.float32 else torch.int16
+    assert torch.equal(out_f.view(view), out_s.view(view))
+    gpu_s = sd.download_cache(spec, t)
+    for f in sd.CACHE_FIELDS:
+        assert np.array_equal(getattr(gpu_f, f), getattr(gpu_s, f)), f
+
+
+def test_fused_invalid_fold_is_skipped_and_reported():
+    spec = synth.CacheSpec(num_slots=16, nheads=16, ngroups=2, state_dtype="fp8")
+    cache = synth.make_cache(spec, 61)
+    step = synth.make_step(spec, 6, 3, 62, 6)
+    step.pnat[:] = [3, 2, 4, 0, 5, 1]
+    k = np.array([2, 3, -1, 0, 5, 1], np.int32)  # entries 1 (k > pnat) and 2 (k < 0) invalid
+    out, gpu, status = _run_fused(spec, cache, step, "bf16", k)
+    assert status == ssu.SSU_STATUS_BAD_FOLD
+    ref_cache = cache.copy()
+    ref, st = O.replay_step(ref_cache, step, num_fold=k)
+    assert st == ssu.SSU_STATUS_BAD_FOLD
+    got = gh.to_f64(out)
+    assert np.all(got[3:9] == 0.0)
+    extra = _state_propagation_bound(spec, step, k, gpu, ref_cache)
+    assert np.all(np.abs(got - ref) <= 2e-2 * (1.0 + np.abs(ref)) + extra + 1e-12)
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
+    for b in (1, 2):
+        s = int(step.slot_idx[b])
+        assert np.array_equal(gpu.state[s], cache.state[s])
+        assert np.array_equal(gpu.x_cache[s], cache.x_cache[s])
+    touched = sorted({int(step.slot_idx[b]) for b in (0, 4, 5)})
+    _check_state(spec, gpu, ref_cache, cache, touched)
