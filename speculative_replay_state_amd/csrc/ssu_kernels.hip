@@ -45,7 +45,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;        // waves per workgroup in every kernel
+constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
+constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
 constexpr int kCbLds = 36;       // LDS row stride (fp32) of C.B in the monolith
 constexpr int kHeadElems = kHeadDim * kDState;
@@ -361,6 +362,43 @@ __device__ __forceinline__ void store_out(const KStep &s, int H, const Entry &e,
   }
 }
 
+// The same rows staged through LDS (ot: kOutTile words of this wave) so that
+// every global store is 16 contiguous bytes per lane and one instruction
+// covers whole 128-byte output rows (bf16: 8 token rows, fp32: 4).
+constexpr int kOutRowWords = 68;                       // 64 fp32 + 4 pad (bank spread)
+constexpr int kOutTile = kMaxTokens * kOutRowWords;    // 32-bit words per wave
+
+template <int OT>
+__device__ __forceinline__ void store_out_staged(const KStep &s, int H, const Entry &e, int h, int lane,
+                                                 const f32x4 acc[4], uint32_t *ot) {
+  const int m = lane & 15, q = lane >> 4;
+  if constexpr (OT == kOutF32) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      *reinterpret_cast<u32x4 *>(ot + m * kOutRowWords + rb * 16 + 4 * q) = __builtin_bit_cast(u32x4, acc[rb]);
+  } else {
+    // bf16 rows of 64 values = 32 words, same row pitch
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      *reinterpret_cast<u32x2 *>(ot + m * kOutRowWords + rb * 8 + 2 * q) =
+          u32x2{pack_bf16(acc[rb][0], acc[rb][1]), pack_bf16(acc[rb][2], acc[rb][3])};
+  }
+  wave_sync();
+  constexpr int kChunks = OT == kOutF32 ? 16 : 8;  // 16-byte chunks per token row
+  constexpr int kRowsPer = 64 / kChunks;           // token rows per instruction
+  const int c = lane % kChunks, i0 = lane / kChunks;
+#pragma unroll
+  for (int i = i0; i < kMaxTokens; i += kRowsPer) {
+    if (i < e.Tb) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + i * kOutRowWords + 4 * c);
+      uint8_t *dst = static_cast<uint8_t *>(s.out) +
+                     (((int64_t)(e.bos + i) * H + h) * kHeadDim) * (OT == kOutF32 ? 4 : 2) + 16 * c;
+      st16_nt(dst, v);
+    }
+  }
+  wave_sync();  // LDS reads done before the tile is reused
+}
+
 template <int OT>
 __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry &e, int h, int lane) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -383,24 +421,25 @@ __device__ __forceinline__ void zero_out_head(const KStep &s, int H, const Entry
 // bf16 and exact.  The A operands do not depend on rb and are built once.
 // ---------------------------------------------------------------------------
 
-// fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448):
-// the quotient v / sc, correctly rounded, is taken from y = fp32(1 / sc) with
-// one residual step (Markstein's correction: y correctly rounded and v * y
-// within one ulp give the correctly rounded quotient; valid for sc in
-// [2^-60, 2^100]).  No clamp is needed: |v| <= max|row| bounds |v / sc| by
-// 448 (1 + 2^-23), which the round-to-nearest conversion maps to 448.
-__device__ __forceinline__ u32x2 fp8_encode8_fast(const float *v, float sc, float y) {
-  float qv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float q0 = v[e] * y;
-    const float r = fmaf(-q0, sc, v[e]);
-    qv[e] = fmaf(r, y, q0);
-  }
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+// A lane's quarter row (32 values t of quarter q of row 16 rb + m) is held
+// as eight f32x4 MFMA accumulators in the fold's order: value t sits in
+// acc[t % 8][t / 8].  Decode, the fold's MFMAs, the row max and the encode
+// all work on that layout, so no value is ever moved between registers.
+#define QV(acc, t) (acc)[(t) & 7][(t) >> 3]
+
+// fp8 encode of 8 values of a row whose scale is sc = fp32(max|row| / 448),
+// fast form: q = v * y with y = fp32(1 / sc).  The product is within one ulp
+// of the correctly rounded quotient v / sc, so the code can only differ from
+// the quotient's where that quotient lies within an ulp of a rounding
+// midpoint of e4m3 (the reciprocal reading of the encoder; such a code is one
+// step away).  No clamp is needed: |v| <= max|row| bounds |q| by
+// 448 (1 + 2^-22), which the round-to-nearest conversion maps to 448.  Valid
+// while y is a normal number: sc in [2^-60, 2^100].
+__device__ __forceinline__ u32x2 fp8_encode8_rcp(const float *v, float y) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * y, v[1] * y, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * y, v[3] * y, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * y, v[5] * y, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * y, v[7] * y, w1, true);
   return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
 
@@ -418,47 +457,55 @@ __device__ __forceinline__ u32x2 fp8_encode8_div(const float *v, float sc) {
 
 __device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && sc <= 0x1p100f; }
 
-// Max |v| over the 32 values t of a lane's quarter row, then over the four
-// lanes (q = 0..3) that hold the same row.
-__device__ __forceinline__ float quarter_row_max(const float *v) {
+// Max |v| over a lane's quarter row, then over the four lanes (q = 0..3) that
+// hold the same row.
+__device__ __forceinline__ float quarter_row_max(const f32x4 *acc) {
   float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int t = 0; t < 32; t += 2) {
-    a = fmaxf(a, fabsf(v[t]));
-    b = fmaxf(b, fabsf(v[t + 1]));
+  for (int nb = 0; nb < 8; ++nb) {
+    a = fmaxf(a, fmaxf(fabsf(acc[nb][0]), fabsf(acc[nb][1])));
+    b = fmaxf(b, fmaxf(fabsf(acc[nb][2]), fabsf(acc[nb][3])));
   }
   float mx = fmaxf(a, b);
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   return fmaxf(mx, __shfl_xor(mx, 32, 64));
 }
 
-// Encodes the 32 values of one quarter row (value t in v[t]) into the lane's
-// 16-byte chunks of a row block (2 * element bytes of them); fp8 uses the
-// row scale sc and y = fp32(1 / sc) (fast: Markstein quotient valid).
+// Encodes a quarter row into the lane's 16-byte chunks of a row block
+// (2 * element bytes of them; chunk u holds values t = u * (16 / eb) ...).
+// fp8 uses the row scale sc and y = fp32(1 / sc) (fast: y normal).
 template <int ST>
-__device__ __forceinline__ void encode_quarter(const float *v, float sc, float y, bool fast, u32x4 *ch) {
+__device__ __forceinline__ void encode_quarter(const f32x4 *acc, float sc, float y, bool fast, u32x4 *ch) {
   if constexpr (ST == kFP8) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const u32x2 lo = fast ? fp8_encode8_fast(v + 16 * u, sc, y) : fp8_encode8_div(v + 16 * u, sc);
-      const u32x2 hi = fast ? fp8_encode8_fast(v + 16 * u + 8, sc, y) : fp8_encode8_div(v + 16 * u + 8, sc);
+      float lo8[8], hi8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo8[i] = QV(acc, 16 * u + i);
+        hi8[i] = QV(acc, 16 * u + 8 + i);
+      }
+      const u32x2 lo = fast ? fp8_encode8_rcp(lo8, y) : fp8_encode8_div(lo8, sc);
+      const u32x2 hi = fast ? fp8_encode8_rcp(hi8, y) : fp8_encode8_div(hi8, sc);
       ch[u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   } else if constexpr (ST == kF32) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      ch[u] = u32x4{__float_as_uint(v[4 * u]), __float_as_uint(v[4 * u + 1]), __float_as_uint(v[4 * u + 2]),
-                    __float_as_uint(v[4 * u + 3])};
+      ch[u] = u32x4{__float_as_uint(QV(acc, 4 * u)), __float_as_uint(QV(acc, 4 * u + 1)),
+                    __float_as_uint(QV(acc, 4 * u + 2)), __float_as_uint(QV(acc, 4 * u + 3))};
   } else if constexpr (ST == kBF16) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      ch[u] = u32x4{pack_bf16(v[8 * u], v[8 * u + 1]), pack_bf16(v[8 * u + 2], v[8 * u + 3]),
-                    pack_bf16(v[8 * u + 4], v[8 * u + 5]), pack_bf16(v[8 * u + 6], v[8 * u + 7])};
+      ch[u] = u32x4{pack_bf16(QV(acc, 8 * u), QV(acc, 8 * u + 1)), pack_bf16(QV(acc, 8 * u + 2), QV(acc, 8 * u + 3)),
+                    pack_bf16(QV(acc, 8 * u + 4), QV(acc, 8 * u + 5)),
+                    pack_bf16(QV(acc, 8 * u + 6), QV(acc, 8 * u + 7))};
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      ch[u] = u32x4{pack_f16(v[8 * u], v[8 * u + 1]), pack_f16(v[8 * u + 2], v[8 * u + 3]),
-                    pack_f16(v[8 * u + 4], v[8 * u + 5]), pack_f16(v[8 * u + 6], v[8 * u + 7])};
+      ch[u] = u32x4{pack_f16(QV(acc, 8 * u), QV(acc, 8 * u + 1)), pack_f16(QV(acc, 8 * u + 2), QV(acc, 8 * u + 3)),
+                    pack_f16(QV(acc, 8 * u + 4), QV(acc, 8 * u + 5)),
+                    pack_f16(QV(acc, 8 * u + 6), QV(acc, 8 * u + 7))};
   }
 }
 
@@ -469,9 +516,10 @@ __device__ __forceinline__ void store_chunks(uint8_t *hp, int rb, int lane, cons
   for (int u = 0; u < 2 * kEB; ++u) st16_nt(hp + tile_chunk(rb, u, lane, kEB), ch[u]);
 }
 
-// Decodes one lane's chunks of a row block into v[t] (t = 0..31), times f.
+// Decodes one lane's chunks of a row block into the quarter-row layout,
+// times f.
 template <int ST>
-__device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, float *v) {
+__device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, f32x4 *acc) {
   if constexpr (ST == kFP8) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -479,29 +527,29 @@ __device__ __forceinline__ void decode_quarter(const u32x4 *raw, float f, float 
       for (int w = 0; w < 4; ++w) {
         const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], false);
         const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[u][w], true);
-        v[16 * u + 4 * w + 0] = f * a[0];
-        v[16 * u + 4 * w + 1] = f * a[1];
-        v[16 * u + 4 * w + 2] = f * b[0];
-        v[16 * u + 4 * w + 3] = f * b[1];
+        QV(acc, 16 * u + 4 * w + 0) = f * a[0];
+        QV(acc, 16 * u + 4 * w + 1) = f * a[1];
+        QV(acc, 16 * u + 4 * w + 2) = f * b[0];
+        QV(acc, 16 * u + 4 * w + 3) = f * b[1];
       }
   } else if constexpr (ST == kF32) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * u + e] = f * __uint_as_float(raw[u][e]);
+      for (int e = 0; e < 4; ++e) QV(acc, 4 * u + e) = f * __uint_as_float(raw[u][e]);
   } else if constexpr (ST == kBF16) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        v[8 * u + e] = f * bf2f((e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu));
+        QV(acc, 8 * u + e) = f * bf2f((e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu));
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bits = (e & 1) ? (raw[u][e >> 1] >> 16) : (raw[u][e >> 1] & 0xFFFFu);
-        v[8 * u + e] = f * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+        QV(acc, 8 * u + e) = f * (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
       }
   }
 }
@@ -617,26 +665,23 @@ __device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const 
   using WC = Win<KW>;
   using V = typename WC::V;
   const int m = lane & 15, q = lane >> 4;
-  float v[32];
-  decode_quarter<ST>(ch, ST == kFP8 ? fo.D0 * old_scale : fo.D0, v);
+  f32x4 acc[8];
+  decode_quarter<ST>(ch, ST == kFP8 ? fo.D0 * old_scale : fo.D0, acc);
   const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    f32x4 a = {v[nb], v[8 + nb], v[16 + nb], v[24 + nb]};
-    a = mfma_win<KW>(fo.ahi[nb], xb, a);
-    a = mfma_win<KW>(fo.alo[nb], xb, a);
-    if constexpr (ST == kF32) a = mfma_win<KW>(fo.alo2[nb], xb, a);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v[8 * jj + nb] = a[jj];
+    acc[nb] = mfma_win<KW>(fo.ahi[nb], xb, acc[nb]);
+    acc[nb] = mfma_win<KW>(fo.alo[nb], xb, acc[nb]);
+    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.alo2[nb], xb, acc[nb]);
   }
   float sc = 1.f, y = 1.f;
   bool fast = true;
   if constexpr (ST == kFP8) {
-    sc = fp8_row_scale(quarter_row_max(v));
+    sc = fp8_row_scale(quarter_row_max(acc));
     y = 1.0f / sc;
     fast = __all(scale_fast(sc));
   }
-  encode_quarter<ST>(v, sc, y, fast, ch);
+  encode_quarter<ST>(acc, sc, y, fast, ch);
   return sc;
 }
 
@@ -658,7 +703,8 @@ struct HeadLoads {
   u32x4 raw[4][kNLD];                   // lane l = 16 q + m: chunk u of quarter q of row 16 rb + m
   u32x4 xw[Win<KW>::kRounds];                // x window chunks
   f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
-  float dtv;                                 // lane s: stored dt' (s < pnat) or dt + dt_bias (new)
+  float dtv;                                 // lane s: stored dt' (s < pnat) or raw dt (new)
+  float dtb, Ah, Dh;                         // dt_bias[h], A[h], D[h]
 };
 
 // Per-(entry, group) loads: C of the new tokens and the C.B row of token m.
@@ -681,8 +727,11 @@ __device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int
     for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, T::kEB));
 }
 
-// The readout window of (entry, h): dt (ring dt' or raw dt + dt_bias) in lane
-// s and the x chunks of the combined window.
+// The readout window of (entry, h): dt in lane s (ring dt' or raw dt), the
+// head's dt_bias, A and D, and the x chunks of the combined window.  Nothing
+// loaded here is used before the head's compute phase: one counter tracks a
+// wave's loads in issue order, so using a value loaded here right away would
+// also wait for every load issued before it, including a prefetched tile.
 template <int ST, int KW>
 __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
                                             HeadLoads<ST, KW> &ld) {
@@ -695,9 +744,12 @@ __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, con
       const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
       ld.dtv = dtring[ring_pos(e.r, lane, L)];
     } else {
-      ld.dtv = s.dt[(int64_t)(e.bos + lane - e.pnat) * H + h] + s.dt_bias[h];
+      ld.dtv = s.dt[(int64_t)(e.bos + lane - e.pnat) * H + h];
     }
   }
+  ld.dtb = s.dt_bias[h];
+  ld.Ah = s.A[h];
+  ld.Dh = s.D[h];
   const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)e.slot * c.x_stride) +
                           (int64_t)h * L * kHeadDim;
 #pragma unroll
@@ -770,7 +822,7 @@ __device__ __forceinline__ void load_cb_row(const Entry &e, const float *cb, int
 template <int ST, int OT, int KW>
 __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, const Entry &e, int h,
                                              const HeadLoads<ST, KW> &ld, const ItemLoads<ST, KW> &il,
-                                             uint16_t *xT, int lane) {
+                                             uint16_t *xT, uint32_t *ot, int lane) {
   using WC = Win<KW>;
   using V = typename WC::V;
   const int m = lane & 15, q = lane >> 4;
@@ -781,11 +833,11 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   //    softplus'd and appended to the dt ring.  Then the inclusive decay prefix.
   float dtp = ld.dtv;
   if (lane >= e.pnat && lane < S) {
-    dtp = softplus_f(ld.dtv);
+    dtp = softplus_f(ld.dtv + ld.dtb);
     float *dtring = reinterpret_cast<float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
     dtring[ring_pos(e.r, lane, L)] = dtp;
   }
-  const float cum = scan_win<KW>(s.A[h] * dtp, lane);
+  const float cum = scan_win<KW>(ld.Ah * dtp, lane);
 
   // 2. x window -> LDS, transposed to xT[p][s]; new tokens appended to the x
   //    ring.  Positions s >= S hold zeros.
@@ -807,7 +859,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   const int ti = e.pnat + m;
   const float ct = __shfl(cum, ti < KW ? ti : KW - 1, 64);
   const float beta = tok_ok ? expf(ct) : 0.f;
-  const float Dh = s.D[h];
+  const float Dh = ld.Dh;
   V whi, wlo, wlo2;
 #pragma unroll
   for (int tt = 0; tt < WC::kE; ++tt) {
@@ -877,7 +929,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   wave_sync();  // xT reads done before the tile is reused
 
   // 6. output rows of the new tokens
-  store_out<OT>(s, H, e, h, lane, acc);
+  store_out_staged<OT>(s, H, e, h, lane, acc, ot);
 }
 
 // ---------------------------------------------------------------------------
@@ -896,11 +948,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 void replay_kernel(KCache c, KStep s, int d) {
   __shared__ uint16_t xT_all[kWaves][kHeadDim * Win<KW>::kXS];
   __shared__ float cbw_all[SPLIT ? 1 : kWaves][SPLIT ? 4 : kMaxTokens * kCbLds];
+  __shared__ __align__(16) uint32_t ot_all[kWaves][kOutTile];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nc = c.hpg / d;
   const int64_t nitems = (int64_t)s.batch * c.G * d;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
   uint16_t *xT = xT_all[wave];
+  uint32_t *ot = ot_all[wave];
   for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += nw) {
     const int chunk = (int)(item % d);
     const int64_t bg = item / d;
@@ -933,7 +987,7 @@ void replay_kernel(KCache c, KStep s, int d) {
     if constexpr (ST == kF32) {  // a 32 KiB fp32 tile per head: no room for a second buffer
       for (int j = 0; j < nc; ++j) {
         if (j > 0) load_head<ST, KW>(c, s, e, h0 + j, lane, la);
-        head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+        head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
       }
       continue;
     }
@@ -941,18 +995,18 @@ void replay_kernel(KCache c, KStep s, int d) {
     for (; j + 2 < nc; j += 2) {  // heads j + 1 and j + 2 exist: prefetch unconditionally
       load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
       load_head<ST, KW>(c, s, e, h0 + j + 2, lane, la);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
     }
     if (j + 1 < nc) {  // two heads left
       load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
     } else {  // one head left
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, lane);
+      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
     }
   }
 }
@@ -984,16 +1038,17 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
 }
 
 template <int ST, int KW>
-__global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int32_t *slot_idx,
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : (KW == 32 ? 2 : 3))))
+void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
   using WC = Win<KW>;
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   constexpr int kNLD = 2 * kEB;
-  __shared__ uint16_t xT_all[kWaves][kHeadDim * WC::kXS];
+  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
-  const int h = (blockIdx.x - j * htiles) * kWaves + wave;
+  const int h = (blockIdx.x - j * htiles) * kHeadWaves + wave;
   if (h >= c.H) return;
   const int slot = slot_idx[j], k = num_fold[j], L = c.L;
   if (slot <= 0 || slot >= c.num_slots) return;
@@ -1066,14 +1121,15 @@ __global__ __launch_bounds__(kWaves * 64) void flush_kernel(KCache c, const int3
 // ---------------------------------------------------------------------------
 
 template <int ST, int OT, int KW>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : 3)))
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : (KW == 32 ? 2 : 3))))
 void fused_kernel(KCache c, KStep s, int htiles) {
-  __shared__ uint16_t xT_all[kWaves][kHeadDim * Win<KW>::kXS];
-  __shared__ float cbw_all[kWaves][kMaxTokens * kCbLds];
+  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
+  __shared__ float cbw_all[kHeadWaves][kMaxTokens * kCbLds];
+  __shared__ __align__(16) uint32_t ot_all[kHeadWaves][kOutTile];
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.x / htiles;
-  const int h = (blockIdx.x - b * htiles) * kWaves + wave;
+  const int h = (blockIdx.x - b * htiles) * kHeadWaves + wave;
   if (h >= c.H) return;
   const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
   uint16_t *xT = xT_all[wave];
@@ -1095,13 +1151,14 @@ void fused_kernel(KCache c, KStep s, int htiles) {
 
   // 2. fold the first k live tokens: the new tile replaces ld.raw, the new
   //    fp8 row scales of rows 16 rb + m replace fl.osc
+  const float Ah = s.A[h];
   FoldHeadLoads<ST, KW> fl;  // fp8: the old scales even when k == 0
   load_fold_head<ST, KW>(c, e.slot, h, e.r0, e.k, lane, fl);
   if (e.k > 0) {
     FoldBLoads<KW> fb;
     load_fold_B<KW>(c, e.slot, g, e.r0, e.k, lane, fb);
     FoldOps<ST, KW> fo;
-    fold_setup<ST, KW>(s.A[h], e.k, fl, fb, xT, lane, fo);
+    fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, lane, fo);
     wave_sync();  // xT written by this wave -> read below
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
@@ -1147,7 +1204,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     wave_sync();
     load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   }
-  head_compute<ST, OT, KW>(c, s, e, h, ld, il, xT, lane);
+  head_compute<ST, OT, KW>(c, s, e, h, ld, il, xT, ot_all[wave], lane);
 }
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
@@ -1189,23 +1246,23 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
   const float *src = states + (int64_t)j * states_stride + (int64_t)h * kHeadElems +
                      (16 * rb + m) * kDState + 32 * q;
-  float v[32];
+  f32x4 acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 4 * u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * u + e] = a[e];
+    for (int e = 0; e < 4; ++e) QV(acc, 4 * u + e) = a[e];
   }
   float sc = 1.f, y = 1.f;
   bool fast = true;
   if constexpr (ST == kFP8) {
-    sc = fp8_row_scale(quarter_row_max(v));
+    sc = fp8_row_scale(quarter_row_max(acc));
     y = 1.0f / sc;
     fast = __all(scale_fast(sc));
     if (q == 0) reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + 16 * rb + m] = sc;
   }
   u32x4 ch[2 * kEB];
-  encode_quarter<ST>(v, sc, y, fast, ch);
+  encode_quarter<ST>(acc, sc, y, fast, ch);
   store_chunks<ST>(hp, rb, lane, ch);
 }
 
@@ -1273,8 +1330,8 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
 
 template <int ST, int OT>
 hipError_t fused_t(const KCache &c, const KStep &s, hipStream_t st) {
-  const int htiles = (c.H + kWaves - 1) / kWaves;
-  const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kWaves * 64);
+  const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
+  const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kHeadWaves * 64);
   if (c.L <= 16)
     fused_kernel<ST, OT, 16><<<grid, block, 0, st>>>(c, s, htiles);
   else
@@ -1301,8 +1358,8 @@ hipError_t split_t(const KCache &c, const KStep &s, hipStream_t st) {
 template <int ST>
 hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                    int n, hipStream_t st) {
-  const int htiles = (c.H + kWaves - 1) / kWaves;
-  const dim3 grid((unsigned)((int64_t)n * htiles)), block(kWaves * 64);
+  const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
+  const dim3 grid((unsigned)((int64_t)n * htiles)), block(kHeadWaves * 64);
   if (c.L <= 16)
     flush_kernel<ST, 16><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
   else
