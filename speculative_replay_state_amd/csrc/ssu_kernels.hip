@@ -91,6 +91,12 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
+// One of four values for a lane-varying i in [0, 4), taken by value so that
+// no register array is indexed at run time (that would go through scratch).
+__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int i) {
+  return i < 2 ? (i == 0 ? v0 : v1) : (i == 2 ? v2 : v3);
+}
+
 __device__ __forceinline__ int ring_pos(int r, int s, int L) {
   int p = r + s;
   return p >= L ? p - L : p;
@@ -1086,7 +1092,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   wave_sync();  // xT written by this wave -> read below
 
   // 3. row block by row block: decode and decay, rank-k update, encode, store
-  float *scp = reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim;
+  float scs[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     u32x4 ch[kNLD];
@@ -1097,11 +1103,12 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
       else
         ch[u] = raw[rb][u];
     }
-    const float sc = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ch);
-    if constexpr (ST == kFP8)
-      if (q == 0) scp[16 * rb + m] = sc;
+    scs[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ch);
     store_chunks<ST>(hp, rb, lane, ch);
   }
+  // new row scales: lane l holds row l's (row 16 q + m is in rb = q)
+  if constexpr (ST == kFP8)
+    (reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(scs[0], scs[1], scs[2], scs[3], q);
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,13 +1184,8 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) store_chunks<ST>(hp, rb, lane, ld.raw[rb]);
-    if constexpr (ST == kFP8) {
-      float *scp = reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim;
-      if (q == 0) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) scp[16 * rb + m] = fl.osc[rb];
-      }
-    }
+    if constexpr (ST == kFP8)  // lane l holds row l's new scale (row 16 q + m is in rb = q)
+      (reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(fl.osc[0], fl.osc[1], fl.osc[2], fl.osc[3], q);
   }
   if constexpr (ST == kFP8) {
 #pragma unroll

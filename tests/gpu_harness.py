@@ -84,3 +84,56 @@ def check_cache_after_step(spec, before: synth.CacheArrays, gpu: synth.CacheArra
     unchanged = ref.dt_cache[:, :nb].view(np.uint32) == before.dt_cache[:, :nb].view(np.uint32)
     assert np.array_equal(gpu.dt_cache[:, :nb].view(np.uint32)[unchanged],
                           before.dt_cache[:, :nb].view(np.uint32)[unchanged])
+
+
+def check_state(spec, gpu, ref, before, touched):
+    untouched = [s for s in range(spec.num_slots) if s not in touched]
+    assert np.array_equal(gpu.state[untouched], before.state[untouched])
+    assert np.array_equal(gpu.state[:, spec.state_bytes():], before.state[:, spec.state_bytes():])
+    if not touched:
+        return
+    if spec.state_dtype == "fp8":
+        g = np.stack([gpu.state_view(s) for s in touched])
+        r = np.stack([ref.state_view(s) for s in touched])
+        frac, dist = fp8_code_agreement(g, r)
+        assert frac >= 0.999 and dist <= 1, (frac, dist)
+        gs = np.stack([gpu.scale_view(s) for s in touched]).astype(np.float64)
+        rs = np.stack([ref.scale_view(s) for s in touched]).astype(np.float64)
+        assert np.max(np.abs(gs - rs) / rs) <= 1e-5
+    else:
+        g = np.stack([_decode_state(gpu, s) for s in touched])
+        r = np.stack([_decode_state(ref, s) for s in touched])
+        assert rel_err(g, r) <= (1e-4 if spec.state_dtype == "f32" else 2e-2)
+
+
+def state_propagation_bound(spec, step, k, gpu, ref_cache):
+    """Per output element, the most the readout can move between the GPU's
+    re-encoded checkpoint and the oracle's: the readout of token i is
+    beta_i C_i.h with beta_i = exp(cumA) <= 1 (A < 0, dt' >= 0), so the two
+    differ by at most sum_n |C_i[n]| |h_gpu[p, n] - h_ref[p, n]|.  The state
+    check bounds those differences (fp8: one code in at most 0.1 % of the
+    elements), and this lets the output check accept the readout of any
+    checkpoint that passes it."""
+    extra = np.zeros((step.tokens, spec.nheads, spec.headdim))
+    hpg = spec.nheads // spec.ngroups
+    C = bf16_bits_to_f64(step.C)
+    for b in range(step.batch):
+        slot = int(step.slot_idx[b])
+        if k[b] <= 0 or not 0 < slot < spec.num_slots:
+            continue
+        bos = int(step.cu_seqlens[b]) if step.cu_seqlens is not None else b * step.T
+        tb = (int(step.cu_seqlens[b + 1]) - bos) if step.cu_seqlens is not None else step.T
+        dh = np.abs(_decode_state(gpu, slot) - _decode_state(ref_cache, slot))  # [H, P, N]
+        for h in range(spec.nheads):
+            extra[bos:bos + tb, h, :] = np.abs(C[bos:bos + tb, h // hpg]) @ dh[h].T
+    return extra
+
+
+def bf16_bits_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def _decode_state(cache, slot):
+    from oracle import ssu_oracle as O
+    return O.decode_state(cache, slot)

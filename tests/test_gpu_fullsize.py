@@ -1,0 +1,118 @@
+"""Parity at the benchmark's full sizes, in the launch configurations the
+benchmark times, on sampled entries.
+
+Each case draws a full-size cache on the GPU (the benchmark's value laws),
+runs the step (and flush) on every entry through the C ABI, and checks a
+sample of entries (the first, the last and six random ones) against the fp64
+oracle run on exactly those entries: outputs, ring appends, ring_start and,
+where a flush ran, the re-encoded checkpoints.  Bounds as in the reduced
+parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import device as sd
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import gpu_harness as gh
+    import speculative_replay_state_amd as ssu
+from oracle import ssu_oracle as O
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# (workload, algo): the five benchmark workloads at their full sizes
+FULL = {
+    "tiny_b2": dict(nheads=8, ngroups=1, state="f32", batch=2, slots=4, T=1, pnat_max=8, out="f32"),
+    "mtp_b64": dict(nheads=64, ngroups=8, state="bf16", batch=64, slots=128, T=4, pnat_max=4, out="bf16"),
+    "prod_b256": dict(nheads=128, ngroups=8, state="f16", batch=256, slots=513, T=8, pnat_max=8, out="bf16"),
+    "prod_b512": dict(nheads=128, ngroups=8, state="f16", batch=512, slots=1025, T=8, pnat_max=8, out="bf16"),
+    "fp8_b256": dict(nheads=128, ngroups=8, state="fp8", batch=256, slots=513, T=4, pnat_max=0, out="bf16",
+                     flush=(1, 4)),
+    "large_b1024": dict(nheads=128, ngroups=8, state="bf16", batch=1024, slots=2048, T=8, pnat_max=8,
+                        out="bf16", varlen=True, pad=256),
+}
+RUNS = [("tiny_b2", "monolith"), ("mtp_b64", "monolith"), ("mtp_b64", "split"), ("prod_b256", "monolith"),
+        ("prod_b256", "split"), ("prod_b512", "monolith"), ("fp8_b256", "fused"), ("fp8_b256", "separate"),
+        ("large_b1024", "monolith")]
+
+
+@pytest.mark.parametrize("name,algo", RUNS)
+def test_full_size_sampled(name, algo):
+    cfg = FULL[name]
+    seed = 9000 + len(name) * 7 + len(algo)
+    print("case", name, algo, flush=True)
+    spec = synth.CacheSpec(num_slots=cfg["slots"], nheads=cfg["nheads"], ngroups=cfg["ngroups"],
+                           state_dtype=cfg["state"], slot_pad=cfg.get("pad", 0))
+    t = sd.make_cache_device(spec, seed, gh.DEV)
+    rng = np.random.default_rng(seed)
+    B = cfg["batch"]
+    slots = np.sort(rng.choice(np.arange(1, spec.num_slots), B, replace=False)).astype(np.int32)
+    step = synth.make_step(spec, B, cfg["T"], seed + 1, cfg["pnat_max"], varlen=cfg.get("varlen", False),
+                           slots=slots, pnat_fixed=0 if cfg["pnat_max"] == 0 else None)
+    k = None
+    if "flush" in cfg:
+        k = synth.flush_counts(B, cfg["flush"][0], cfg["flush"][1], seed + 2)
+        if algo == "fused":
+            step.pnat[:] = k  # the previous step's accepted tokens, folded first
+    sample = sorted({0, B - 1, *rng.choice(np.arange(B), min(6, B), replace=False).tolist()})
+    before, smap = sd.download_subset(spec, t, [int(slots[b]) for b in sample])
+    sub = sd.subset_step(step, sample, smap)
+
+    st = sd.upload_step(step, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    out = gh.out_tensor(step, spec, cfg["out"])
+    kt = None if k is None else torch.from_numpy(k).to(gh.DEV)
+    if algo == "fused":
+        desc = ssu.make_step_desc(B, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"], st["B"],
+                                  st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, cfg["out"], None,
+                                  "auto", num_fold=kt)
+        ssu.replay_step(dc, desc)
+    else:
+        gh.run_step(dc, st, step, out, cfg["out"], "split" if algo == "split" else "monolith")
+        if algo == "separate":
+            ssu.flush(dc, st["slot_idx"], kt, st["A"])
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == 0
+    after, _ = sd.download_subset(spec, t, [int(slots[b]) for b in sample])
+
+    ref_cache = before.copy()
+    ks = None if k is None else k[sample].astype(np.int32)
+    if algo == "fused":
+        ref, status = O.replay_step(ref_cache, sub, num_fold=ks)
+    else:
+        ref, status = O.replay_step(ref_cache, sub)
+        if algo == "separate":
+            assert O.flush(ref_cache, sub.slot_idx, ks, sub.A) == 0
+    assert status == 0
+
+    rows = []
+    for b in sample:
+        lo = int(step.cu_seqlens[b]) if step.cu_seqlens is not None else b * step.T
+        hi = int(step.cu_seqlens[b + 1]) if step.cu_seqlens is not None else (b + 1) * step.T
+        rows.extend(range(lo, hi))
+    got = gh.to_f64(out)[rows]
+    tol = gh.tol_for(spec.state_dtype, cfg["out"]) * (1.0 + np.abs(ref))
+    if algo == "fused":
+        tol = tol + gh.state_propagation_bound(after.spec, sub, ks, after, ref_cache)
+    excess = np.abs(got - ref) - tol
+    assert np.all(excess <= 1e-12), "max excess %g (rel err %g)" % (np.max(excess), gh.rel_err(got, ref))
+
+    assert np.array_equal(after.ring_start, ref_cache.ring_start)
+    assert np.array_equal(after.x_cache, ref_cache.x_cache)
+    assert np.array_equal(after.B_cache, ref_cache.B_cache)
+    nb = spec.dt_bytes()
+    assert np.array_equal(after.dt_cache[:, nb:], ref_cache.dt_cache[:, nb:])
+    g = after.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    r = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
+    assert gh.rel_err(g, r) <= 1e-6
+    touched = [i + 1 for i, b in enumerate(sample) if k is not None and k[b] > 0]
+    gh.check_state(after.spec, after, ref_cache, before, touched)

@@ -50,54 +50,6 @@ def _run_fused(spec, cache, step, out_dtype, k, algo="auto"):
     return out, sd.download_cache(spec, t), int(dc.status.item())
 
 
-def _check_state(spec, gpu, ref, before, touched):
-    untouched = [s for s in range(spec.num_slots) if s not in touched]
-    assert np.array_equal(gpu.state[untouched], before.state[untouched])
-    assert np.array_equal(gpu.state[:, spec.state_bytes():], before.state[:, spec.state_bytes():])
-    if not touched:
-        return
-    if spec.state_dtype == "fp8":
-        g = np.stack([gpu.state_view(s) for s in touched])
-        r = np.stack([ref.state_view(s) for s in touched])
-        frac, dist = gh.fp8_code_agreement(g, r)
-        assert frac >= 0.999 and dist <= 1, (frac, dist)
-        gs = np.stack([gpu.scale_view(s) for s in touched]).astype(np.float64)
-        rs = np.stack([ref.scale_view(s) for s in touched]).astype(np.float64)
-        assert np.max(np.abs(gs - rs) / rs) <= 1e-5
-    else:
-        g = np.stack([O.decode_state(gpu, s) for s in touched])
-        r = np.stack([O.decode_state(ref, s) for s in touched])
-        assert gh.rel_err(g, r) <= (1e-4 if spec.state_dtype == "f32" else 2e-2)
-
-
-def _state_propagation_bound(spec, step, k, gpu, ref_cache):
-    """Per output element, the most the readout can move between the GPU's
-    re-encoded checkpoint and the oracle's: the readout of token i is
-    beta_i C_i.h with beta_i = exp(cumA) <= 1 (A < 0, dt' >= 0), so the two
-    differ by at most sum_n |C_i[n]| |h_gpu[p, n] - h_ref[p, n]|.  The state
-    check bounds those differences (fp8: one code in at most 0.1 % of the
-    elements), and this lets the output check accept the readout of any
-    checkpoint that passes it."""
-    extra = np.zeros((step.tokens, spec.nheads, spec.headdim))
-    hpg = spec.nheads // spec.ngroups
-    C = R_bf16(step.C)
-    for b in range(step.batch):
-        slot = int(step.slot_idx[b])
-        if k[b] <= 0 or not 0 < slot < spec.num_slots:
-            continue
-        bos = int(step.cu_seqlens[b]) if step.cu_seqlens is not None else b * step.T
-        tb = (int(step.cu_seqlens[b + 1]) - bos) if step.cu_seqlens is not None else step.T
-        dh = np.abs(O.decode_state(gpu, slot) - O.decode_state(ref_cache, slot))  # [H, P, N]
-        for h in range(spec.nheads):
-            extra[bos:bos + tb, h, :] = np.abs(C[bos:bos + tb, h // hpg]) @ dh[h].T
-    return extra
-
-
-def R_bf16(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
-        torch.float64).numpy()
-
-
 @pytest.mark.parametrize("case", list(CASES))
 def test_fused_step_parity(case):
     spec, cache, step, out_dtype = _setup(case, 3000 + len(case))
@@ -109,7 +61,7 @@ def test_fused_step_parity(case):
     ref, st = O.replay_step(ref_cache, step, num_fold=k)
     assert st == 0
     got = gh.to_f64(out)
-    extra = _state_propagation_bound(spec, step, k, gpu, ref_cache)
+    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
     excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, out_dtype) * (1.0 + np.abs(ref)) - extra
     assert np.all(excess <= 1e-12), "max excess %g (plain rel err %g)" % (np.max(excess), gh.rel_err(got, ref))
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
@@ -120,7 +72,7 @@ def test_fused_step_parity(case):
     rd = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
     assert gh.rel_err(gd, rd) <= 1e-6
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
-    _check_state(spec, gpu, ref_cache, cache, touched)
+    gh.check_state(spec, gpu, ref_cache, cache, touched)
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -179,7 +131,7 @@ def test_fused_invalid_fold_is_skipped_and_reported():
     assert st == ssu.SSU_STATUS_BAD_FOLD
     got = gh.to_f64(out)
     assert np.all(got[3:9] == 0.0)
-    extra = _state_propagation_bound(spec, step, k, gpu, ref_cache)
+    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
     assert np.all(np.abs(got - ref) <= 2e-2 * (1.0 + np.abs(ref)) + extra + 1e-12)
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     for b in (1, 2):
@@ -187,4 +139,4 @@ def test_fused_invalid_fold_is_skipped_and_reported():
         assert np.array_equal(gpu.state[s], cache.state[s])
         assert np.array_equal(gpu.x_cache[s], cache.x_cache[s])
     touched = sorted({int(step.slot_idx[b]) for b in (0, 4, 5)})
-    _check_state(spec, gpu, ref_cache, cache, touched)
+    gh.check_state(spec, gpu, ref_cache, cache, touched)
