@@ -12,7 +12,7 @@
  *
  *     dt'  = softplus(dt + dt_bias[h])
  *     h   <- exp(A[h] * dt') * h  +  dt' * x (outer) B
- *     y    = h . C  +  D[h] * x
+ *     y    = h . C  +  D[h] * x                 (times z sigmoid(z) when gated)
  *
  * Sources (cited by page title and section):
  *  - FlashInfer PR "mamba checkpointing SSU: two-kernel split + ring-buffer
@@ -43,6 +43,10 @@
  *    fp8 e4m3fn (OCP, max 448), per row of dstate: m = max |h|, scale =
  *    fp32(m / 448) (1 when that is 0), code = nearest e4m3fn value of
  *    fp32(h / scale) after clamping to [-448, 448], ties to even code.
+ *  - The optional output gate is Mamba-2's: y * z * sigmoid(z) with z bf16
+ *    [tok][H][P], applied to the fp64 readout; dt_softplus = 0 makes dt' the
+ *    plain dt + dt_bias (FlashInfer PR, the HAS_Z output and dt_softplus
+ *    flags named in its commits).
  *  - A padding entry (slot <= 0 or slot >= num_slots) writes zero output rows
  *    and touches no cache.  An entry with pnat < 0 or pnat + T_b > L is
  *    treated the same way and raises status bit 1; a flush entry with k < 0
@@ -319,11 +323,24 @@ static void ssu_token(double *h, int P, int N, double a, double d,
  * append the new tokens' x, B and dt' to the ring.  The checkpoint and
  * ring_start are not modified.  Returns the status bits.
  */
+/*
+ * dt' of a new token.  With dt_softplus (the default of the pages) it is
+ * softplus(dt + dt_bias); without it (the dt_softplus = false variant named
+ * in the FlashInfer PR's commits) it is dt + dt_bias itself.
+ */
+static double new_dt(float dt, float bias, int dt_softplus) {
+  const double v = (double)dt + (double)bias;
+  return dt_softplus ? or_softplus(v) : v;
+}
+
+/* The output gate z * sigmoid(z) (Mamba-2's SiLU gate on the readout). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
 int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlens,
                    const int32_t *slot_idx, const int32_t *pnat,
                    const uint16_t *x, const uint16_t *Bm, const uint16_t *Cm,
                    const float *dt, const float *A, const float *D,
-                   const float *dt_bias, double *out) {
+                   const float *dt_bias, const uint16_t *z, int dt_softplus, double *out) {
   const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
             L = c->ring_len, HPG = H / G;
   int status = 0;
@@ -373,7 +390,7 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
       /* new tokens: softplus, update, read out */
       for (int i = 0; i < Tb; ++i) {
         int64_t tok = bos + i;
-        double d = or_softplus((double)dt[tok * H + hh] + (double)dt_bias[hh]);
+        double d = new_dt(dt[tok * H + hh], dt_bias[hh], dt_softplus);
         for (int p = 0; p < P; ++p) xv[p] = or_bf16_value(x[(tok * H + hh) * P + p]);
         for (int n = 0; n < N; ++n) Bv[n] = or_bf16_value(Bm[(tok * G + g) * N + n]);
         ssu_token(h, P, N, A[hh], d, xv, Bv);
@@ -381,7 +398,9 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
           double y = 0.0;
           for (int n = 0; n < N; ++n)
             y += h[p * N + n] * or_bf16_value(Cm[(tok * G + g) * N + n]);
-          out[(tok * H + hh) * P + p] = y + (double)D[hh] * xv[p];
+          y += (double)D[hh] * xv[p];
+          if (z) y *= silu(or_bf16_value(z[(tok * H + hh) * P + p]));
+          out[(tok * H + hh) * P + p] = y;
         }
       }
       free(h); free(xv); free(Bv);
@@ -400,7 +419,7 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
       int64_t tok = bos + i;
       int pos = (r + p0 + i) % L;
       for (int hh = 0; hh < H; ++hh) {
-        float d = (float)or_softplus((double)dt[tok * H + hh] + (double)dt_bias[hh]);
+        float d = (float)new_dt(dt[tok * H + hh], dt_bias[hh], dt_softplus);
         memcpy(ds + ((int64_t)hh * L + pos) * 4, &d, 4);
         memcpy(xs + ((int64_t)hh * L + pos) * P * 2, x + (tok * H + hh) * P, (size_t)P * 2);
       }

@@ -65,7 +65,7 @@ def lib():
             P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
             L.or_replay_step.restype = I
             L.or_replay_step.argtypes = [ctypes.POINTER(_OrCache), I, I, P, P, P, P, P, P, P,
-                                         P, P, P, P]
+                                         P, P, P, P, I, P]
             L.or_flush.restype = I
             L.or_flush.argtypes = [ctypes.POINTER(_OrCache), I, P, P, P]
             L.or_init_state.restype = None
@@ -117,6 +117,9 @@ _STATUS_BAD_FOLD = 2
 def replay_step(cache, step, num_fold=None):
     """Replay step (see or_replay_step).  Returns (out fp64 [tokens, H, P], status).
 
+    The step's optional `z` (bf16 bits like x) gates the output with
+    z * sigmoid(z); `dt_softplus` False makes dt' = dt + dt_bias.
+
     With num_fold ([batch] ints) the step is the fused flush-in-step: for each
     entry the step would process (valid slot, 0 <= pnat, pnat + T_b <= L, a
     valid ring_start and T_b within max_seqlen) and k = num_fold[b] in
@@ -142,10 +145,14 @@ def replay_step(cache, step, num_fold=None):
     slots = _c(step.slot_idx, np.int32)
     pnat = _c(step.pnat, np.int32)
     cu = None if step.cu_seqlens is None else _c(step.cu_seqlens, np.int32)
+    z = getattr(step, "z", None)
+    z = None if z is None else _c(z, np.uint16)
     assert x.shape == (ntok, s.nheads, s.headdim) and B.shape == (ntok, s.ngroups, s.dstate)
+    assert z is None or z.shape == x.shape
     st = lib().or_replay_step(ctypes.byref(oc), step.batch, step.T, _ptr(cu), _ptr(slots),
                               _ptr(pnat), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
-                              _ptr(D), _ptr(db), out.ctypes.data)
+                              _ptr(D), _ptr(db), _ptr(z), int(getattr(step, "dt_softplus", True)),
+                              out.ctypes.data)
     return out, st
 
 

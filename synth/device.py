@@ -94,6 +94,7 @@ def upload_step(step: StepInputs, device) -> Dict[str, torch.Tensor]:
         dt=torch.from_numpy(step.dt).to(device),
         A=torch.from_numpy(step.A).to(device), D=torch.from_numpy(step.D).to(device),
         dt_bias=torch.from_numpy(step.dt_bias).to(device),
+        z=None if step.z is None else u16(step.z),
     )
     return t
 
@@ -115,4 +116,5 @@ def subset_step(step: StepInputs, entries: Sequence[int], slot_map) -> StepInput
     return StepInputs(len(entries), step.T, slots, step.pnat[entries].astype(np.int32),
                       np.asarray(cu, np.int32) if step.cu_seqlens is not None else None,
                       step.x[rows], step.B[rows], step.C[rows], step.dt[rows],
-                      step.A, step.D, step.dt_bias)
+                      step.A, step.D, step.dt_bias, None if step.z is None else step.z[rows],
+                      step.dt_softplus)

@@ -190,6 +190,8 @@ class StepInputs:
     A: np.ndarray  # f32 [H]
     D: np.ndarray  # f32 [H]
     dt_bias: np.ndarray  # f32 [H]
+    z: Optional[np.ndarray] = None  # uint16 (bf16 bits) [tokens, H, P]: output gate, or None
+    dt_softplus: bool = True  # False: dt' = dt + dt_bias (no softplus)
 
     @property
     def tokens(self) -> int:
@@ -275,13 +277,15 @@ def make_params(spec: CacheSpec, seed: int):
 
 def make_step(spec: CacheSpec, batch: int, T: int, seed: int, pnat_max: int,
               varlen: bool = False, slots: Optional[np.ndarray] = None,
-              n_padding: int = 0, pnat_fixed: Optional[int] = None) -> StepInputs:
+              n_padding: int = 0, pnat_fixed: Optional[int] = None, with_z: bool = False,
+              dt_softplus: bool = True) -> StepInputs:
     """One decode step over `batch` entries.
 
     Active entries use unique random slots from [1, num_slots) (or `slots`);
     the first `n_padding` entries (after a seeded shuffle) are padding (slot 0).
     pnat ~ U{0..pnat_max} (or `pnat_fixed`); with `varlen`, T_b ~ U{1..T} and
-    the inputs are packed along cu_seqlens.
+    the inputs are packed along cu_seqlens.  `with_z` adds an output gate
+    z ~ N(0, 1) in bf16 (drawn last, so the other values do not change).
     """
     g = _gen(seed)
     H, G, P, N = spec.nheads, spec.ngroups, spec.headdim, spec.dstate
@@ -309,7 +313,9 @@ def make_step(spec: CacheSpec, batch: int, T: int, seed: int, pnat_max: int,
     C = _bf16_bits(torch.randn(ntok, G, N, generator=g))
     dt = (torch.randn(ntok, H, generator=g, dtype=torch.float64) * 0.5).to(torch.float32).numpy()
     A, D, dt_bias = make_params(spec, seed + 7919)
-    return StepInputs(batch, T, slots, pnat.astype(np.int32), cu, x, B, C, dt, A, D, dt_bias)
+    z = _bf16_bits(torch.randn(ntok, H, P, generator=g)) if with_z else None
+    return StepInputs(batch, T, slots, pnat.astype(np.int32), cu, x, B, C, dt, A, D, dt_bias, z,
+                      dt_softplus)
 
 
 # ---------------------------------------------------------------------------

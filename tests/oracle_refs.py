@@ -71,7 +71,8 @@ def sequence(cache, step, b, h):
     xn = bf16_to_f64(step.x[toks, h])
     Bn = bf16_to_f64(step.B[toks, g])
     Cn = bf16_to_f64(step.C[toks, g])
-    dn = softplus_torch(step.dt[toks, h].astype(np.float64) + float(step.dt_bias[h]))
+    raw = step.dt[toks, h].astype(np.float64) + float(step.dt_bias[h])
+    dn = softplus_torch(raw) if getattr(step, "dt_softplus", True) else raw
     return dict(dtp=np.concatenate([dr, dn]), x=np.concatenate([xr, xn]),
                 B=np.concatenate([Br, Bn]), C=Cn, xnew=xn, pnat=p, Tb=Tb, bos=bos,
                 slot=slot, g=g)

@@ -14,6 +14,7 @@ import itertools
 import mpmath
 import numpy as np
 import pytest
+import torch
 
 import synth
 from tests import oracle_refs as R
@@ -158,6 +159,58 @@ def test_flush_then_step_invariance(oracle):
     out2, st = oracle.replay_step(c2, step2)
     assert st == 0
     assert np.array_equal(out2, ref_out)
+
+
+def test_z_gate_closed_form(oracle):
+    """Gated readout: the closed form times z sigmoid(z), z through torch's
+    bf16 decode and torch's sigmoid (independent of the oracle's C)."""
+    spec = synth.CacheSpec(num_slots=6, nheads=4, ngroups=2, headdim=8, dstate=16, ring_len=8,
+                           state_dtype="f64")
+    cache = synth.make_cache(spec, 13)
+    step = synth.make_step(spec, 3, 3, 14, 5, with_z=True)
+    out, st = oracle.replay_step(cache.copy(), step)
+    assert st == 0
+    zv = R.bf16_to_f64(step.z)
+    gate = zv * torch.sigmoid(torch.from_numpy(zv)).numpy()
+    for b in range(step.batch):
+        h0 = R.state_f64(cache, int(step.slot_idx[b]))
+        for h in range(spec.nheads):
+            seq = R.sequence(cache, step, b, h)
+            want = R.closed_form_outputs(h0[h], float(step.A[h]), float(step.D[h]), seq)
+            rows = slice(seq["bos"], seq["bos"] + seq["Tb"])
+            assert _rel_err(out[rows, h], want * gate[rows, h]) <= 1e-12
+    step.z[:] = 0  # silu(0) = 0: every output is exactly zero
+    out0, _ = oracle.replay_step(cache.copy(), step)
+    assert np.all(out0 == 0.0)
+
+
+def test_dt_softplus_off_closed_form(oracle):
+    """dt_softplus = False: dt' = dt + dt_bias, in the readout and in the
+    appended dt ring."""
+    spec = synth.CacheSpec(num_slots=6, nheads=4, ngroups=2, headdim=8, dstate=16, ring_len=8,
+                           state_dtype="f64")
+    cache = synth.make_cache(spec, 23)
+    step = synth.make_step(spec, 3, 3, 24, 5, dt_softplus=False)
+    c2 = cache.copy()
+    out, st = oracle.replay_step(c2, step)
+    assert st == 0
+    L = spec.ring_len
+    for b in range(step.batch):
+        slot = int(step.slot_idx[b])
+        h0 = R.state_f64(cache, slot)
+        for h in range(spec.nheads):
+            seq = R.sequence(cache, step, b, h)
+            want = R.closed_form_outputs(h0[h], float(step.A[h]), float(step.D[h]), seq)
+            rows = slice(seq["bos"], seq["bos"] + seq["Tb"])
+            assert _rel_err(out[rows, h], want) <= 1e-12
+            for i in range(seq["Tb"]):
+                pos = (int(cache.ring_start[slot]) + seq["pnat"] + i) % L
+                want_dt = np.float32(step.dt[seq["bos"] + i, h]) + np.float32(step.dt_bias[h])
+                assert c2.dt_view(slot)[h, pos] == want_dt
+    # and it differs from the softplus run
+    step.dt_softplus = True
+    out_sp, _ = oracle.replay_step(cache.copy(), step)
+    assert not np.allclose(out_sp, out)
 
 
 def test_fused_flush_in_step_f64(oracle):
