@@ -149,6 +149,13 @@ typedef struct ssu_cache {
  *   num_fold    [batch] i32 or NULL: fused flush-in-step (see ssu_replay_step).
  *               Runs in the monolith: AUTO resolves to MONOLITH, an explicit
  *               SPLIT returns SSU_ERR_UNSUPPORTED.
+ *   z           [rows][nheads][64] io_dtype or NULL: output gate; each output
+ *               value is y * z * sigmoid(z), computed in fp32 before the
+ *               output is rounded [FI, the HAS_Z output flag].  16-byte
+ *               aligned.
+ *   no_dt_softplus  0: dt' = softplus(dt + dt_bias) (the default of [VD]);
+ *               nonzero: dt' = dt + dt_bias [FI, the dt_softplus flag].  The
+ *               dt ring stores dt' either way.
  * Requirements: 1 <= max_seqlen <= min(16, ring_len); pointers 16-byte
  * aligned (dt, A, D, dt_bias: 4-byte).  Active slots must be unique.
  */
@@ -170,6 +177,8 @@ typedef struct ssu_step {
   size_t workspace_bytes;
   ssu_algo algo;
   const int32_t *num_fold;
+  const void *z;
+  int32_t no_dt_softplus;
 } ssu_step;
 
 /* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen):

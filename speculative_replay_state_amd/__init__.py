@@ -64,7 +64,7 @@ class SsuStep(ctypes.Structure):
         ("A", _P), ("D", _P), ("dt_bias", _P),
         ("out", _P), ("out_dtype", ctypes.c_int),
         ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("algo", ctypes.c_int),
-        ("num_fold", _P),
+        ("num_fold", _P), ("z", _P), ("no_dt_softplus", _I32),
     ]
 
 
@@ -191,13 +191,14 @@ class DeviceCache:
 
 
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
-                   out_dtype="bf16", workspace=None, algo="auto", num_fold=None) -> SsuStep:
+                   out_dtype="bf16", workspace=None, algo="auto", num_fold=None, z=None,
+                   dt_softplus=True) -> SsuStep:
     return SsuStep(
         batch, max_seqlen, _ptr(slot_idx), _ptr(pnat), _ptr(cu_seqlens),
         _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
         _ptr(out), SSU_F32 if out_dtype == "f32" else SSU_BF16,
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        ALGO_CODES[algo], _ptr(num_fold))
+        ALGO_CODES[algo], _ptr(num_fold), _ptr(z), 0 if dt_softplus else 1)
 
 
 def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:

@@ -155,6 +155,7 @@ int check_step(const ssu_cache *c, const ssu_step *s) {
   if (s->algo != SSU_ALGO_AUTO && s->algo != SSU_ALGO_MONOLITH && s->algo != SSU_ALGO_SPLIT)
     return fail(SSU_ERR_INVALID, "unknown algo %d", (int)s->algo);
   if (s->num_fold && !aligned4(s->num_fold)) return fail(SSU_ERR_INVALID, "num_fold must be 4-byte aligned");
+  if (s->z && !aligned16(s->z)) return fail(SSU_ERR_INVALID, "z must be 16-byte aligned");
   if (s->num_fold && s->algo == SSU_ALGO_SPLIT)
     return fail(SSU_ERR_UNSUPPORTED, "the fused flush (num_fold) runs in the monolith only; use AUTO or MONOLITH");
   return SSU_OK;
@@ -204,6 +205,8 @@ int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t st
   k.pnat = step->prev_num_accepted;
   k.cu = step->cu_seqlens;
   k.fold = step->num_fold;
+  k.z = static_cast<const uint16_t *>(step->z);
+  k.dt_softplus = step->no_dt_softplus ? 0 : 1;
   k.x = static_cast<const uint16_t *>(step->x);
   k.B = static_cast<const uint16_t *>(step->B);
   k.C = static_cast<const uint16_t *>(step->C);

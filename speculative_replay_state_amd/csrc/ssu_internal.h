@@ -52,6 +52,8 @@ struct KStep {
   const float *dt_bias;
   void *out;
   float *cb;  // SPLIT scratch [batch][G][T][kCbStride]
+  const uint16_t *z;  // NULL, or the output gate (bf16) [rows][H][64]
+  int dt_softplus;    // 1: dt' = softplus(dt + dt_bias); 0: dt' = dt + dt_bias
 };
 
 hipError_t launch_replay_monolith(const KCache &c, const KStep &s, int state_type, int out_type,

@@ -374,11 +374,44 @@ __device__ __forceinline__ void store_out(const KStep &s, int H, const Entry &e,
 constexpr int kOutRowWords = 68;                       // 64 fp32 + 4 pad (bank spread)
 constexpr int kOutTile = kMaxTokens * kOutRowWords;    // 32-bit words per wave
 
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+
+// Gate chunks of the staged store's lane mapping, loaded with the head's
+// prefetch: bf16 out, lane (c = l % 8, i0 = l / 8): 8 values of tokens
+// i0 + 8 r; fp32 out, lane (c = l % 16, i0 = l / 16): 4 values of tokens
+// i0 + 4 r, two tokens per u32x4.
 template <int OT>
-__device__ __forceinline__ void store_out_staged(const KStep &s, int H, const Entry &e, int h, int lane,
-                                                 const f32x4 acc[4], uint32_t *ot) {
-  const int m = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void load_gate(const KStep &s, int H, const Entry &e, int h, int lane, u32x4 zw[2]) {
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   if constexpr (OT == kOutF32) {
+    const int c = lane & 15, i0 = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * r;
+      const u32x2 v = i < e.Tb ? ld8(s.z + ((int64_t)(e.bos + i) * H + h) * kHeadDim + 4 * c) : u32x2{0u, 0u};
+      if (r & 1) {
+        zw[r >> 1][2] = v[0];
+        zw[r >> 1][3] = v[1];
+      } else {
+        zw[r >> 1][0] = v[0];
+        zw[r >> 1][1] = v[1];
+      }
+    }
+  } else {
+    const int c = lane & 7, i0 = lane >> 3;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = i0 + 8 * r;
+      zw[r] = i < e.Tb ? ld16(s.z + ((int64_t)(e.bos + i) * H + h) * kHeadDim + 8 * c) : zero4;
+    }
+  }
+}
+
+template <int OT, bool HAS_Z>
+__device__ __forceinline__ void store_out_staged(const KStep &s, int H, const Entry &e, int h, int lane,
+                                                 const f32x4 acc[4], const u32x4 zw[2], uint32_t *ot) {
+  const int m = lane & 15, q = lane >> 4;
+  if constexpr (OT == kOutF32 || HAS_Z) {  // fp32 rows (the gate is applied before rounding)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
       *reinterpret_cast<u32x4 *>(ot + m * kOutRowWords + rb * 16 + 4 * q) = __builtin_bit_cast(u32x4, acc[rb]);
@@ -390,13 +423,31 @@ __device__ __forceinline__ void store_out_staged(const KStep &s, int H, const En
           u32x2{pack_bf16(acc[rb][0], acc[rb][1]), pack_bf16(acc[rb][2], acc[rb][3])};
   }
   wave_sync();
-  constexpr int kChunks = OT == kOutF32 ? 16 : 8;  // 16-byte chunks per token row
+  constexpr int kChunks = OT == kOutF32 ? 16 : 8;  // 16-byte output chunks per token row
   constexpr int kRowsPer = 64 / kChunks;           // token rows per instruction
   const int c = lane % kChunks, i0 = lane / kChunks;
 #pragma unroll
-  for (int i = i0; i < kMaxTokens; i += kRowsPer) {
+  for (int r = 0; r < kMaxTokens / kRowsPer; ++r) {
+    const int i = i0 + kRowsPer * r;
     if (i < e.Tb) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + i * kOutRowWords + 4 * c);
+      u32x4 v;
+      if constexpr (!HAS_Z) {
+        v = *reinterpret_cast<const u32x4 *>(ot + i * kOutRowWords + 4 * c);
+      } else if constexpr (OT == kOutF32) {
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(ot + i * kOutRowWords + 4 * c);
+        const uint32_t z01 = zw[r >> 1][(r & 1) * 2], z23 = zw[r >> 1][(r & 1) * 2 + 1];
+        v = u32x4{__float_as_uint(y[0] * silu_f(bf2f(z01 & 0xFFFFu))), __float_as_uint(y[1] * silu_f(bf2f(z01 >> 16))),
+                  __float_as_uint(y[2] * silu_f(bf2f(z23 & 0xFFFFu))), __float_as_uint(y[3] * silu_f(bf2f(z23 >> 16)))};
+      } else {
+        const f32x4 y0 = *reinterpret_cast<const f32x4 *>(ot + i * kOutRowWords + 8 * c);
+        const f32x4 y1 = *reinterpret_cast<const f32x4 *>(ot + i * kOutRowWords + 8 * c + 4);
+        const u32x4 zz = zw[r];
+        float g[8];
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) g[e2] = silu_f(bf2f((e2 & 1) ? (zz[e2 >> 1] >> 16) : (zz[e2 >> 1] & 0xFFFFu)));
+        v = u32x4{pack_bf16(y0[0] * g[0], y0[1] * g[1]), pack_bf16(y0[2] * g[2], y0[3] * g[3]),
+                  pack_bf16(y1[0] * g[4], y1[1] * g[5]), pack_bf16(y1[2] * g[6], y1[3] * g[7])};
+      }
       uint8_t *dst = static_cast<uint8_t *>(s.out) +
                      (((int64_t)(e.bos + i) * H + h) * kHeadDim) * (OT == kOutF32 ? 4 : 2) + 16 * c;
       st16_nt(dst, v);
@@ -711,6 +762,7 @@ struct HeadLoads {
   f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
   float dtv;                                 // lane s: stored dt' (s < pnat) or raw dt (new)
   float dtb, Ah, Dh;                         // dt_bias[h], A[h], D[h]
+  u32x4 zw[2];                               // output gate chunks (gated variant only)
 };
 
 // Per-(entry, group) loads: C of the new tokens and the C.B row of token m.
@@ -738,9 +790,10 @@ __device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int
 // loaded here is used before the head's compute phase: one counter tracks a
 // wave's loads in issue order, so using a value loaded here right away would
 // also wait for every load issued before it, including a prefetched tile.
-template <int ST, int KW>
+template <int ST, int OT, int KW, bool HAS_Z>
 __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
                                             HeadLoads<ST, KW> &ld) {
+  if constexpr (HAS_Z) load_gate<OT>(s, c.H, e, h, lane, ld.zw);
   using WC = Win<KW>;
   const int H = c.H, L = c.L, S = e.pnat + e.Tb;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -771,7 +824,7 @@ __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, con
 
 // Every per-head load of the replay: checkpoint, fp8 row scales of rows
 // 16 rb + 4 q + j, and the window.
-template <int ST, int KW>
+template <int ST, int OT, int KW, bool HAS_Z>
 __device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
                                           HeadLoads<ST, KW> &ld) {
   const int q = lane >> 4;
@@ -782,7 +835,7 @@ __device__ __forceinline__ void load_head(const KCache &c, const KStep &s, const
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) ld.rscale[rb] = *reinterpret_cast<const f32x4 *>(sp + rb * 16 + 4 * q);
   }
-  load_window<ST, KW>(c, s, e, h, lane, ld);
+  load_window<ST, OT, KW, HAS_Z>(c, s, e, h, lane, ld);
 }
 
 template <int ST, int KW>
@@ -825,7 +878,7 @@ __device__ __forceinline__ void load_cb_row(const Entry &e, const float *cb, int
                          : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-template <int ST, int OT, int KW>
+template <int ST, int OT, int KW, bool HAS_Z>
 __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, const Entry &e, int h,
                                              const HeadLoads<ST, KW> &ld, const ItemLoads<ST, KW> &il,
                                              uint16_t *xT, uint32_t *ot, int lane) {
@@ -839,7 +892,8 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   //    softplus'd and appended to the dt ring.  Then the inclusive decay prefix.
   float dtp = ld.dtv;
   if (lane >= e.pnat && lane < S) {
-    dtp = softplus_f(ld.dtv + ld.dtb);
+    dtp = ld.dtv + ld.dtb;
+    if (s.dt_softplus) dtp = softplus_f(dtp);
     float *dtring = reinterpret_cast<float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
     dtring[ring_pos(e.r, lane, L)] = dtp;
   }
@@ -935,7 +989,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   wave_sync();  // xT reads done before the tile is reused
 
   // 6. output rows of the new tokens
-  store_out_staged<OT>(s, H, e, h, lane, acc, ot);
+  store_out_staged<OT, HAS_Z>(s, H, e, h, lane, acc, ld.zw, ot);
 }
 
 // ---------------------------------------------------------------------------
@@ -949,7 +1003,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
 // Both run identical arithmetic, so their outputs are bit-identical.
 // ---------------------------------------------------------------------------
 
-template <int ST, int OT, int KW, bool SPLIT>
+template <int ST, int OT, int KW, bool SPLIT, bool HAS_Z>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void replay_kernel(KCache c, KStep s, int d) {
   __shared__ uint16_t xT_all[kWaves][kHeadDim * Win<KW>::kXS];
@@ -974,7 +1028,7 @@ void replay_kernel(KCache c, KStep s, int d) {
     }
     HeadLoads<ST, KW> la, lb;
     ItemLoads<ST, KW> il;
-    load_head<ST, KW>(c, s, e, h0, lane, la);
+    load_head<ST, OT, KW, HAS_Z>(c, s, e, h0, lane, la);
     load_item_c<ST, KW>(c, s, e, g, lane, il);
     if constexpr (SPLIT) {
       load_cb_row<ST, KW>(e, s.cb + ((int64_t)b * c.G + g) * s.T * kCbStride, kCbStride, lane, il);
@@ -992,27 +1046,27 @@ void replay_kernel(KCache c, KStep s, int d) {
     }
     if constexpr (ST == kF32) {  // a 32 KiB fp32 tile per head: no room for a second buffer
       for (int j = 0; j < nc; ++j) {
-        if (j > 0) load_head<ST, KW>(c, s, e, h0 + j, lane, la);
-        head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
+        if (j > 0) load_head<ST, OT, KW, HAS_Z>(c, s, e, h0 + j, lane, la);
+        head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j, la, il, xT, ot, lane);
       }
       continue;
     }
     int j = 0;
     for (; j + 2 < nc; j += 2) {  // heads j + 1 and j + 2 exist: prefetch unconditionally
-      load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
+      load_head<ST, OT, KW, HAS_Z>(c, s, e, h0 + j + 1, lane, lb);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
-      load_head<ST, KW>(c, s, e, h0 + j + 2, lane, la);
+      head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j, la, il, xT, ot, lane);
+      load_head<ST, OT, KW, HAS_Z>(c, s, e, h0 + j + 2, lane, la);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
+      head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
     }
     if (j + 1 < nc) {  // two heads left
-      load_head<ST, KW>(c, s, e, h0 + j + 1, lane, lb);
+      load_head<ST, OT, KW, HAS_Z>(c, s, e, h0 + j + 1, lane, lb);
       __builtin_amdgcn_sched_barrier(0);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
-      head_compute<ST, OT, KW>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
+      head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j, la, il, xT, ot, lane);
+      head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j + 1, lb, il, xT, ot, lane);
     } else {  // one head left
-      head_compute<ST, OT, KW>(c, s, e, h0 + j, la, il, xT, ot, lane);
+      head_compute<ST, OT, KW, HAS_Z>(c, s, e, h0 + j, la, il, xT, ot, lane);
     }
   }
 }
@@ -1127,7 +1181,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // appends the group's B rows.
 // ---------------------------------------------------------------------------
 
-template <int ST, int OT, int KW>
+template <int ST, int OT, int KW, bool HAS_Z>
 __global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : (KW == 32 ? 2 : 3))))
 void fused_kernel(KCache c, KStep s, int htiles) {
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
@@ -1175,7 +1229,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   // 3. the readout's loads, then the new tile's stores (in this order: one
   //    counter tracks a wave's loads and stores in issue order, so loads
   //    issued after the stores would wait for the writes)
-  load_window<ST, KW>(c, s, e, h, lane, ld);
+  load_window<ST, OT, KW, HAS_Z>(c, s, e, h, lane, ld);
   ItemLoads<ST, KW> il;
   load_item_c<ST, KW>(c, s, e, g, lane, il);
   CbLoads<KW> cl;
@@ -1206,7 +1260,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     wave_sync();
     load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   }
-  head_compute<ST, OT, KW>(c, s, e, h, ld, il, xT, ot_all[wave], lane);
+  head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, ot_all[wave], lane);
 }
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
@@ -1312,10 +1366,10 @@ int chunks_per_group(int64_t batch, int G, int hpg, int64_t resident_waves) {
   return hpg;
 }
 
-template <int ST, int OT, int KW, bool SPLIT>
+template <int ST, int OT, int KW, bool SPLIT, bool HAS_Z>
 hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
   static int resident = 0;  // blocks resident on the device (per template instance)
-  if (resident == 0) resident = resident_blocks(replay_kernel<ST, OT, KW, SPLIT>, 0);
+  if (resident == 0) resident = resident_blocks(replay_kernel<ST, OT, KW, SPLIT, HAS_Z>, 0);
   if (SPLIT) {
     const int64_t pre_items = (int64_t)s.batch * c.G;
     precompute_kernel<KW><<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
@@ -1326,35 +1380,40 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
   const int64_t items = (int64_t)s.batch * c.G * d;
   const int64_t need = (items + kWaves - 1) / kWaves;
   const int64_t blocks = need < resident ? need : resident;
-  replay_kernel<ST, OT, KW, SPLIT><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s, d);
+  replay_kernel<ST, OT, KW, SPLIT, HAS_Z><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s, d);
   return hipGetLastError();
 }
 
-template <int ST, int OT>
-hipError_t fused_t(const KCache &c, const KStep &s, hipStream_t st) {
+template <int ST, int OT, bool HAS_Z>
+hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
   const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kHeadWaves * 64);
   if (c.L <= 16)
-    fused_kernel<ST, OT, 16><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 16, HAS_Z><<<grid, block, 0, st>>>(c, s, htiles);
   else
-    fused_kernel<ST, OT, 32><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 32, HAS_Z><<<grid, block, 0, st>>>(c, s, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   step_ring_advance_kernel<<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
   return hipGetLastError();
 }
 
+template <int ST, int OT, bool SPLIT, bool HAS_Z>
+hipError_t replay_z(const KCache &c, const KStep &s, hipStream_t st) {
+  return c.L <= 16 ? replay_kw<ST, OT, 16, SPLIT, HAS_Z>(c, s, st) : replay_kw<ST, OT, 32, SPLIT, HAS_Z>(c, s, st);
+}
+
 template <int ST, int OT>
 hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
-  if (s.fold) return fused_t<ST, OT>(c, s, st);
-  return c.L <= 16 ? replay_kw<ST, OT, 16, false>(c, s, st) : replay_kw<ST, OT, 32, false>(c, s, st);
+  if (s.fold) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
+  return s.z ? replay_z<ST, OT, false, true>(c, s, st) : replay_z<ST, OT, false, false>(c, s, st);
 }
 
 template <int ST, int OT>
 hipError_t split_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
-  return c.L <= 16 ? replay_kw<ST, OT, 16, true>(c, s, st) : replay_kw<ST, OT, 32, true>(c, s, st);
+  return s.z ? replay_z<ST, OT, true, true>(c, s, st) : replay_z<ST, OT, true, false>(c, s, st);
 }
 
 template <int ST>

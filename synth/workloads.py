@@ -285,7 +285,8 @@ def make_step(spec: CacheSpec, batch: int, T: int, seed: int, pnat_max: int,
     the first `n_padding` entries (after a seeded shuffle) are padding (slot 0).
     pnat ~ U{0..pnat_max} (or `pnat_fixed`); with `varlen`, T_b ~ U{1..T} and
     the inputs are packed along cu_seqlens.  `with_z` adds an output gate
-    z ~ N(0, 1) in bf16 (drawn last, so the other values do not change).
+    z ~ N(0, 1) in bf16 (drawn last, so the other values do not change);
+    `dt_softplus` False draws dt so that dt + dt_bias follows the ring dt' law.
     """
     g = _gen(seed)
     H, G, P, N = spec.nheads, spec.ngroups, spec.headdim, spec.dstate
@@ -314,6 +315,12 @@ def make_step(spec: CacheSpec, batch: int, T: int, seed: int, pnat_max: int,
     dt = (torch.randn(ntok, H, generator=g, dtype=torch.float64) * 0.5).to(torch.float32).numpy()
     A, D, dt_bias = make_params(spec, seed + 7919)
     z = _bf16_bits(torch.randn(ntok, H, P, generator=g)) if with_z else None
+    if not dt_softplus:
+        # dt already processed by the caller: dt + dt_bias itself is the step
+        # size, drawn with the ring dt' law (log-uniform on [0.004, 0.5])
+        lo, hi = math.log(0.004), math.log(0.5)
+        dtp = torch.exp(lo + (hi - lo) * torch.rand(ntok, H, generator=g, dtype=torch.float64))
+        dt = (dtp - torch.from_numpy(dt_bias.astype(np.float64))[None, :]).to(torch.float32).numpy()
     return StepInputs(batch, T, slots, pnat.astype(np.int32), cu, x, B, C, dt, A, D, dt_bias, z,
                       dt_softplus)
 

@@ -107,6 +107,7 @@ STEP_ERRORS = [
     (dict(workspace=FAKE, workspace_bytes=16), -4, "workspace"),
     (dict(num_fold=FAKE), -2, "monolith only"),
     (dict(num_fold=FAKE + 2, algo=0), -1, "num_fold"),
+    (dict(z=FAKE + 8), -1, "z must be 16-byte aligned"),
 ]
 
 
