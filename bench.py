@@ -398,16 +398,26 @@ def _cpu_model():
     return None
 
 
+def kernel_source_sha256():
+    """Hash of the library's device and launch sources (file names and bytes)."""
+    csrc = os.path.join(ROOT, "speculative_replay_state_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".cuh", ".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed counter summary
     profiles/<kernel>_<workload>_hbm_traffic.md, or None when that summary is
     missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (kernel, workload))
-    src = os.path.join(ROOT, "speculative_replay_state_amd", "csrc", "ssu_kernels.hip")
     try:
         text = open(path).read()
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256()
     except OSError:
         return None
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)

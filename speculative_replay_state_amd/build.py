@@ -2,8 +2,10 @@
 
     python -m speculative_replay_state_amd.build
 
-Compiles csrc/ssu_kernels.hip (device code) and csrc/ssu_api.cpp (host entry
-points) and links them into speculative_replay_state_amd/libssu.so.
+Compiles the device code (csrc/ssu_kernels.cuh through ssu_kernels_inst.hip,
+once per state type, in parallel), the dispatch (csrc/ssu_launch.cpp) and the
+host entry points (csrc/ssu_api.cpp), and links them into
+speculative_replay_state_amd/libssu.so.
 """
 from __future__ import annotations
 
@@ -46,18 +48,22 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="ssu_build_") as tmp:
-        k_obj = os.path.join(tmp, "ssu_kernels.o")
-        a_obj = os.path.join(tmp, "ssu_api.o")
-        jobs = [
-            [hipcc, "--offload-arch=" + ARCH, *COMMON, "-c", os.path.join(CSRC, "ssu_kernels.hip"),
-             "-o", k_obj],
-            [hipcc, "--offload-arch=" + ARCH, *COMMON, "-x", "hip", "-c",
-             os.path.join(CSRC, "ssu_api.cpp"), "-o", a_obj],
-        ]
-        with concurrent.futures.ThreadPoolExecutor(2) as ex:
+        objs, jobs = [], []
+        # the kernels once per state type (fp32, bf16, fp16, fp8), compiled in parallel
+        for st in range(4):
+            o = os.path.join(tmp, "ssu_kernels_%d.o" % st)
+            objs.append(o)
+            jobs.append([hipcc, "--offload-arch=" + ARCH, *COMMON, "-DSSU_INST_ST=%d" % st, "-c",
+                         os.path.join(CSRC, "ssu_kernels_inst.hip"), "-o", o])
+        for src in ("ssu_launch.cpp", "ssu_api.cpp"):
+            o = os.path.join(tmp, src.replace(".cpp", ".o"))
+            objs.append(o)
+            jobs.append([hipcc, "--offload-arch=" + ARCH, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src),
+                         "-o", o])
+        with concurrent.futures.ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 1)) as ex:
             outs = list(ex.map(_run, jobs))
         tmp_lib = LIB + ".tmp%d" % os.getpid()
-        outs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp_lib, k_obj, a_obj]))
+        outs.append(_run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp_lib, *objs]))
         os.replace(tmp_lib, LIB)
     if verbose:
         for o in outs:

@@ -1,5 +1,7 @@
 // Internal interface between the host entry points (ssu_api.cpp) and the
-// gfx950 kernels (ssu_kernels.hip).  Not part of the public ABI.
+// gfx950 kernels (ssu_kernels.cuh, instantiated per state type by
+// ssu_kernels_inst.hip, dispatched in ssu_launch.cpp).  Not part of the
+// public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -55,6 +57,19 @@ struct KStep {
   const uint16_t *z;  // NULL, or the output gate (bf16) [rows][H][64]
   int dt_softplus;    // 1: dt' = softplus(dt + dt_bias); 0: dt' = dt + dt_bias
 };
+
+// Per-state-type entry points (definitions in ssu_kernels.cuh, one explicit
+// instantiation per state type).
+template <int ST>
+hipError_t replay_monolith_st(const KCache &c, const KStep &s, int out_type, hipStream_t stream);
+template <int ST>
+hipError_t replay_split_st(const KCache &c, const KStep &s, int out_type, hipStream_t stream);
+template <int ST>
+hipError_t flush_st(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int n,
+                    hipStream_t stream);
+template <int ST>
+hipError_t init_st(const KCache &c, const float *states, int64_t states_stride, const int32_t *slot_idx, int n,
+                   hipStream_t stream);
 
 hipError_t launch_replay_monolith(const KCache &c, const KStep &s, int state_type, int out_type,
                                   hipStream_t stream);

@@ -29,6 +29,8 @@
 // caller-provided fp32 scratch from a precompute kernel and a persistent
 // grid-stride kernel replays every (entry, head).  Both run the same device
 // functions in the same order, so their outputs are bit-identical.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1265,6 +1267,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
 // entry the step folded (same validity rules as the step itself).
+template <int ST>
 __global__ void step_ring_advance_kernel(KCache c, KStep s) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= s.batch) return;
@@ -1273,6 +1276,7 @@ __global__ void step_ring_advance_kernel(KCache c, KStep s) {
 }
 
 // Ring bookkeeping after a flush: ring_start <- (ring_start + k) mod L.
+template <int ST>
 __global__ void ring_advance_kernel(KCache c, const int32_t *slot_idx, const int32_t *num_fold, int n) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
@@ -1330,6 +1334,7 @@ __device__ __forceinline__ void zero_bytes(uint8_t *p, int64_t nbytes, int tid, 
     *reinterpret_cast<uint32_t *>(p + i) = 0u;
 }
 
+template <int ST>
 __global__ __launch_bounds__(256) void init_clear_kernel(KCache c, const int32_t *slot_idx) {
   const int slot = slot_idx[blockIdx.x];
   if (slot <= 0 || slot >= c.num_slots) return;
@@ -1394,7 +1399,7 @@ hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
     fused_kernel<ST, OT, 32, HAS_Z><<<grid, block, 0, st>>>(c, s, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  step_ring_advance_kernel<<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
+  step_ring_advance_kernel<ST><<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
   return hipGetLastError();
 }
 
@@ -1427,7 +1432,7 @@ hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_
     flush_kernel<ST, 32><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  ring_advance_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);
+  ring_advance_kernel<ST><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);
   return hipGetLastError();
 }
 
@@ -1438,52 +1443,34 @@ hipError_t init_t(const KCache &c, const float *states, int64_t stride, const in
                                                                                          slot_idx);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  init_clear_kernel<<<dim3((unsigned)n), dim3(256), 0, st>>>(c, slot_idx);
+  init_clear_kernel<ST><<<dim3((unsigned)n), dim3(256), 0, st>>>(c, slot_idx);
   return hipGetLastError();
 }
 
 }  // namespace
 
-#define SSU_DISPATCH_ST_OT(FN, ...)                                        \
-  switch (state_type * 2 + out_type) {                                     \
-    case kF32 * 2 + kOutF32: return FN<kF32, kOutF32>(__VA_ARGS__);        \
-    case kF32 * 2 + kOutBF16: return FN<kF32, kOutBF16>(__VA_ARGS__);      \
-    case kBF16 * 2 + kOutF32: return FN<kBF16, kOutF32>(__VA_ARGS__);      \
-    case kBF16 * 2 + kOutBF16: return FN<kBF16, kOutBF16>(__VA_ARGS__);    \
-    case kF16 * 2 + kOutF32: return FN<kF16, kOutF32>(__VA_ARGS__);        \
-    case kF16 * 2 + kOutBF16: return FN<kF16, kOutBF16>(__VA_ARGS__);      \
-    case kFP8 * 2 + kOutF32: return FN<kFP8, kOutF32>(__VA_ARGS__);        \
-    case kFP8 * 2 + kOutBF16: return FN<kFP8, kOutBF16>(__VA_ARGS__);      \
-    default: return hipErrorInvalidValue;                                  \
-  }
-
-#define SSU_DISPATCH_ST(FN, ...)                   \
-  switch (state_type) {                            \
-    case kF32: return FN<kF32>(__VA_ARGS__);       \
-    case kBF16: return FN<kBF16>(__VA_ARGS__);     \
-    case kF16: return FN<kF16>(__VA_ARGS__);       \
-    case kFP8: return FN<kFP8>(__VA_ARGS__);       \
-    default: return hipErrorInvalidValue;          \
-  }
-
-hipError_t launch_replay_monolith(const KCache &c, const KStep &s, int state_type, int out_type,
-                                  hipStream_t stream) {
-  SSU_DISPATCH_ST_OT(mono_t, c, s, stream)
+// Entry points of one state type, instantiated once per state type (each in
+// its own translation unit, so the kernels compile in parallel).
+template <int ST>
+hipError_t replay_monolith_st(const KCache &c, const KStep &s, int out_type, hipStream_t stream) {
+  return out_type == kOutF32 ? mono_t<ST, kOutF32>(c, s, stream) : mono_t<ST, kOutBF16>(c, s, stream);
 }
 
-hipError_t launch_replay_split(const KCache &c, const KStep &s, int state_type, int out_type,
-                               hipStream_t stream) {
-  SSU_DISPATCH_ST_OT(split_t, c, s, stream)
+template <int ST>
+hipError_t replay_split_st(const KCache &c, const KStep &s, int out_type, hipStream_t stream) {
+  return out_type == kOutF32 ? split_t<ST, kOutF32>(c, s, stream) : split_t<ST, kOutBF16>(c, s, stream);
 }
 
-hipError_t launch_flush(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
-                        int n, int state_type, hipStream_t stream) {
-  SSU_DISPATCH_ST(flush_t, c, slot_idx, num_fold, A, n, stream)
+template <int ST>
+hipError_t flush_st(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int n,
+                    hipStream_t stream) {
+  return flush_t<ST>(c, slot_idx, num_fold, A, n, stream);
 }
 
-hipError_t launch_init(const KCache &c, const float *states, int64_t states_stride, const int32_t *slot_idx,
-                       int n, int state_type, hipStream_t stream) {
-  SSU_DISPATCH_ST(init_t, c, states, states_stride, slot_idx, n, stream)
+template <int ST>
+hipError_t init_st(const KCache &c, const float *states, int64_t states_stride, const int32_t *slot_idx, int n,
+                   hipStream_t stream) {
+  return init_t<ST>(c, states, states_stride, slot_idx, n, stream);
 }
 
 }  // namespace ssu

@@ -162,6 +162,6 @@ def test_product_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "speculative_replay_state_amd")
     for dirpath, _, files in os.walk(pkg):
         for f in files:
-            if f.endswith((".py", ".cpp", ".hip", ".h")):
+            if f.endswith((".py", ".cpp", ".hip", ".h", ".cuh")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.lower(), f
