@@ -47,6 +47,15 @@
  *    [tok][H][P], applied to the fp64 readout; dt_softplus = 0 makes dt' the
  *    plain dt + dt_bias (FlashInfer PR, the HAS_Z output and dt_softplus
  *    flags named in its commits).
+ *  - Separate checkpoints (vLLM PR "Add separate CuTeDSL ReplaySSM
+ *    checkpoints", Overview and Claims: an FP16 recurrence checkpoint with
+ *    "SR7" and an FP8 read checkpoint with nearest encoding): with a
+ *    recurrence checkpoint, the flush folds from it, writes it back with
+ *    stochastic rounding to fp16 and writes the read checkpoint with the
+ *    nearest encoding of the same fp32 result; steps read only the read
+ *    checkpoint; init writes both from the FP32 prefill states.  "SR7" is
+ *    read as stochastic rounding with 7 random bits per value (or_sr_f16),
+ *    the bits coming from Philox4x32-10 keyed by a per-call 64-bit seed.
  *  - A padding entry (slot <= 0 or slot >= num_slots) writes zero output rows
  *    and touches no cache.  An entry with pnat < 0 or pnat + T_b > L is
  *    treated the same way and raises status bit 1; a flush entry with k < 0
@@ -191,6 +200,77 @@ uint8_t or_enc_e4m3_sat(double v) {
 double or_softplus(double v) { return v > 20.0 ? v : log1p(exp(v)); }
 
 /* ---------------------------------------------------------------------- */
+/* Counter-based random bits and stochastic rounding.                      */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Philox4x32 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011), written from its definition: a round maps
+ * (c0, c1, c2, c3) with key (k0, k1) to
+ *   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+ * with M0 = 0xD2511F53, M1 = 0xCD9E8D57 and 64-bit products split into
+ * hi / lo words; between rounds the key is bumped by the Weyl constants
+ * (0x9E3779B9, 0xBB67AE85).  The standard generator uses 10 rounds.
+ */
+void or_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds, uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < rounds; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/*
+ * The 7 random bits of value e (index p * N + n inside its head) of one
+ * (slot, head) for a given seed: Philox4x32-10 with counter
+ * (e / 16, head, slot, 0) and key (seed low word, seed high word) gives 16
+ * bytes; value e takes byte e % 16 (little-endian within each word) and uses
+ * its low 7 bits.
+ */
+static unsigned sr_bits(uint64_t seed, int slot, int head, int e) {
+  const uint32_t ctr[4] = {(uint32_t)(e / 16), (uint32_t)head, (uint32_t)slot, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  or_philox4x32(ctr, key, 10, out);
+  const int j = e % 16;
+  return (out[j / 4] >> (8 * (j % 4))) & 0x7Fu;
+}
+
+/*
+ * Stochastic rounding of an fp32 value to fp16 with 7 random bits u in
+ * [0, 128): with lo and hi the two fp16 values that bracket |v| (lo <= |v| <
+ * hi; past the largest finite value hi is infinity, standing at 2^16), the
+ * result is hi (away from zero) when u < 128 (|v| - lo) / (hi - lo), else lo;
+ * values that are exactly representable stay.  The sign is kept; NaN gives
+ * the quiet NaN 0x7E00.
+ */
+uint16_t or_sr_f16(float v, unsigned u) {
+  build_tables();
+  if (isnan(v)) return 0x7E00;
+  const uint16_t s = signbit(v) ? 0x8000 : 0;
+  const double a = fabs((double)v);
+  if (a >= 65536.0) return s | 0x7C00;
+  int lo = 0, hi = 0x7C00; /* g_f16_tab[0x7C00] = 2^16 stands for infinity */
+  while (hi - lo > 1) {    /* invariant: tab[lo] <= a < tab[hi] */
+    const int mid = (lo + hi) / 2;
+    if (g_f16_tab[mid] <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  if (g_f16_tab[lo] == a) return s | (uint16_t)lo;
+  const double frac = (a - g_f16_tab[lo]) / (g_f16_tab[hi] - g_f16_tab[lo]);
+  return s | (uint16_t)((double)u < 128.0 * frac ? hi : lo);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Cache description.                                                      */
 /* ---------------------------------------------------------------------- */
 
@@ -209,6 +289,10 @@ typedef struct {
   uint8_t *dt_cache;
   int64_t dt_stride;
   int32_t *ring_start;
+  /* Separate checkpoints: the FP16 recurrence checkpoint (same layout as the
+   * state, element type fp16) or NULL when the state is the only checkpoint. */
+  uint8_t *recur;
+  int64_t recur_stride;
 } or_cache;
 
 static int state_elem_bytes(int dt) {
@@ -261,6 +345,30 @@ static void decode_state(const or_cache *c, int slot, int head, double *h) {
       }
       h[p * N + n] = v;
     }
+  }
+}
+
+/* Decode the FP16 recurrence checkpoint of (slot, head) into h[P*N]. */
+static void decode_recur(const or_cache *c, int slot, int head, double *h) {
+  const int P = c->headdim, N = c->dstate;
+  const uint8_t *base = c->recur + (int64_t)slot * c->recur_stride + (int64_t)head * P * N * 2;
+  for (int p = 0; p < P; ++p)
+    for (int n = 0; n < N; ++n) {
+      uint16_t u;
+      memcpy(&u, base + elem_offset(c, 2, p, n), 2);
+      h[p * N + n] = or_f16_value(u);
+    }
+}
+
+/* Write one row of an fp32 state into the recurrence checkpoint with
+ * stochastic rounding (random bits from the seed, slot, head and index). */
+static void encode_recur_row(const or_cache *c, int slot, int head, int p, const float *row,
+                             uint64_t seed) {
+  const int P = c->headdim, N = c->dstate;
+  uint8_t *base = c->recur + (int64_t)slot * c->recur_stride + (int64_t)head * P * N * 2;
+  for (int n = 0; n < N; ++n) {
+    const uint16_t u = or_sr_f16(row[n], sr_bits(seed, slot, head, p * N + n));
+    memcpy(base + elem_offset(c, 2, p, n), &u, 2);
   }
 }
 
@@ -441,7 +549,7 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
  * flush's FP32 state), re-encode it, and advance ring_start by k (mod L).
  */
 int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
-             const int32_t *num_fold, const float *A) {
+             const int32_t *num_fold, const float *A, uint64_t seed) {
   const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
             L = c->ring_len, HPG = H / G;
   int status = 0;
@@ -461,7 +569,10 @@ int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
       double *xv = (double *)malloc(sizeof(double) * P);
       double *Bv = (double *)malloc(sizeof(double) * N);
       float *row = (float *)malloc(sizeof(float) * N);
-      decode_state(c, slot, hh, h);
+      if (c->recur)
+        decode_recur(c, slot, hh, h); /* separate checkpoints: fold the FP16 recurrence one */
+      else
+        decode_state(c, slot, hh, h);
       const uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
       const uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
       const uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
@@ -480,6 +591,7 @@ int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
         for (int p = 0; p < P; ++p) {
           for (int q = 0; q < N; ++q) row[q] = (float)h[p * N + q];
           encode_row(c, slot, hh, p, row);
+          if (c->recur) encode_recur_row(c, slot, hh, p, row, seed);
         }
       }
       free(h); free(xv); free(Bv); free(row);
@@ -503,7 +615,7 @@ int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
  * slot's x/B/dt rings and set ring_start to 0.  Invalid slots are ignored.
  */
 void or_init_state(const or_cache *c, const float *states, int64_t states_stride,
-                   const int32_t *slot_idx, int n) {
+                   const int32_t *slot_idx, int n, uint64_t seed) {
   const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
             L = c->ring_len;
   build_tables();
@@ -518,8 +630,10 @@ void or_init_state(const or_cache *c, const float *states, int64_t states_stride
         store_state_f64(c, slot, hh, h);
         free(h);
       } else {
-        for (int p = 0; p < P; ++p)
+        for (int p = 0; p < P; ++p) {
           encode_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N);
+          if (c->recur) encode_recur_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N, seed);
+        }
       }
     }
     memset(c->x_cache + (int64_t)slot * c->x_stride, 0, (size_t)H * L * P * 2);
@@ -550,6 +664,12 @@ void or_f16_value_array(const uint16_t *b, double *out, int64_t n) {
 }
 void or_e4m3_value_array(const uint8_t *b, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = or_e4m3_value(b[i]);
+}
+void or_sr_f16_array(const float *v, const uint8_t *u, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_sr_f16(v[i], u[i]);
+}
+void or_sr_bits_array(uint64_t seed, int slot, int head, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)sr_bits(seed, slot, head, (int)i);
 }
 void or_softplus_array(const double *v, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = or_softplus(v[i]);

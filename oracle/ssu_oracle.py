@@ -54,6 +54,7 @@ class _OrCache(ctypes.Structure):
         ("B_cache", ctypes.c_void_p), ("B_stride", ctypes.c_int64),
         ("dt_cache", ctypes.c_void_p), ("dt_stride", ctypes.c_int64),
         ("ring_start", ctypes.c_void_p),
+        ("recur", ctypes.c_void_p), ("recur_stride", ctypes.c_int64),
     ]
 
 
@@ -67,9 +68,15 @@ def lib():
             L.or_replay_step.argtypes = [ctypes.POINTER(_OrCache), I, I, P, P, P, P, P, P, P,
                                          P, P, P, P, I, P]
             L.or_flush.restype = I
-            L.or_flush.argtypes = [ctypes.POINTER(_OrCache), I, P, P, P]
+            L.or_flush.argtypes = [ctypes.POINTER(_OrCache), I, P, P, P, ctypes.c_uint64]
             L.or_init_state.restype = None
-            L.or_init_state.argtypes = [ctypes.POINTER(_OrCache), P, I64, P, I]
+            L.or_init_state.argtypes = [ctypes.POINTER(_OrCache), P, I64, P, I, ctypes.c_uint64]
+            L.or_philox4x32.restype = None
+            L.or_philox4x32.argtypes = [P, P, I, P]
+            L.or_sr_f16_array.restype = None
+            L.or_sr_f16_array.argtypes = [P, P, P, I64]
+            L.or_sr_bits_array.restype = None
+            L.or_sr_bits_array.argtypes = [ctypes.c_uint64, I, I, P, I64]
             for name in ("or_enc_bf16_array", "or_enc_f16_array", "or_enc_e4m3_array",
                          "or_bf16_value_array", "or_f16_value_array", "or_e4m3_value_array",
                          "or_softplus_array"):
@@ -100,6 +107,8 @@ def _as_orcache(cache) -> _OrCache:
               cache.ring_start):
         assert a.flags["C_CONTIGUOUS"]
     assert cache.ring_start.dtype == np.int32
+    recur = getattr(cache, "recur", None)
+    assert recur is None or recur.flags["C_CONTIGUOUS"]
     return _OrCache(
         s.num_slots, s.nheads, s.ngroups, s.headdim, s.dstate, s.ring_len,
         _DTYPE_CODE[s.state_dtype], {"rowmajor": 0, "tiled": 1}[s.state_layout],
@@ -108,13 +117,14 @@ def _as_orcache(cache) -> _OrCache:
         cache.x_cache.ctypes.data, cache.x_cache.shape[1],
         cache.B_cache.ctypes.data, cache.B_cache.shape[1],
         cache.dt_cache.ctypes.data, cache.dt_cache.shape[1],
-        cache.ring_start.ctypes.data)
+        cache.ring_start.ctypes.data,
+        None if recur is None else recur.ctypes.data, 0 if recur is None else recur.shape[1])
 
 
 _STATUS_BAD_FOLD = 2
 
 
-def replay_step(cache, step, num_fold=None):
+def replay_step(cache, step, num_fold=None, seed=0):
     """Replay step (see or_replay_step).  Returns (out fp64 [tokens, H, P], status).
 
     The step's optional `z` (bf16 bits like x) gates the output with
@@ -127,10 +137,10 @@ def replay_step(cache, step, num_fold=None):
     step then runs with pnat - k live tokens from the new ring start; an entry
     with k outside [0, pnat] is skipped like padding (zero output rows, cache
     untouched) and reported with status bit 2.  This is by definition the
-    composition of flush and replay_step below.
+    composition of flush (with `seed`) and replay_step below.
     """
     if num_fold is not None:
-        return _fused_step(cache, step, np.asarray(num_fold, np.int32))
+        return _fused_step(cache, step, np.asarray(num_fold, np.int32), seed)
     s = cache.spec
     oc = _as_orcache(cache)
     ntok = step.tokens
@@ -156,7 +166,7 @@ def replay_step(cache, step, num_fold=None):
     return out, st
 
 
-def _fused_step(cache, step, k):
+def _fused_step(cache, step, k, seed):
     s = cache.spec
     assert k.shape == (step.batch,)
     if step.cu_seqlens is not None:
@@ -185,7 +195,7 @@ def _fused_step(cache, step, k):
             fold_k.append(kb)
             pnat[b] = p - kb
     if fold_slots:
-        st = flush(cache, np.array(fold_slots, np.int32), np.array(fold_k, np.int32), step.A)
+        st = flush(cache, np.array(fold_slots, np.int32), np.array(fold_k, np.int32), step.A, seed)
         assert st == 0
     sub = _replace(step, slot_idx=slots, pnat=pnat)
     out, st = replay_step(cache, sub)
@@ -197,17 +207,20 @@ def _replace(step, **kw):
     return dataclasses.replace(step, **kw)
 
 
-def flush(cache, slot_idx, num_fold, A):
-    """Fold the first k live ring tokens into each listed slot's checkpoint."""
+def flush(cache, slot_idx, num_fold, A, seed=0):
+    """Fold the first k live ring tokens into each listed slot's checkpoint
+    (with a recurrence checkpoint: fold from it, write it back with
+    stochastic rounding drawn from `seed`, and re-encode the read one)."""
     oc = _as_orcache(cache)
     slots = _c(slot_idx, np.int32)
     k = _c(num_fold, np.int32)
     A = _c(A, np.float32)
     assert slots.shape == k.shape
-    return lib().or_flush(ctypes.byref(oc), slots.shape[0], _ptr(slots), _ptr(k), _ptr(A))
+    return lib().or_flush(ctypes.byref(oc), slots.shape[0], _ptr(slots), _ptr(k), _ptr(A),
+                          ctypes.c_uint64(int(seed)))
 
 
-def init_state(cache, states, slot_idx, states_stride=None):
+def init_state(cache, states, slot_idx, states_stride=None, seed=0):
     """Encode fp32 states [n, H, P, N] into the listed slots and clear their rings."""
     s = cache.spec
     oc = _as_orcache(cache)
@@ -217,7 +230,7 @@ def init_state(cache, states, slot_idx, states_stride=None):
         states = np.ascontiguousarray(states)
         states_stride = s.nheads * s.headdim * s.dstate
     lib().or_init_state(ctypes.byref(oc), states.ctypes.data, int(states_stride), _ptr(slots),
-                        slots.shape[0])
+                        slots.shape[0], ctypes.c_uint64(int(seed)))
 
 
 def set_threads(n: int) -> None:
@@ -227,6 +240,39 @@ def set_threads(n: int) -> None:
 
 def max_threads() -> int:
     return int(lib().or_max_threads())
+
+
+def philox4x32(ctr, key, rounds=10):
+    """Philox4x32 with the given round count: four 32-bit counter words and
+    two key words in, four words out."""
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    assert c.shape == (4,) and k.shape == (2,)
+    out = np.empty(4, np.uint32)
+    lib().or_philox4x32(c.ctypes.data, k.ctypes.data, int(rounds), out.ctypes.data)
+    return out
+
+
+def sr_f16(v, u):
+    """Stochastic rounding of fp32 values to fp16 bits with 7-bit randoms u."""
+    v = np.ascontiguousarray(v, np.float32)
+    u = np.ascontiguousarray(u, np.uint8)
+    assert v.shape == u.shape
+    out = np.empty(v.shape, np.uint16)
+    lib().or_sr_f16_array(v.ctypes.data, u.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def sr_bits(seed, slot, head, n):
+    """The 7-bit randoms of values 0..n-1 of (slot, head) for `seed`."""
+    out = np.empty(n, np.uint8)
+    lib().or_sr_bits_array(ctypes.c_uint64(int(seed)), int(slot), int(head), out.ctypes.data, n)
+    return out
+
+
+def decode_recur(cache, slot):
+    """fp64 [H, P, N] value of one slot's FP16 recurrence checkpoint."""
+    return f16_value(cache.recur_logical(slot))
 
 
 def _arr(fn, a, in_dtype, out_dtype):

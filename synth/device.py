@@ -21,12 +21,14 @@ _STRIDE_KEY = {"state": "state", "scale": "scale", "x_cache": "x", "B_cache": "B
 def upload_cache(cache: CacheArrays, device) -> Dict[str, torch.Tensor]:
     t = {f: torch.from_numpy(getattr(cache, f)).to(device) for f in CACHE_FIELDS}
     t["ring_start"] = torch.from_numpy(cache.ring_start).to(device)
+    t["recur"] = None if cache.recur is None else torch.from_numpy(cache.recur).to(device)
     return t
 
 
 def download_cache(spec: CacheSpec, t: Dict[str, torch.Tensor]) -> CacheArrays:
+    recur = t.get("recur")
     return CacheArrays(spec, *(t[f].cpu().numpy() for f in CACHE_FIELDS),
-                       t["ring_start"].cpu().numpy())
+                       t["ring_start"].cpu().numpy(), None if recur is None else recur.cpu().numpy())
 
 
 def download_subset(spec: CacheSpec, t: Dict[str, torch.Tensor], slots: Sequence[int]):
@@ -39,7 +41,9 @@ def download_subset(spec: CacheSpec, t: Dict[str, torch.Tensor], slots: Sequence
     sub = CacheSpec(**{**spec.__dict__, "num_slots": len(slots) + 1})
     arrs = [t[f].index_select(0, idx).cpu().numpy() for f in CACHE_FIELDS]
     rs = t["ring_start"].index_select(0, idx).cpu().numpy()
-    return CacheArrays(sub, *arrs, rs), {s: i + 1 for i, s in enumerate(slots)}
+    recur = t.get("recur")
+    recur = None if recur is None else recur.index_select(0, idx).cpu().numpy()
+    return CacheArrays(sub, *arrs, rs, recur), {s: i + 1 for i, s in enumerate(slots)}
 
 
 def _bf16_bytes(x: torch.Tensor) -> torch.Tensor:
@@ -79,6 +83,13 @@ def make_cache_device(spec: CacheSpec, seed: int, device, h0_std: float = 0.1,
         d = torch.exp(lo + (hi - lo) * torch.rand(n, H, L, generator=g, device=device))
         t["dt_cache"][sl, : spec.dt_bytes()] = d.view(torch.uint8).reshape(n, -1)
     t["ring_start"] = torch.randint(0, L, (S,), generator=g, device=device, dtype=torch.int32)
+    t["recur"] = None
+    if spec.separate:
+        t["recur"] = torch.full((S, st["recur"]), CANARY, dtype=torch.uint8, device=device)
+        for s0 in range(0, S, chunk_slots):
+            n = min(chunk_slots, S - s0)
+            h0 = torch.randn(n, H, P, N, generator=g, device=device) * h0_std
+            t["recur"][s0:s0 + n, : spec.recur_bytes()] = h0.to(torch.float16).view(torch.uint8).reshape(n, -1)
     return t
 
 

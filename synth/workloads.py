@@ -59,6 +59,7 @@ class CacheSpec:
     state_dtype: str = "bf16"
     slot_pad: int = 0  # bytes appended to every per-slot stride
     state_layout: str = ""  # "tiled" (the library's layout, 64 x 128 heads) or "rowmajor"
+    separate: bool = False  # an FP16 recurrence checkpoint next to the read checkpoint
 
     def __post_init__(self):
         assert self.state_dtype in DTYPES
@@ -71,6 +72,9 @@ class CacheSpec:
     # packed per-slot byte sizes
     def state_bytes(self):
         return self.nheads * self.headdim * self.dstate * ELEM_BYTES[self.state_dtype]
+
+    def recur_bytes(self):
+        return self.nheads * self.headdim * self.dstate * 2
 
     def scale_bytes(self):
         return self.nheads * self.headdim * 4
@@ -87,13 +91,16 @@ class CacheSpec:
     def strides(self):
         """Per-slot byte strides (packed size rounded to 16 B, plus the pad)."""
         p = self.slot_pad
-        return dict(
+        d = dict(
             state=_round16(self.state_bytes()) + p,
             scale=_round16(self.scale_bytes()) + p,
             x=_round16(self.x_bytes()) + p,
             B=_round16(self.B_bytes()) + p,
             dt=_round16(self.dt_bytes()) + p,
         )
+        if self.separate:
+            d["recur"] = _round16(self.recur_bytes()) + p
+        return d
 
 
 def tiled_index(eb: int) -> np.ndarray:
@@ -122,11 +129,25 @@ class CacheArrays:
     B_cache: np.ndarray
     dt_cache: np.ndarray
     ring_start: np.ndarray  # int32 [num_slots]
+    recur: Optional[np.ndarray] = None  # uint8 [num_slots, stride]: FP16 recurrence checkpoint
 
     def copy(self) -> "CacheArrays":
         return CacheArrays(self.spec, *(a.copy() for a in (
             self.state, self.scale, self.x_cache, self.B_cache, self.dt_cache,
-            self.ring_start)))
+            self.ring_start)), None if self.recur is None else self.recur.copy())
+
+    def recur_view(self, slot):
+        """Recurrence checkpoint (fp16 bits) of one slot in storage order, [H, P * N]."""
+        s = self.spec
+        return self.recur[slot, : s.recur_bytes()].view(np.uint16).reshape(s.nheads, s.headdim * s.dstate)
+
+    def recur_logical(self, slot):
+        """Recurrence checkpoint (fp16 bits) of one slot as [H, P, N] (a copy)."""
+        s = self.spec
+        v = self.recur_view(slot)
+        if s.state_layout == "rowmajor":
+            return v.reshape(s.nheads, s.headdim, s.dstate).copy()
+        return v[:, tiled_index(2)]
 
     # typed views of the packed part of one slot (for tests)
     def _state_np_dtype(self):
@@ -260,8 +281,13 @@ def make_cache(spec: CacheSpec, seed: int, h0_std: float = 0.1) -> CacheArrays:
     _fill_slots(arrs["B"], Br)
     _fill_slots(arrs["dt"], dtr)
     ring_start = torch.randint(0, L, (S,), generator=g, dtype=torch.int32).numpy()
+    recur = None
+    if spec.separate:  # drawn last, so the other values do not depend on the mode
+        recur = arrs["recur"]
+        h0r = torch.randn(S, H, P, N, generator=g, dtype=torch.float64) * h0_std
+        _fill_slots(recur, _f16_bits(h0r.to(torch.float32)).view(np.uint8).reshape(S, -1))
     return CacheArrays(spec, arrs["state"], arrs["scale"], arrs["x"], arrs["B"], arrs["dt"],
-                       ring_start.copy())
+                       ring_start.copy(), recur)
 
 
 def make_params(spec: CacheSpec, seed: int):
