@@ -245,15 +245,18 @@ static unsigned sr_bits(uint64_t seed, int slot, int head, int e) {
 
 /*
  * Stochastic rounding of an fp32 value to fp16 with 7 random bits u in
- * [0, 128): with lo and hi the two fp16 values that bracket |v| (lo <= |v| <
- * hi; past the largest finite value hi is infinity, standing at 2^16), the
- * result is hi (away from zero) when u < 128 (|v| - lo) / (hi - lo), else lo;
- * values that are exactly representable stay.  The sign is kept; NaN gives
- * the quiet NaN 0x7E00.
+ * [0, 128), in the usual few-random-bits form: with lo and hi the two fp16
+ * values that bracket |v| (lo <= |v| < hi; past the largest finite value hi
+ * is infinity, standing at 2^16) and f = (|v| - lo) / (hi - lo), keep the
+ * top 7 bits of f, floor(128 f), add u, and round away from zero (to hi)
+ * when the sum carries, i.e. floor(128 f) + u >= 128, else to lo.  Values
+ * that are exactly representable stay; a value rounds away with probability
+ * floor(128 f) / 128.  The sign is kept; NaN gives a quiet NaN (0x7E00 with
+ * the sign of v).
  */
 uint16_t or_sr_f16(float v, unsigned u) {
   build_tables();
-  if (isnan(v)) return 0x7E00;
+  if (isnan(v)) return signbit(v) ? 0xFE00 : 0x7E00;
   const uint16_t s = signbit(v) ? 0x8000 : 0;
   const double a = fabs((double)v);
   if (a >= 65536.0) return s | 0x7C00;
@@ -266,8 +269,8 @@ uint16_t or_sr_f16(float v, unsigned u) {
       hi = mid;
   }
   if (g_f16_tab[lo] == a) return s | (uint16_t)lo;
-  const double frac = (a - g_f16_tab[lo]) / (g_f16_tab[hi] - g_f16_tab[lo]);
-  return s | (uint16_t)((double)u < 128.0 * frac ? hi : lo);
+  const double frac = (a - g_f16_tab[lo]) / (g_f16_tab[hi] - g_f16_tab[lo]); /* exact */
+  return s | (uint16_t)(floor(128.0 * frac) + (double)u >= 128.0 ? hi : lo);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -3,7 +3,9 @@
 vLLM PR "Add separate CuTeDSL ReplaySSM checkpoints" (Overview, Claims):
 an FP16 recurrence checkpoint written with stochastic rounding ("SR7") and
 an FP8 read checkpoint written with nearest encoding.  Readings: "SR7" =
-stochastic rounding with 7 random bits per value; the bits come from
+stochastic rounding with 7 random bits per value in the usual form (the top
+7 bits of the discarded fraction plus 7 random bits, rounding away from zero
+on a carry); the bits come from
 Philox4x32-10 keyed by a per-call 64-bit seed with counter (value / 16,
 head, slot, 0).  Pinned against the generator's published known-answer
 vectors, an independent numpy statement of stochastic rounding checked over
@@ -39,7 +41,8 @@ def test_philox_known_answers(oracle, ctr, key, out):
 def _sr_numpy(v, u):
     """Stochastic rounding fp32 -> fp16 by its definition, in numpy: lo, hi
     bracket |v| among the fp16 values (hi = 2^16 standing for infinity past
-    65504); round away from zero iff u < 128 (|v| - lo) / (hi - lo)."""
+    65504), f = (|v| - lo) / (hi - lo); round away from zero iff
+    floor(128 f) + u >= 128."""
     with np.errstate(all="ignore"):
         return _sr_numpy_impl(np.asarray(v, np.float32), u)
 
@@ -55,7 +58,7 @@ def _sr_numpy_impl(v, u):
     hi = np.where(np.isinf(hi) & np.isfinite(lo), 65536.0, hi)
     with np.errstate(invalid="ignore", divide="ignore"):
         frac = np.where(np.isfinite(lo) & (hi > lo), (a - lo) / (hi - lo), 0.0)
-    up = u.astype(np.float64) < 128.0 * frac
+    up = np.floor(128.0 * frac) + u.astype(np.float64) >= 128.0
     res = np.where(up, hi, lo)
     res = np.where(res >= 65536.0, np.inf, res)
     out = (np.sign(v) * res).astype(np.float16)
@@ -86,7 +89,7 @@ def test_sr_matches_definition_for_every_random_value(oracle):
 
 def test_sr_counts_and_exact_values(oracle):
     """Over the 128 random values a value rounds away from zero exactly
-    ceil(128 frac) times; fp16 values never move."""
+    floor(128 frac) times; fp16 values never move."""
     rng = np.random.default_rng(12)
     v = (rng.standard_normal(300) * 0.5).astype(np.float32)
     all_u = np.arange(128, dtype=np.uint8)
@@ -102,7 +105,22 @@ def test_sr_counts_and_exact_values(oracle):
         lo, hi = float(lo), float(hi)
         assert np.all((res == lo) | (res == hi))
         frac = (a - lo) / (hi - lo)
-        assert int(np.sum(res == hi)) == int(np.ceil(128 * frac)), (x, frac)
+        assert int(np.sum(res == hi)) == int(np.floor(128 * frac)), (x, frac)
+
+
+def test_sr_special_values(oracle):
+    """NaN stays a quiet NaN with its sign; values below 1/128 of the fp16
+    spacing above an fp16 value never round away; 65504 < |v| < 65536 goes
+    to infinity only from the top 7 bits of its fraction."""
+    u = np.arange(128, dtype=np.uint8)
+    nan = oracle.sr_f16(np.full(128, np.nan, np.float32), u)
+    assert np.all(nan == 0x7E00)
+    assert np.all(oracle.sr_f16(np.full(128, -np.nan, np.float32), u) == 0xFE00)
+    tiny = np.float32(2.0 ** -24 / 256)  # 1/256 of the subnormal spacing
+    assert np.all(oracle.sr_f16(np.full(128, tiny, np.float32), u) == 0)
+    big = np.float32(65504.0 + 32.0 * 0.75)  # f = 3/4 between 65504 and "65536"
+    got = oracle.sr_f16(np.full(128, big, np.float32), u)
+    assert int(np.sum(got == 0x7C00)) == 96 and int(np.sum(got == 0x7BFF)) == 32
 
 
 def test_sr_bits_come_from_philox(oracle):
@@ -115,13 +133,13 @@ def test_sr_bits_come_from_philox(oracle):
 
 
 def test_sr_is_unbiased_up_to_the_7_bit_resolution(oracle):
-    """Mean over many seeds: lo + (hi - lo) ceil(128 frac) / 128."""
+    """Mean over many seeds: lo + (hi - lo) floor(128 frac) / 128."""
     x = np.float32(0.123456)
     lo = float(np.float16(x)) if float(np.float16(x)) <= float(x) else float(
         np.nextafter(np.float16(x), np.float16(0)))
     hi = float(np.nextafter(np.float16(lo), np.float16(np.inf)))
     frac = (float(x) - lo) / (hi - lo)
-    p = np.ceil(128 * frac) / 128
+    p = np.floor(128 * frac) / 128
     n = 4000
     got = np.array([oracle.sr_f16(np.array([x]), oracle.sr_bits(s, 1, 0, 1)).view(np.float16)[0]
                     for s in range(n)], np.float64)
