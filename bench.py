@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload fp8|prod|mtp|large|tiny]
                     [--algo auto|monolith|split] [--batch B] [--no-cpu-baseline]
+                    [--no-fuse] [--separate]
 
 One step = one pass of the whole hot path over one batch: the replay step
 (dt' softplus, decay prefix, C.B, checkpoint replay and readout, ring appends)
@@ -13,7 +14,9 @@ T = 4 new tokens, k ~ U{1..4} accepted tokens flushed every step.  By
 default the flush is fused into the step: each call folds the k tokens the
 previous step accepted (pnat = num_fold = k) and then replays the 4 new ones,
 reading each checkpoint once; --no-fuse times the step with pnat = 0 followed
-by a separate ssu_flush of k tokens instead.
+by a separate ssu_flush of k tokens instead.  --separate (fp8 workload) adds
+the FP16 recurrence checkpoint: folds read and write it (stochastic rounding,
+a new seed every call) and write the fp8 read checkpoint the steps read.
 
 Inputs are synthetic, drawn on the GPU (synth package) and resident in HBM
 before timing.  To measure HBM rather than the 256 MB Infinity Cache the
@@ -99,6 +102,18 @@ def fused_bytes(spec, H, G, k, Tb, out_bytes=2):
     return step_bytes(spec, H, G, [0] * len(k), Tb, out_bytes) + flush_bytes(spec, H, G, k) - saved
 
 
+def recur_bytes(H):
+    """FP16 recurrence checkpoint bytes of one slot (separate checkpoints)."""
+    return H * 64 * 128 * 2
+
+
+def separate_extra_bytes(spec, H, k):
+    """What separate checkpoints add to a fold of each entry with k > 0: the
+    recurrence checkpoint is read and written, the read checkpoint (+ scales)
+    only written."""
+    return int(sum(2 * recur_bytes(H) - state_bytes(spec, H) for kk in k if kk > 0))
+
+
 def flush_bytes(spec, H, G, k):
     """Algorithmic bytes of one flush: checkpoint read + write and the k ring
     tokens (x, B, dt') read, per entry with k > 0."""
@@ -125,6 +140,8 @@ def main():
     ap.add_argument("--fuse", action=argparse.BooleanOptionalAction, default=True,
                     help="flush workloads: fold the accepted tokens inside the replay step (one "
                          "ssu_replay_step with num_fold) instead of a separate ssu_flush call")
+    ap.add_argument("--separate", action="store_true",
+                    help="fp8 workload: separate FP16 recurrence checkpoint (stochastic rounding)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +159,9 @@ def main():
     wl = dict(WORKLOADS[args.workload])
     wl_batch = wl["batch"]
     fused = bool(wl["flush"]) and args.fuse
+    if args.separate and (not wl["flush"] or wl["state_dtype"] != "fp8"):
+        print("--separate needs a workload with flushes and an fp8 checkpoint (fp8)", file=sys.stderr)
+        sys.exit(2)
     if args.batch:
         wl["batch"] = args.batch
     batch, H, G, T = wl["batch"], wl["nheads"], wl["ngroups"], wl["T"]
@@ -149,7 +169,7 @@ def main():
 
     # --- cache with rotating arenas (HBM, not the Infinity Cache) -----------
     probe = synth.CacheSpec(num_slots=2, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
-                            slot_pad=wl["slot_pad"])
+                            slot_pad=wl["slot_pad"], separate=args.separate)
     st_ = probe.strides()
     slot_bytes = sum(st_.values())
     if args.arenas is None:
@@ -160,12 +180,12 @@ def main():
         arenas = args.arenas
     num_slots = arenas * batch + 1
     spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
-                           slot_pad=wl["slot_pad"])
+                           slot_pad=wl["slot_pad"], separate=args.separate)
     tcache = sd.make_cache_device(spec, args.seed, dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     dc = ssu.DeviceCache(num_slots, H, G, spec.ring_len, spec.state_dtype, tcache["state"],
                          tcache["scale"], tcache["x_cache"], tcache["B_cache"], tcache["dt_cache"],
-                         tcache["ring_start"], status)
+                         tcache["ring_start"], status, recur=tcache.get("recur"))
 
     rng = np.random.default_rng(args.seed)
     perm = rng.permutation(np.arange(1, num_slots, dtype=np.int32))
@@ -206,6 +226,7 @@ def main():
         a = i % arenas
         if ev is not None:
             ev[0].record(stream)
+        descs[a].sr_seed = i  # a new stochastic-rounding seed every call (separate checkpoints)
         rc = ssu.ssu_replay_step(cdesc, descs[a], sh)
         if rc:
             raise ssu.SsuError(rc, ssu.ssu_last_error())
@@ -214,7 +235,7 @@ def main():
         if wl["flush"] and not fused:
             t = tsteps[a]
             rc = ssu.ssu_flush(cdesc, t["slot_idx"].data_ptr(), flush_k[a].data_ptr(), t["A"].data_ptr(),
-                               batch, sh)
+                               batch, sr_seed=i, stream=sh)
             if rc:
                 raise ssu.SsuError(rc, ssu.ssu_last_error())
             if ev is not None:
@@ -268,11 +289,14 @@ def main():
     tbs = [np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch for s in steps_in]
     if fused:
         sbytes = float(np.mean([fused_bytes(spec, H, G, k.cpu().numpy(), tb, ob)
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if args.separate else 0)
                                 for k, tb in zip(flush_k, tbs)]))
         fbytes = 0.0
     else:
         sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat, tb, ob) for s, tb in zip(steps_in, tbs)]))
-        fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy()) for k in flush_k])) if flush_k else 0.0
+        fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy())
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if args.separate else 0)
+                                for k in flush_k])) if flush_k else 0.0
     step_avg = float(np.mean(step_ms))
     kernels = {"replay_step": {"algo": algo_used, "fused_flush": fused, "avg_us": 1e3 * step_avg,
                                "bytes": sbytes, "GBps": sbytes / (step_avg * 1e6)}}
@@ -317,6 +341,8 @@ def main():
             "workload": args.workload + ": " + wl["desc"],
             "batch": batch, "nheads": H, "ngroups": G, "headdim": 64, "dstate": 128, "ring_len": 16,
             "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "algo": algo_used,
+            "separate_checkpoints": (None if not args.separate else
+                                     "FP16 recurrence checkpoint, stochastic rounding, fp8 read checkpoint"),
             "flush": (None if not wl["flush"] else
                       "fused into the replay step (ssu_replay_step with num_fold = pnat = k)" if fused
                       else "separate ssu_flush after the step"),
@@ -333,7 +359,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": (measured_traffic(dominant, args.workload + ("_fused" if fused else ""))
+            "traffic": (measured_traffic(dominant, args.workload + ("_fused" if fused else "")
+                                         + ("_separate" if args.separate else ""))
                         if batch == wl_batch else None),
         },
         "kernels": kernels,
@@ -363,11 +390,11 @@ def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused):
         while True:
             c = host.copy()
             if fused:
-                O.replay_step(c, sub, num_fold=k)
+                O.replay_step(c, sub, num_fold=k, seed=reps)
             else:
                 O.replay_step(c, sub)
                 if k is not None:
-                    O.flush(c, sub.slot_idx, k, sub.A)
+                    O.flush(c, sub.slot_idx, k, sub.A, reps)
             tokens += sub.tokens
             reps += 1
             el = time.perf_counter() - t0

@@ -109,6 +109,19 @@ enum {
  * all 64 lanes side by side, so every 16-byte-per-lane load or store of a
  * row block is 1 KiB contiguous.  ssu_init_state writes this layout from
  * plain row-major fp32 [headdim][dstate] states.
+ * Separate checkpoints [VP Overview, Claims]: recur_state [slot][nheads][64 *
+ * 128] fp16 in the same tiled layout as state (or NULL for one shared
+ * checkpoint).  With it, state is the read checkpoint every step reads, and
+ * recur_state the recurrence checkpoint: flushes fold from it, write it back
+ * with stochastic rounding (below) and write state with the nearest encoding
+ * of the same fp32 result; init writes both.  Stochastic rounding: a value
+ * goes to the fp16 neighbour away from zero when floor(128 f) + u >= 128,
+ * f = (|v| - lo) / (hi - lo) (lo <= |v| < hi its fp16 neighbours, infinity
+ * past 65504), else toward zero; u is the low 7 bits of byte e % 16 of
+ * Philox4x32-10 at counter (e / 16, head, slot, 0) keyed by the call's
+ * 64-bit sr_seed (e = p * 128 + n); a caller passes a different seed on
+ * every call.  recur_state requires
+ * state_dtype == SSU_FP8_E4M3 (else SSU_ERR_UNSUPPORTED).
  * Requirements: headdim == 64, dstate == 128, nheads % ngroups == 0,
  * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer and slot stride
  * 16-byte aligned.  status may be NULL.
@@ -129,6 +142,8 @@ typedef struct ssu_cache {
   int64_t dt_slot_stride;
   int32_t *ring_start;
   int32_t *status;
+  void *recur_state;
+  int64_t recur_slot_stride;
 } ssu_cache;
 
 /*
@@ -179,6 +194,7 @@ typedef struct ssu_step {
   const int32_t *num_fold;
   const void *z;
   int32_t no_dt_softplus;
+  uint64_t sr_seed; /* stochastic-rounding seed of a fused fold (separate checkpoints) */
 } ssu_step;
 
 /* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen):
@@ -197,7 +213,7 @@ size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seq
  * slot ids must be unique.  n == 0 is a no-op.
  */
 int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
-                   const int32_t *slot_idx, int32_t n, hipStream_t stream);
+                   const int32_t *slot_idx, int32_t n, uint64_t sr_seed, hipStream_t stream);
 
 /*
  * One replay step [FI items 1-2; VD selective_state_update_replayssm].
@@ -235,7 +251,7 @@ int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t st
  * The caller's next pnat for the slot is pnat + accepted - k.
  */
 int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold,
-              const float *A, int32_t n, hipStream_t stream);
+              const float *A, int32_t n, uint64_t sr_seed, hipStream_t stream);
 
 /* The algorithm SSU_ALGO_AUTO resolves to for this step (MONOLITH or SPLIT),
  * or a negative error code. */

@@ -53,6 +53,7 @@ class SsuCache(ctypes.Structure):
         ("B_cache", _P), ("B_slot_stride", _I64),
         ("dt_cache", _P), ("dt_slot_stride", _I64),
         ("ring_start", _P), ("status", _P),
+        ("recur_state", _P), ("recur_slot_stride", _I64),
     ]
 
 
@@ -64,18 +65,18 @@ class SsuStep(ctypes.Structure):
         ("A", _P), ("D", _P), ("dt_bias", _P),
         ("out", _P), ("out_dtype", ctypes.c_int),
         ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("algo", ctypes.c_int),
-        ("num_fold", _P), ("z", _P), ("no_dt_softplus", _I32),
+        ("num_fold", _P), ("z", _P), ("no_dt_softplus", _I32), ("sr_seed", ctypes.c_uint64),
     ]
 
 
 _lib.ssu_workspace_size.restype = ctypes.c_size_t
 _lib.ssu_workspace_size.argtypes = [ctypes.POINTER(SsuCache), _I32, _I32]
 _lib.ssu_init_state.restype = ctypes.c_int
-_lib.ssu_init_state.argtypes = [ctypes.POINTER(SsuCache), _P, _I64, _P, _I32, _P]
+_lib.ssu_init_state.argtypes = [ctypes.POINTER(SsuCache), _P, _I64, _P, _I32, ctypes.c_uint64, _P]
 _lib.ssu_replay_step.restype = ctypes.c_int
 _lib.ssu_replay_step.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep), _P]
 _lib.ssu_flush.restype = ctypes.c_int
-_lib.ssu_flush.argtypes = [ctypes.POINTER(SsuCache), _P, _P, _P, _I32, _P]
+_lib.ssu_flush.argtypes = [ctypes.POINTER(SsuCache), _P, _P, _P, _I32, ctypes.c_uint64, _P]
 _lib.ssu_resolve_algo.restype = ctypes.c_int
 _lib.ssu_resolve_algo.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep)]
 _lib.ssu_get_split_threshold.restype = _I64
@@ -115,16 +116,18 @@ def ssu_workspace_size(cache: SsuCache, batch: int, max_seqlen: int) -> int:
 
 
 def ssu_init_state(cache: SsuCache, states: int, states_batch_stride: int, slot_idx: int, n: int,
-                   stream: int = 0) -> int:
-    return _lib.ssu_init_state(ctypes.byref(cache), states, states_batch_stride, slot_idx, n, stream)
+                   sr_seed: int = 0, stream: int = 0) -> int:
+    return _lib.ssu_init_state(ctypes.byref(cache), states, states_batch_stride, slot_idx, n, sr_seed,
+                               stream)
 
 
 def ssu_replay_step(cache: SsuCache, step: SsuStep, stream: int = 0) -> int:
     return _lib.ssu_replay_step(ctypes.byref(cache), ctypes.byref(step), stream)
 
 
-def ssu_flush(cache: SsuCache, slot_idx: int, num_fold: int, A: int, n: int, stream: int = 0) -> int:
-    return _lib.ssu_flush(ctypes.byref(cache), slot_idx, num_fold, A, n, stream)
+def ssu_flush(cache: SsuCache, slot_idx: int, num_fold: int, A: int, n: int, sr_seed: int = 0,
+              stream: int = 0) -> int:
+    return _lib.ssu_flush(ctypes.byref(cache), slot_idx, num_fold, A, n, sr_seed, stream)
 
 
 def ssu_resolve_algo(cache: SsuCache, step: SsuStep) -> int:
@@ -176,6 +179,7 @@ class DeviceCache:
     status: object = None
     headdim: int = 64
     dstate: int = 128
+    recur: object = None  # FP16 recurrence checkpoint (separate checkpoints) or None
 
     def desc(self) -> SsuCache:
         fp8 = self.state_dtype == "fp8"
@@ -187,37 +191,38 @@ class DeviceCache:
             _ptr(self.x_cache), self.x_cache.stride(0),
             _ptr(self.B_cache), self.B_cache.stride(0),
             _ptr(self.dt_cache), self.dt_cache.stride(0),
-            _ptr(self.ring_start), _ptr(self.status))
+            _ptr(self.ring_start), _ptr(self.status),
+            _ptr(self.recur), 0 if self.recur is None else self.recur.stride(0))
 
 
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
                    out_dtype="bf16", workspace=None, algo="auto", num_fold=None, z=None,
-                   dt_softplus=True) -> SsuStep:
+                   dt_softplus=True, sr_seed=0) -> SsuStep:
     return SsuStep(
         batch, max_seqlen, _ptr(slot_idx), _ptr(pnat), _ptr(cu_seqlens),
         _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
         _ptr(out), SSU_F32 if out_dtype == "f32" else SSU_BF16,
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        ALGO_CODES[algo], _ptr(num_fold), _ptr(z), 0 if dt_softplus else 1)
+        ALGO_CODES[algo], _ptr(num_fold), _ptr(z), 0 if dt_softplus else 1, int(sr_seed))
 
 
 def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:
     return ssu_workspace_size(cache.desc(), batch, max_seqlen)
 
 
-def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, stream=None):
+def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, stream=None, sr_seed=0):
     """ssu_init_state with torch tensors (states f32 [n, H, 64, 128] on device)."""
     n = slot_idx.numel()
     if states_batch_stride is None:
         states_batch_stride = states.stride(0) if n else 0
     _check(ssu_init_state(cache.desc(), _ptr(states), states_batch_stride, _ptr(slot_idx), n,
-                          _stream(stream)))
+                          int(sr_seed), _stream(stream)))
 
 
 def replay_step(cache: DeviceCache, step: SsuStep, stream=None):
     _check(ssu_replay_step(cache.desc(), step, _stream(stream)))
 
 
-def flush(cache: DeviceCache, slot_idx, num_fold, A, stream=None):
-    _check(ssu_flush(cache.desc(), _ptr(slot_idx), _ptr(num_fold), _ptr(A), slot_idx.numel(),
+def flush(cache: DeviceCache, slot_idx, num_fold, A, stream=None, sr_seed=0):
+    _check(ssu_flush(cache.desc(), _ptr(slot_idx), _ptr(num_fold), _ptr(A), slot_idx.numel(), int(sr_seed),
                      _stream(stream)))

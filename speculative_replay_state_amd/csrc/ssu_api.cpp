@@ -78,6 +78,10 @@ int check_cache(const ssu_cache *c) {
     return fail(SSU_ERR_INVALID, "cache tensors must not be NULL");
   if (c->state_dtype == SSU_FP8_E4M3 && !c->state_scale)
     return fail(SSU_ERR_INVALID, "fp8 state requires state_scale");
+  if (c->recur_state && c->state_dtype != SSU_FP8_E4M3)
+    return fail(SSU_ERR_UNSUPPORTED, "recur_state (separate checkpoints) requires an fp8 state");
+  if (c->recur_state && !aligned16(c->recur_state))
+    return fail(SSU_ERR_INVALID, "recur_state must be 16-byte aligned");
   if (!aligned16(c->state) || !aligned16(c->x_cache) || !aligned16(c->B_cache) || !aligned16(c->dt_cache) ||
       (c->state_scale && !aligned16(c->state_scale)) || !aligned4(c->ring_start) ||
       (c->status && !aligned4(c->status)))
@@ -94,6 +98,7 @@ int check_cache(const ssu_cache *c) {
       {"x_cache", c->x_slot_stride, H * L * ssu::kHeadDim * 2, true},
       {"B_cache", c->B_slot_stride, G * L * ssu::kDState * 2, true},
       {"dt_cache", c->dt_slot_stride, H * L * 4, true},
+      {"recur_state", c->recur_slot_stride, H * ssu::kHeadDim * ssu::kDState * 2, c->recur_state != nullptr},
   };
   for (auto &t : s) {
     if (!t.used) continue;
@@ -107,7 +112,7 @@ int check_cache(const ssu_cache *c) {
   return SSU_OK;
 }
 
-ssu::KCache kcache(const ssu_cache *c) {
+ssu::KCache kcache(const ssu_cache *c, uint64_t seed) {
   ssu::KCache k;
   k.state = static_cast<uint8_t *>(c->state);
   k.state_stride = c->state_slot_stride;
@@ -126,6 +131,10 @@ ssu::KCache kcache(const ssu_cache *c) {
   k.G = c->ngroups;
   k.L = c->ring_len;
   k.hpg = c->nheads / c->ngroups;
+  k.recur = static_cast<uint8_t *>(c->recur_state);
+  k.recur_stride = c->recur_slot_stride;
+  k.seed_lo = (uint32_t)seed;
+  k.seed_hi = (uint32_t)(seed >> 32);
   return k;
 }
 
@@ -226,16 +235,16 @@ int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t st
                   step->workspace_bytes, step->workspace ? "" : ", NULL");
     if (!aligned16(step->workspace)) return fail(SSU_ERR_INVALID, "workspace must be 16-byte aligned");
     k.cb = static_cast<float *>(step->workspace);
-    err = ssu::launch_replay_split(kcache(cache), k, st, ot, stream);
+    err = ssu::launch_replay_split(kcache(cache, step->sr_seed), k, st, ot, stream);
   } else {
-    err = ssu::launch_replay_monolith(kcache(cache), k, st, ot, stream);
+    err = ssu::launch_replay_monolith(kcache(cache, step->sr_seed), k, st, ot, stream);
   }
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
 }
 
 int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
-              int32_t n, hipStream_t stream) {
+              int32_t n, uint64_t sr_seed, hipStream_t stream) {
   int rc = check_cache(cache);
   if (rc != SSU_OK) return rc;
   if (n < 0) return fail(SSU_ERR_INVALID, "n must be >= 0 (got %d)", n);
@@ -244,13 +253,13 @@ int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *nu
   if (!aligned4(slot_idx) || !aligned4(num_fold) || !aligned4(A))
     return fail(SSU_ERR_INVALID, "slot_idx, num_fold and A must be 4-byte aligned");
   hipError_t err =
-      ssu::launch_flush(kcache(cache), slot_idx, num_fold, A, n, state_type_of(cache->state_dtype), stream);
+      ssu::launch_flush(kcache(cache, sr_seed), slot_idx, num_fold, A, n, state_type_of(cache->state_dtype), stream);
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
 }
 
 int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
-                   const int32_t *slot_idx, int32_t n, hipStream_t stream) {
+                   const int32_t *slot_idx, int32_t n, uint64_t sr_seed, hipStream_t stream) {
   int rc = check_cache(cache);
   if (rc != SSU_OK) return rc;
   if (n < 0) return fail(SSU_ERR_INVALID, "n must be >= 0 (got %d)", n);
@@ -259,7 +268,7 @@ int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_b
   if (states_batch_stride < 0) return fail(SSU_ERR_INVALID, "states_batch_stride must be >= 0");
   if (!aligned16(states) || states_batch_stride % 4 != 0 || !aligned4(slot_idx))
     return fail(SSU_ERR_INVALID, "states must be 16-byte aligned with a stride that is a multiple of 4");
-  hipError_t err = ssu::launch_init(kcache(cache), states, states_batch_stride, slot_idx, n,
+  hipError_t err = ssu::launch_init(kcache(cache, sr_seed), states, states_batch_stride, slot_idx, n,
                                     state_type_of(cache->state_dtype), stream);
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();

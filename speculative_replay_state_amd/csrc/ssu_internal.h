@@ -36,6 +36,9 @@ struct KCache {
   int32_t *ring_start;
   int32_t *status;
   int num_slots, H, G, L, hpg;
+  uint8_t *recur;        // NULL, or the FP16 recurrence checkpoint (separate checkpoints)
+  int64_t recur_stride;
+  uint32_t seed_lo, seed_hi;  // this call's stochastic-rounding seed
 };
 
 // One replay step.

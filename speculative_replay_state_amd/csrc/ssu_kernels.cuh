@@ -575,6 +575,61 @@ __device__ __forceinline__ void store_chunks(uint8_t *hp, int rb, int lane, cons
   for (int u = 0; u < 2 * kEB; ++u) st16_nt(hp + tile_chunk(rb, u, lane, kEB), ch[u]);
 }
 
+// ---------------------------------------------------------------------------
+// Stochastic rounding for the FP16 recurrence checkpoint.  Each value of a
+// (slot, head) takes 7 random bits: Philox4x32-10 (Salmon, Moraes, Dror and
+// Shaw, SC 2011) with counter (value / 16, head, slot, 0) and the call's
+// 64-bit seed as key gives 16 bytes, and value index e uses the low 7 bits of
+// byte e % 16 (little-endian within each 32-bit word).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 ctr, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * ctr[0], p1 = (uint64_t)0xCD9E8D57u * ctr[2];
+    ctr = u32x4{(uint32_t)(p1 >> 32) ^ ctr[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ ctr[3] ^ k1,
+                (uint32_t)p0};
+  }
+  return ctr;
+}
+
+// Stochastic rounding fp32 -> fp16 with 7 random bits u: keep the top 7 bits
+// of the fraction fp16 discards, add u, round away from zero on a carry.
+// gfx950's v_cvt_sr_f16_f32 adds the top 13 bits of its random word to the
+// top 13 discarded bits (also in the fp16 subnormal range, and carrying to
+// infinity past 65504); the word u << 25 puts 64 u there, and a carry of
+// R13 + 64 u out of 13 bits is exactly one of floor(R13 / 64) + u out of 7.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t sr_f16_pair(float v0, uint32_t r0, float v1, uint32_t r1) {
+  f16x2_t o = {0, 0};
+  o = __builtin_amdgcn_cvt_sr_f16_f32(o, v0, r0, false);
+  o = __builtin_amdgcn_cvt_sr_f16_f32(o, v1, r1, true);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+// The recurrence checkpoint chunks (fp16) of a quarter row, stochastically
+// rounded: row p of (slot, head), quarter q.  Value n = 32 q + t takes byte
+// t % 16 of Philox call t / 16 (counter p * 8 + 2 q + t / 16).
+__device__ __forceinline__ void encode_quarter_sr(const f32x4 *acc, const KCache &c, int slot, int head, int p,
+                                                  int q, u32x4 *ch) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const u32x4 r = philox4x32_10(u32x4{(uint32_t)(p * 8 + 2 * q + w), (uint32_t)head, (uint32_t)slot, 0u},
+                                  c.seed_lo, c.seed_hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // values 16 w + 2 i, 16 w + 2 i + 1: bytes 2 i, 2 i + 1
+      const uint32_t word = r[i >> 1], sh = 16 * (i & 1);
+      const uint32_t r0 = (word >> sh) << 25, r1 = (word >> (sh + 8)) << 25;
+      ch[2 * w + (i >> 2)][i & 3] = sr_f16_pair(QV(acc, 16 * w + 2 * i), r0, QV(acc, 16 * w + 2 * i + 1), r1);
+    }
+  }
+}
+
 // Decodes one lane's chunks of a row block into the quarter-row layout,
 // times f.
 template <int ST>
@@ -741,6 +796,37 @@ __device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const 
     fast = __all(scale_fast(sc));
   }
   encode_quarter<ST>(acc, sc, y, fast, ch);
+  return sc;
+}
+
+// The same with separate checkpoints: decode the FP16 recurrence chunks rch,
+// fold, write the read checkpoint chunks ch (nearest encoding in ST) and the
+// new recurrence chunks into rch (stochastic rounding).
+template <int ST, int KW>
+__device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb,
+                                                   int lane, const KCache &c, int slot, int head, u32x4 *rch,
+                                                   u32x4 *ch) {
+  using WC = Win<KW>;
+  using V = typename WC::V;
+  const int m = lane & 15, q = lane >> 4;
+  f32x4 acc[8];
+  decode_quarter<kF16>(rch, fo.D0, acc);
+  const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    acc[nb] = mfma_win<KW>(fo.ahi[nb], xb, acc[nb]);
+    acc[nb] = mfma_win<KW>(fo.alo[nb], xb, acc[nb]);
+    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.alo2[nb], xb, acc[nb]);
+  }
+  float sc = 1.f, y = 1.f;
+  bool fast = true;
+  if constexpr (ST == kFP8) {
+    sc = fp8_row_scale(quarter_row_max(acc));
+    y = 1.0f / sc;
+    fast = __all(scale_fast(sc));
+  }
+  encode_quarter<ST>(acc, sc, y, fast, ch);
+  encode_quarter_sr(acc, c, slot, head, 16 * rb + m, q, rch);
   return sc;
 }
 
@@ -1099,8 +1185,8 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
   }
 }
 
-template <int ST, int KW>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : (KW == 32 ? 2 : 3))))
+template <int ST, int KW, bool SEP>
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
 void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
@@ -1130,8 +1216,15 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 
   // 1. loads, issued before any arithmetic (fp32: the checkpoint per row
   //    block, below)
-  u32x4 raw[ST == kF32 ? 1 : 4][kNLD];
-  if constexpr (ST != kF32) {
+  u32x4 raw[(ST == kF32 || SEP) ? 1 : 4][kNLD];
+  u32x4 rraw[SEP ? 4 : 1][4];  // separate checkpoints: the FP16 recurrence tile
+  uint8_t *rp = SEP ? c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2) : nullptr;
+  if constexpr (SEP) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rraw[rb][u] = ld16_nt(rp + tile_chunk(rb, u, lane, 2));
+  } else if constexpr (ST != kF32) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -1152,14 +1245,19 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     u32x4 ch[kNLD];
+    if constexpr (SEP) {
+      scs[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, slot, h, rraw[rb], ch);
+      store_chunks<kF16>(rp, rb, lane, rraw[rb]);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kNLD; ++u) {
-      if constexpr (ST == kF32)
-        ch[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
-      else
-        ch[u] = raw[rb][u];
+      for (int u = 0; u < kNLD; ++u) {
+        if constexpr (ST == kF32)
+          ch[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
+        else
+          ch[u] = raw[rb][u];
+      }
+      scs[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ch);
     }
-    scs[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ch);
     store_chunks<ST>(hp, rb, lane, ch);
   }
   // new row scales: lane l holds row l's (row 16 q + m is in rb = q)
@@ -1183,8 +1281,8 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // appends the group's B rows.
 // ---------------------------------------------------------------------------
 
-template <int ST, int OT, int KW, bool HAS_Z>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : (KW == 32 ? 2 : 3))))
+template <int ST, int OT, int KW, bool HAS_Z, bool SEP>
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
 void fused_kernel(KCache c, KStep s, int htiles) {
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
   __shared__ float cbw_all[kHeadWaves][kMaxTokens * kCbLds];
@@ -1199,11 +1297,27 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   float *cbw = cbw_all[wave];
 
   // 1. the checkpoint as soon as the slot is known (in bounds for any valid
-  //    slot; discarded if the entry turns out to be skipped)
+  //    slot; discarded if the entry turns out to be skipped).  Separate
+  //    checkpoints: an entry that asks for a fold reads the FP16 recurrence
+  //    tile (the fold writes the read tile from it), any other the read tile.
+  //    A replayed entry folds exactly the k it asks for, so the choice holds.
   HeadLoads<ST, KW> ld;
+  u32x4 rraw[SEP ? 4 : 1][4];
   {
     const int slot = s.slot_idx[b];
-    if (slot > 0 && slot < c.num_slots) load_state<ST, KW>(c, slot, h, lane, ld);
+    if (slot > 0 && slot < c.num_slots) {
+      bool recur_tile = false;
+      if constexpr (SEP) recur_tile = s.fold[b] > 0;
+      if (recur_tile) {
+        const uint8_t *rp = c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rraw[rb][u] = ld16_nt(rp + tile_chunk(rb, u, lane, 2));
+      } else {
+        load_state<ST, KW>(c, slot, h, lane, ld);
+      }
+    }
   }
   const Entry e = load_entry(c, s, b, h == 0);
   if (e.mode == 0) return;
@@ -1224,7 +1338,12 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, lane, fo);
     wave_sync();  // xT written by this wave -> read below
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+    for (int rb = 0; rb < 4; ++rb) {
+      if constexpr (SEP)
+        fl.osc[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, e.slot, h, rraw[rb], ld.raw[rb]);
+      else
+        fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+    }
     wave_sync();  // the fold's xT reads done before the readout rewrites xT
   }
 
@@ -1240,6 +1359,11 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) store_chunks<ST>(hp, rb, lane, ld.raw[rb]);
+    if constexpr (SEP) {
+      uint8_t *rp = c.recur + (int64_t)e.slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) store_chunks<kF16>(rp, rb, lane, rraw[rb]);
+    }
     if constexpr (ST == kFP8)  // lane l holds row l's new scale (row 16 q + m is in rb = q)
       (reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(fl.osc[0], fl.osc[1], fl.osc[2], fl.osc[3], q);
   }
@@ -1324,6 +1448,14 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
   u32x4 ch[2 * kEB];
   encode_quarter<ST>(acc, sc, y, fast, ch);
   store_chunks<ST>(hp, rb, lane, ch);
+  if constexpr (ST == kFP8) {
+    if (c.recur) {  // separate checkpoints: the FP16 recurrence one, stochastically rounded
+      u32x4 rch[4];
+      encode_quarter_sr(acc, c, slot, h, 16 * rb + m, q, rch);
+      store_chunks<kF16>(c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2), rb, lane,
+                         rch);
+    }
+  }
 }
 
 __device__ __forceinline__ void zero_bytes(uint8_t *p, int64_t nbytes, int tid, int nthreads) {
@@ -1389,18 +1521,28 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int ST, int OT, bool HAS_Z>
-hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
+template <int ST, int OT, bool HAS_Z, bool SEP>
+hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
   const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kHeadWaves * 64);
   if (c.L <= 16)
-    fused_kernel<ST, OT, 16, HAS_Z><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 16, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles);
   else
-    fused_kernel<ST, OT, 32, HAS_Z><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 32, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   step_ring_advance_kernel<ST><<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
   return hipGetLastError();
+}
+
+// Separate checkpoints exist for the fp8 read checkpoint only (the API
+// rejects recur_state with any other state type).
+template <int ST, int OT, bool HAS_Z>
+hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
+  if constexpr (ST == kFP8) {
+    if (c.recur) return fused_zs<ST, OT, HAS_Z, true>(c, s, st);
+  }
+  return fused_zs<ST, OT, HAS_Z, false>(c, s, st);
 }
 
 template <int ST, int OT, bool SPLIT, bool HAS_Z>
@@ -1426,10 +1568,21 @@ hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_
                    int n, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
   const dim3 grid((unsigned)((int64_t)n * htiles)), block(kHeadWaves * 64);
-  if (c.L <= 16)
-    flush_kernel<ST, 16><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
-  else
-    flush_kernel<ST, 32><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+  bool sep = false;
+  if constexpr (ST == kFP8) sep = c.recur != nullptr;
+  if (sep) {
+    if constexpr (ST == kFP8) {
+      if (c.L <= 16)
+        flush_kernel<ST, 16, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+      else
+        flush_kernel<ST, 32, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+    }
+  } else {
+    if (c.L <= 16)
+      flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+    else
+      flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   ring_advance_kernel<ST><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);

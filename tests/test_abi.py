@@ -88,8 +88,8 @@ def test_cache_validation(ssu, kw, code, msg):
     c = _cache(ssu, **kw)
     assert ssu.ssu_replay_step(c, _step(ssu)) == code
     assert msg in ssu.ssu_last_error()
-    assert ssu.ssu_flush(c, FAKE, FAKE, FAKE, 3) == code
-    assert ssu.ssu_init_state(c, FAKE, 0, FAKE, 3) == code
+    assert ssu.ssu_flush(c, FAKE, FAKE, FAKE, 3, 1) == code
+    assert ssu.ssu_init_state(c, FAKE, 0, FAKE, 3, 1) == code
     assert ssu.ssu_workspace_size(c, 4, 4) == 0
 
 
