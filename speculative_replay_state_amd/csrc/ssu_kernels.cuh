@@ -258,13 +258,36 @@ __device__ __forceinline__ f32x4 mfma_win(typename Win<KW>::V a, typename Win<KW
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Inclusive prefix sum over lanes 0..KW-1 (Hillis-Steele).
+// Cross-lane moves.  lane_get: the value of lane src (any lane, one LDS
+// permute); lane_get_uniform: the value of lane src for a wave-uniform src
+// (a scalar read); lane_xor: the value of lane ^ mask.
+__device__ __forceinline__ float lane_get(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ float lane_get_uniform(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ float lane_xor(float v, int lane, int mask) {
+  return lane_get(v, lane ^ mask);
+}
+
+// Inclusive prefix sum over lanes 0..KW-1: a Hillis-Steele scan inside each
+// row of 16 lanes (row shifts, lanes past the row start add zero), then for
+// KW = 32 the second row adds the first row's total.
+template <int D>
+__device__ __forceinline__ float row_shr(float v) {  // v of lane - D within the row, 0 past its start
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + D, 0xF, 0xF, true));
+}
+
 template <int KW>
 __device__ __forceinline__ float scan_win(float v, int lane) {
-#pragma unroll
-  for (int d = 1; d < KW; d <<= 1) {
-    const float t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  if constexpr (KW == 32) {
+    const float r0 = lane_get_uniform(v, 15);
+    if (lane >= 16 && lane < 32) v += r0;
   }
   return v;
 }
@@ -518,16 +541,25 @@ __device__ __forceinline__ bool scale_fast(float sc) { return sc >= 0x1p-60f && 
 
 // Max |v| over a lane's quarter row, then over the four lanes (q = 0..3) that
 // hold the same row.
+// max(m, |x|, |y|): the NaN-propagating maximum lowers to gfx950's
+// v_maximum3_f32 with the absolute values as source modifiers; fmaxf would
+// first quiet each input (one more instruction per value, as the kernels run
+// in IEEE mode).  A NaN in a row makes its scale NaN (the row is NaN anyway).
+__device__ __forceinline__ float max3_abs(float m, float x, float y) {
+  return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(fabsf(x), fabsf(y)));
+}
+
 __device__ __forceinline__ float quarter_row_max(const f32x4 *acc) {
   float a = 0.f, b = 0.f;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    a = fmaxf(a, fmaxf(fabsf(acc[nb][0]), fabsf(acc[nb][1])));
-    b = fmaxf(b, fmaxf(fabsf(acc[nb][2]), fabsf(acc[nb][3])));
+    a = max3_abs(a, acc[nb][0], acc[nb][1]);
+    b = max3_abs(b, acc[nb][2], acc[nb][3]);
   }
   float mx = fmaxf(a, b);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const int lane = __lane_id();
+  mx = fmaxf(mx, lane_xor(mx, lane, 16));
+  return fmaxf(mx, lane_xor(mx, lane, 32));
 }
 
 // Encodes a quarter row into the lane's 16-byte chunks of a row block
@@ -724,12 +756,15 @@ __device__ __forceinline__ void load_fold_B(const KCache &c, int slot, int g, in
   }
 }
 
-// The fold's operands: A operands of the 8 tiles, ahi[nb][e] + alo[nb][e]
-// (+ alo2) = coef_s B_s[32 (m / 4) + 8 (m % 4) + nb] for s = kE q + e, and the
-// checkpoint decay D0.
+// The fold's operands: A operands of the 8 tiles, ab[nb][e] =
+// B_s[32 (m / 4) + 8 (m % 4) + nb] for s = kE q + e (bf16, exact), the
+// coefficients cf[e] = coef_s of those positions, and the checkpoint decay D0.
+// The coefficients go into the B operand (coef_s x_s[p], split into bf16
+// parts per row block), which has half as many values per lane as the A side.
 template <int ST, int KW>
 struct FoldOps {
-  typename Win<KW>::V ahi[8], alo[8], alo2[ST == kF32 ? 8 : 1];
+  typename Win<KW>::V ab[8];
+  float cf[Win<KW>::kE];
   float D0;
 };
 
@@ -743,7 +778,7 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
   constexpr int kE = WC::kE;
   const int q = lane >> 4;
   const float cum = scan_win<KW>(Ah * fl.dtp, lane);
-  const float ctot = __shfl(cum, k - 1, 64);
+  const float ctot = lane_get_uniform(cum, k - 1);
   const float coef = lane < k ? expf(ctot - cum) * fl.dtp : 0.f;
   fo.D0 = expf(ctot);
 #pragma unroll
@@ -756,17 +791,40 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
   }
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
-    const float cf = __shfl(coef, kE * q + e, 64);
+    fo.cf[e] = lane_get(coef, kE * q + e);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const float w = cf * bf2f((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu));
-      const __bf16 hi = (__bf16)w;
-      const float r1 = w - (float)hi;
-      const __bf16 lo = (__bf16)r1;
-      fo.ahi[nb][e] = hi;
-      fo.alo[nb][e] = lo;
-      if constexpr (ST == kF32) fo.alo2[nb][e] = (__bf16)(r1 - (float)lo);
-    }
+    for (int nb = 0; nb < 8; ++nb)
+      fo.ab[nb][e] = __builtin_bit_cast(
+          __bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
+  }
+}
+
+// The rank-k update of row block rb into the lane's quarter row:
+// acc[nb] += sum_s B_s[n] (coef_s x_s[p]) for p = 16 rb + m, with coef_s x_s[p]
+// split into bf16 hi + lo (+ lo2 for fp32 state).
+template <int ST, int KW>
+__device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb, int lane,
+                                            f32x4 *acc) {
+  using WC = Win<KW>;
+  using V = typename WC::V;
+  const int m = lane & 15, q = lane >> 4;
+  const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
+  V bhi, blo, blo2;
+#pragma unroll
+  for (int e = 0; e < WC::kE; ++e) {
+    const float w = fo.cf[e] * (float)xb[e];
+    const __bf16 hi = (__bf16)w;
+    const float r1 = w - (float)hi;
+    const __bf16 lo = (__bf16)r1;
+    bhi[e] = hi;
+    blo[e] = lo;
+    if constexpr (ST == kF32) blo2[e] = (__bf16)(r1 - (float)lo);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    acc[nb] = mfma_win<KW>(fo.ab[nb], bhi, acc[nb]);
+    acc[nb] = mfma_win<KW>(fo.ab[nb], blo, acc[nb]);
+    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.ab[nb], blo2, acc[nb]);
   }
 }
 
@@ -776,18 +834,9 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
 template <int ST, int KW>
 __device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb, int lane,
                                                float old_scale, u32x4 *ch) {
-  using WC = Win<KW>;
-  using V = typename WC::V;
-  const int m = lane & 15, q = lane >> 4;
   f32x4 acc[8];
   decode_quarter<ST>(ch, ST == kFP8 ? fo.D0 * old_scale : fo.D0, acc);
-  const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    acc[nb] = mfma_win<KW>(fo.ahi[nb], xb, acc[nb]);
-    acc[nb] = mfma_win<KW>(fo.alo[nb], xb, acc[nb]);
-    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.alo2[nb], xb, acc[nb]);
-  }
+  fold_update<ST, KW>(fo, xT, rb, lane, acc);
   float sc = 1.f, y = 1.f;
   bool fast = true;
   if constexpr (ST == kFP8) {
@@ -806,18 +855,10 @@ template <int ST, int KW>
 __device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb,
                                                    int lane, const KCache &c, int slot, int head, u32x4 *rch,
                                                    u32x4 *ch) {
-  using WC = Win<KW>;
-  using V = typename WC::V;
   const int m = lane & 15, q = lane >> 4;
   f32x4 acc[8];
   decode_quarter<kF16>(rch, fo.D0, acc);
-  const V xb = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    acc[nb] = mfma_win<KW>(fo.ahi[nb], xb, acc[nb]);
-    acc[nb] = mfma_win<KW>(fo.alo[nb], xb, acc[nb]);
-    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.alo2[nb], xb, acc[nb]);
-  }
+  fold_update<ST, KW>(fo, xT, rb, lane, acc);
   float sc = 1.f, y = 1.f;
   bool fast = true;
   if constexpr (ST == kFP8) {
@@ -1005,15 +1046,15 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   //    MFMA, split into bf16 hi + lo (+ lo2 for fp32 state) parts), and the
   //    checkpoint decay beta_i = exp(cumA_{pnat+i}).
   const int ti = e.pnat + m;
-  const float ct = __shfl(cum, ti < KW ? ti : KW - 1, 64);
+  const float ct = lane_get(cum, ti < KW ? ti : KW - 1);
   const float beta = tok_ok ? expf(ct) : 0.f;
   const float Dh = ld.Dh;
   V whi, wlo, wlo2;
 #pragma unroll
   for (int tt = 0; tt < WC::kE; ++tt) {
     const int sig = WC::kE * q + tt;
-    const float cs = __shfl(cum, sig, 64);
-    const float ds = __shfl(dtp, sig, 64);
+    const float cs = lane_get(cum, sig);
+    const float ds = lane_get(dtp, sig);
     const float cbv = il.cbr[tt >> 2][tt & 3];
     float w = 0.f;
     if (tok_ok && sig <= ti) w = expf(ct - cs) * ds * cbv;
@@ -1371,7 +1412,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ld.rscale[rb][j] = __shfl(fl.osc[rb], 4 * q + j, 64);  // row 16 rb + 4 q + j
+      for (int j = 0; j < 4; ++j) ld.rscale[rb][j] = lane_get(fl.osc[rb], 4 * q + j);  // row 16 rb + 4 q + j
   }
 
   // 4. C.B of the group, then the replay of the head from the (new) tile

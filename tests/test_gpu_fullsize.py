@@ -91,6 +91,7 @@ def test_full_size_sampled(name, algo):
     else:
         ref, status = O.replay_step(ref_cache, sub)
         if algo == "separate":
+            mid = ref_cache.copy()  # the state the flush folds from (the step leaves checkpoints alone)
             assert O.flush(ref_cache, sub.slot_idx, ks, sub.A) == 0
     assert status == 0
 
@@ -115,4 +116,5 @@ def test_full_size_sampled(name, algo):
     r = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
     assert gh.rel_err(g, r) <= 1e-6
     touched = [i + 1 for i, b in enumerate(sample) if k is not None and k[b] > 0]
-    gh.check_state(after.spec, after, ref_cache, before, touched)
+    fold = None if ks is None else (sub.slot_idx, ks, sub.A)
+    gh.check_state(after.spec, after, ref_cache, mid if algo == "separate" else before, touched, fold)

@@ -72,7 +72,7 @@ def test_fused_step_parity(case):
     rd = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
     assert gh.rel_err(gd, rd) <= 1e-6
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
-    gh.check_state(spec, gpu, ref_cache, cache, touched)
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -139,4 +139,5 @@ def test_fused_invalid_fold_is_skipped_and_reported():
         assert np.array_equal(gpu.state[s], cache.state[s])
         assert np.array_equal(gpu.x_cache[s], cache.x_cache[s])
     touched = sorted({int(step.slot_idx[b]) for b in (0, 4, 5)})
-    gh.check_state(spec, gpu, ref_cache, cache, touched)
+    k_valid = np.where((k >= 0) & (k <= step.pnat), k, 0).astype(np.int32)
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k_valid, step.A))

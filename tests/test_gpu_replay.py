@@ -148,13 +148,7 @@ def test_flush_parity(state_dtype):
     nb = spec.state_bytes()
     assert np.array_equal(gpu.state[:, nb:], before_flush.state[:, nb:])  # canaries
     if state_dtype == "fp8":
-        g = np.stack([gpu.state_view(s) for s in touched])
-        r = np.stack([ref.state_view(s) for s in touched])
-        frac, dist = gh.fp8_code_agreement(g, r)
-        assert frac >= 0.999 and dist <= 1, (frac, dist)
-        gs = np.stack([gpu.scale_view(s) for s in touched]).astype(np.float64)
-        rs = np.stack([ref.scale_view(s) for s in touched]).astype(np.float64)
-        assert np.max(np.abs(gs - rs) / rs) <= 1e-5
+        gh.check_state(spec, gpu, ref, before_flush, touched, (step.slot_idx, k, step.A))
     else:
         g = np.stack([O.decode_state(gpu, s) for s in touched])
         r = np.stack([O.decode_state(ref, s) for s in touched])

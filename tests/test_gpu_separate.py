@@ -54,26 +54,6 @@ def f16_agreement(got, ref):
     return float((og == orf).mean()), int(np.max(np.abs(og - orf))) if og.size else 0
 
 
-def _f64_fold(spec, before, slots, k, A, absolute):
-    """Exact (fp64) fold of the FP16 recurrence values of `before`, or of
-    their absolute values with |x| and |B| rings: [slot] -> [H, P, N]."""
-    s64 = synth.CacheSpec(**{**spec.__dict__, "state_dtype": "f64", "state_layout": "rowmajor",
-                             "separate": False})
-    x, B = before.x_cache.copy(), before.B_cache.copy()
-    if absolute:
-        x.view(np.uint16)[...] &= 0x7FFF
-        B.view(np.uint16)[...] &= 0x7FFF
-    c = synth.CacheArrays(s64, np.zeros((spec.num_slots, s64.strides()["state"]), np.uint8),
-                          np.zeros((spec.num_slots, s64.strides()["scale"]), np.uint8), x, B,
-                          before.dt_cache.copy(), before.ring_start.copy())
-    touched = sorted({int(sl) for sl, kk in zip(slots, k) if kk > 0 and 0 < sl < spec.num_slots})
-    for sl in touched:
-        h = O.decode_recur(before, sl)
-        c.set_state_logical(sl, np.abs(h) if absolute else h)
-    assert O.flush(c, slots, k, A) == 0
-    return {sl: c.state_logical(sl) for sl in touched}
-
-
 def _check_recur(spec, gpu, before, slots, k, A, seed, min_equal=0.98):
     """Recurrence checkpoints after a fold of k tokens from `before`:
     untouched slots and slot padding bit for bit, folded ones bracketed by
@@ -85,14 +65,14 @@ def _check_recur(spec, gpu, before, slots, k, A, seed, min_equal=0.98):
     assert np.array_equal(gpu.recur[:, nb:], before.recur[:, nb:])  # slot padding
     if not touched:
         return
-    v_ref = _f64_fold(spec, before, slots, k, A, absolute=False)
-    s_abs = _f64_fold(spec, before, slots, k, A, absolute=True)
+    v_ref = gh.f64_fold(spec, before, slots, k, A, absolute=False)
+    s_abs = gh.f64_fold(spec, before, slots, k, A, absolute=True)
     P, N = spec.headdim, spec.dstate
     equal = total = 0
     for sl in touched:
         u = np.stack([O.sr_bits(seed, sl, h, P * N).reshape(P, N) for h in range(spec.nheads)])
         v, S = v_ref[sl], s_abs[sl]
-        E = 2.0 ** -15 * S + 2.0 ** -23 * np.abs(v)
+        E = gh.FOLD_REL * S + 2.0 ** -23 * np.abs(v)
         lo = _f16_ordinal(O.sr_f16(v - E, u))
         hi = _f16_ordinal(O.sr_f16(v + E, u))
         g = _f16_ordinal(gpu.recur_logical(sl))
@@ -186,7 +166,7 @@ def test_separate_flush_parity(name):
     gpu = sd.download_cache(spec, t)
     assert np.array_equal(gpu.ring_start, ref.ring_start)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0})
-    gh.check_state(spec, gpu, ref, before, touched)
+    gh.check_state(spec, gpu, ref, before, touched, (step.slot_idx, k, step.A))
     _check_recur(spec, gpu, before, step.slot_idx, k, step.A, seed)
 
 
@@ -227,7 +207,7 @@ def test_separate_fused_step_parity(name, with_z):
     assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
-    gh.check_state(spec, gpu, ref_cache, cache, touched)
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
     _check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
 
 
@@ -315,7 +295,7 @@ def test_separate_fold_cycles():
         ssu.replay_step(dc, desc)
         torch.cuda.synchronize()
         assert int(dc.status.item()) == 0
-        s_abs = _f64_fold(spec, ref, slots, k, step.A, absolute=True)
+        s_abs = gh.f64_fold(spec, ref, slots, k, step.A, absolute=True)
         O.replay_step(ref, step, num_fold=k, seed=seed)
         gpu = sd.download_cache(spec, t)
         assert np.array_equal(gpu.ring_start, ref.ring_start)
@@ -324,7 +304,7 @@ def test_separate_fold_cycles():
             g, r = O.decode_recur(gpu, sl), O.decode_recur(ref, sl)
             prev = bound.get(sl, 0.0)
             if sl in s_abs:
-                bound[sl] = prev + 2 * _ulp16(r) + 2.0 ** -15 * s_abs[sl]
+                bound[sl] = prev + 2 * _ulp16(r) + gh.FOLD_REL * s_abs[sl]
             over = np.abs(g - r) - bound.get(sl, 0.0)
             assert np.all(over <= 0), (cycle, sl, float(np.max(over)))
             equal += int((g == r).sum())

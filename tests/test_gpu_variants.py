@@ -97,4 +97,4 @@ def test_variants_with_fused_flush(case):
     assert np.all(np.abs(got - ref) <= gh.tol_for(spec.state_dtype, out_dtype) * (1 + np.abs(ref)) + extra + 1e-12)
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
-    gh.check_state(spec, gpu, ref_cache, cache, touched)
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
