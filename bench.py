@@ -319,6 +319,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # --- what plain streams reach on this GPU (context for the roofline) ----
+    streams = hbm_streams(dev)
+
     # --- CPU oracle on a bounded sample of the same workload ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -364,9 +367,34 @@ def main():
                         if batch == wl_batch else None),
         },
         "kernels": kernels,
+        "hbm_stream": dict(streams, frac_of_copy=achieved / streams["copy_GBps"]),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def hbm_streams(dev, nbytes=2 ** 30, reps=5):
+    """GB/s of plain PyTorch streams over 1 GiB buffers on this GPU: a device
+    copy (half reads, half writes, like a read-modify-write of the
+    checkpoint) and a fill (writes).  Best of `reps`."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ops = {"copy_GBps": (lambda: dst.copy_(src), 2 * nbytes), "write_GBps": (lambda: dst.fill_(2.0), nbytes)}
+    out = {}
+    for name, (fn, moved) in ops.items():
+        fn()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        out[name] = moved / (best * 1e6)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused):

@@ -48,6 +48,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
+#ifndef SSU_FUSED_WPE
+#define SSU_FUSED_WPE(ST, KW, SEP) (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))
+#endif
 constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
 constexpr int kCbLds = 36;       // LDS row stride (fp32) of C.B in the monolith
@@ -1323,19 +1326,21 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // ---------------------------------------------------------------------------
 
 template <int ST, int OT, int KW, bool HAS_Z, bool SEP>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(SSU_FUSED_WPE(ST, KW, SEP))))
 void fused_kernel(KCache c, KStep s, int htiles) {
-  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
-  __shared__ float cbw_all[kHeadWaves][kMaxTokens * kCbLds];
-  __shared__ __align__(16) uint32_t ot_all[kHeadWaves][kOutTile];
+  // LDS per wave: the transposed x window and the C.B table, and later (once
+  // both have been read) the output staging tile in the same words.
+  constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
+  constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
+  __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
   constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.x / htiles;
   const int h = (blockIdx.x - b * htiles) * kHeadWaves + wave;
   if (h >= c.H) return;
   const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
-  uint16_t *xT = xT_all[wave];
-  float *cbw = cbw_all[wave];
+  uint16_t *xT = reinterpret_cast<uint16_t *>(lds_all[wave]);
+  float *cbw = reinterpret_cast<float *>(lds_all[wave] + kXTWords);
 
   // 1. the checkpoint as soon as the slot is known (in bounds for any valid
   //    slot; discarded if the entry turns out to be skipped).  Separate
@@ -1427,7 +1432,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     wave_sync();
     load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   }
-  head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, ot_all[wave], lane);
+  head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, lds_all[wave], lane);
 }
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
