@@ -56,6 +56,12 @@
  *    checkpoint; init writes both from the FP32 prefill states.  "SR7" is
  *    read as stochastic rounding with 7 random bits per value (or_sr_f16),
  *    the bits coming from Philox4x32-10 keyed by a per-call 64-bit seed.
+ *  - NVFP4 read checkpoint (same PR, Claims: FP8/NVFP4 read checkpoints with
+ *    nearest encoding; the API page's init computes a maximum over a group's
+ *    heads and a second-level scale max / (6 * 448)): e2m1 elements, an e4m3
+ *    scale per block of 16 along dstate, and an fp32 second-level scale; the
+ *    second-level scale is taken per (slot, head) here (encode_head_nvfp4),
+ *    the unit one fold rewrites, so every flush re-derives it exactly.
  *  - A padding entry (slot <= 0 or slot >= num_slots) writes zero output rows
  *    and touches no cache.  An entry with pnat < 0 or pnat + T_b > L is
  *    treated the same way and raises status bit 1; a flush entry with k < 0
@@ -83,7 +89,7 @@
 #include <string.h>
 #include <omp.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_FP8 = 3, OR_F64 = 4 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_FP8 = 3, OR_F64 = 4, OR_NVFP4 = 5 };
 
 /* ---------------------------------------------------------------------- */
 /* Number formats, written from their definitions.                         */
@@ -125,6 +131,15 @@ double or_e4m3_value(uint8_t code) {
   return s ? -v : v;
 }
 
+double or_e2m1_value(uint8_t code) {
+  /* OCP MX FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit, no
+   * infinities or NaN; exponent 0 is subnormal (0 or 0.5), the largest
+   * magnitude is 1.5 * 2^2 = 6. */
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
 /* Round to nearest, ties to even, by searching the sorted table of the
  * format's non-negative representable values.  `table[i]` is the value of
  * code i (codes 0..n-1 increase with value).  Returns the code of the
@@ -147,6 +162,7 @@ static int nearest_code(const double *table, int n, double a) {
 }
 
 static double g_e4m3_tab[127];   /* codes 0x00..0x7E */
+static double g_e2m1_tab[8];     /* codes 0..7 */
 static double g_f16_tab[0x7C01]; /* codes 0x0000..0x7C00, 0x7C00 = 2^16 */
 static double *g_bf16_tab;       /* codes 0x0000..0x7F80, 0x7F80 = 2^128 */
 static int g_tabs_ready = 0;
@@ -154,6 +170,7 @@ static int g_tabs_ready = 0;
 static void build_tables(void) {
   if (g_tabs_ready) return;
   for (int c = 0; c < 127; ++c) g_e4m3_tab[c] = or_e4m3_value((uint8_t)c);
+  for (int c = 0; c < 8; ++c) g_e2m1_tab[c] = or_e2m1_value((uint8_t)c);
   /* For IEEE rounding the first code past the largest finite value stands
    * for the next power of two: a value at least halfway to it rounds to
    * infinity, and infinity's code is even, as IEEE ties-to-even requires. */
@@ -195,6 +212,16 @@ uint8_t or_enc_e4m3_sat(double v) {
   double a = fabs(v);
   if (a > 448.0) a = 448.0;
   return s | (uint8_t)nearest_code(g_e4m3_tab, 127, a);
+}
+
+/* Saturating e2m1 encoder: nearest, ties to the even code, magnitudes past 6
+ * give 6; the sign is kept (a negative value that rounds to zero gives the
+ * negative zero code 0x8).  NaN -> 0x7. */
+uint8_t or_enc_e2m1_sat(double v) {
+  build_tables();
+  if (isnan(v)) return 0x7;
+  uint8_t s = signbit(v) ? 0x8 : 0;
+  return s | (uint8_t)nearest_code(g_e2m1_tab, 8, fabs(v));
 }
 
 double or_softplus(double v) { return v > 20.0 ? v : log1p(exp(v)); }
@@ -296,6 +323,9 @@ typedef struct {
    * state, element type fp16) or NULL when the state is the only checkpoint. */
   uint8_t *recur;
   int64_t recur_stride;
+  /* NVFP4 state only: the per-(slot, head) second-level scale, f32. */
+  uint8_t *gscale;
+  int64_t gscale_stride;
 } or_cache;
 
 static int state_elem_bytes(int dt) {
@@ -304,8 +334,51 @@ static int state_elem_bytes(int dt) {
   case OR_BF16: return 2;
   case OR_F16: return 2;
   case OR_FP8: return 1;
+  case OR_NVFP4: return 0; /* two elements per byte: see head_bytes */
   default: return 8;
   }
+}
+
+/* Bytes of one head's checkpoint. */
+static int64_t head_bytes(const or_cache *c) {
+  const int64_t PN = (int64_t)c->headdim * c->dstate;
+  return c->state_dtype == OR_NVFP4 ? PN / 2 : PN * state_elem_bytes(c->state_dtype);
+}
+
+/*
+ * NVFP4 checkpoint (a reading of the pages' NVFP4 read checkpoint; the
+ * layout is this library's): element (p, n) is an e2m1 code, blocks of 16
+ * consecutive n of a row share an e4m3 block scale, and each (slot, head) has
+ * an fp32 second-level scale g; the value is e2m1 * e4m3(block) * g.
+ * Codes, row-major: element p N + n in byte (p N + n) / 2, the even element
+ * in the low nibble.  Tiled (P = 64, N = 128): the 32 values of quarter q of
+ * row p (lane l = 16 q + m, rb = p / 16, m = p % 16, t = n % 32) fill the
+ * 16 bytes at rb * 1024 + l * 16, value t in byte t / 2 (even t low nibble).
+ * Block scales (P N / 16 bytes per head), row-major: p (N / 16) + n / 16.
+ * Tiled: the two blocks of lane l's quarter in row block rb are bytes
+ * l * 8 + rb * 2 + (t / 16), so each lane's eight scales are contiguous.
+ */
+static int64_t nvfp4_code_byte(const or_cache *c, int p, int n, int *high) {
+  if (c->state_layout == 0) {
+    const int64_t i = (int64_t)p * c->dstate + n;
+    *high = (int)(i & 1);
+    return i >> 1;
+  }
+  const int rb = p / 16, m = p % 16, q = n / 32, t = n % 32, l = 16 * q + m;
+  *high = t & 1;
+  return (int64_t)rb * 1024 + (int64_t)l * 16 + t / 2;
+}
+
+static int64_t nvfp4_scale_byte(const or_cache *c, int p, int n) {
+  if (c->state_layout == 0) return (int64_t)p * (c->dstate / 16) + n / 16;
+  const int rb = p / 16, m = p % 16, q = n / 32, t = n % 32, l = 16 * q + m;
+  return (int64_t)l * 8 + rb * 2 + t / 16;
+}
+
+static float nvfp4_gscale(const or_cache *c, int slot, int head) {
+  float g;
+  memcpy(&g, c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)head * 4, 4);
+  return g;
 }
 
 /* Byte offset of element (p, n) inside one head's checkpoint.
@@ -326,8 +399,18 @@ static int64_t elem_offset(const or_cache *c, int eb, int p, int n) {
 /* Decode the checkpoint of (slot, head) into h[P*N] (fp64). */
 static void decode_state(const or_cache *c, int slot, int head, double *h) {
   const int P = c->headdim, N = c->dstate, eb = state_elem_bytes(c->state_dtype);
-  const uint8_t *base = c->state + (int64_t)slot * c->state_stride +
-                        (int64_t)head * P * N * eb;
+  const uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * head_bytes(c);
+  if (c->state_dtype == OR_NVFP4) {
+    const uint8_t *sf = c->scale + (int64_t)slot * c->scale_stride + (int64_t)head * (P * N / 16);
+    const double g = nvfp4_gscale(c, slot, head);
+    for (int p = 0; p < P; ++p)
+      for (int n = 0; n < N; ++n) {
+        int hi;
+        const uint8_t byte = base[nvfp4_code_byte(c, p, n, &hi)];
+        h[p * N + n] = or_e2m1_value(hi ? byte >> 4 : byte & 15) * or_e4m3_value(sf[nvfp4_scale_byte(c, p, n)]) * g;
+      }
+    return;
+  }
   for (int p = 0; p < P; ++p) {
     double sc = 1.0;
     if (c->state_dtype == OR_FP8) {
@@ -403,6 +486,46 @@ static void encode_row(const or_cache *c, int slot, int head, int p,
     default: break;
     }
   }
+}
+
+/*
+ * Encode one head of an fp32 state into the NVFP4 checkpoint, nearest
+ * encoding at both levels: g = fp32(max |v| / 2688) (2688 = 6 * 448: the
+ * head's largest value maps to the largest e2m1 value times the largest
+ * e4m3 value; 1 if not positive), and per block of 16 with a = max |v|:
+ * block scale = e4m3_sat(fp32(a / fp32(6 g))), element scale
+ * es = fp32(e4m3 value * g), code = e2m1_sat(fp32(v / es)) (a zero block
+ * scale stores signed zeros).  IEEE single precision throughout.
+ */
+static void encode_head_nvfp4(const or_cache *c, int slot, int head, const float *hv) {
+  const int P = c->headdim, N = c->dstate;
+  uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * head_bytes(c);
+  uint8_t *sf = c->scale + (int64_t)slot * c->scale_stride + (int64_t)head * (P * N / 16);
+  float m = 0.0f;
+  for (int i = 0; i < P * N; ++i)
+    if (fabsf(hv[i]) > m) m = fabsf(hv[i]);
+  float g = m / 2688.0f;
+  if (!(g > 0.0f)) g = 1.0f;
+  memcpy(c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)head * 4, &g, 4);
+  const float ds = 6.0f * g;
+  for (int p = 0; p < P; ++p)
+    for (int n0 = 0; n0 < N; n0 += 16) {
+      float a = 0.0f;
+      for (int i = 0; i < 16; ++i)
+        if (fabsf(hv[p * N + n0 + i]) > a) a = fabsf(hv[p * N + n0 + i]);
+      const float t = a / ds;
+      const uint8_t code = or_enc_e4m3_sat((double)t);
+      sf[nvfp4_scale_byte(c, p, n0)] = code;
+      const float es = (float)or_e4m3_value(code) * g;
+      for (int i = 0; i < 16; ++i) {
+        const float v = hv[p * N + n0 + i];
+        const float q = es > 0.0f ? v / es : 0.0f * v;
+        int hi;
+        uint8_t *byte = base + nvfp4_code_byte(c, p, n0 + i, &hi);
+        const uint8_t e = or_enc_e2m1_sat((double)q);
+        *byte = hi ? (uint8_t)((*byte & 0x0F) | (e << 4)) : (uint8_t)((*byte & 0xF0) | e);
+      }
+    }
 }
 
 /* fp64 state mode (test only, row-major): store without rounding. */
@@ -590,6 +713,13 @@ int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
       }
       if (c->state_dtype == OR_F64) {
         store_state_f64(c, slot, hh, h);
+      } else if (c->state_dtype == OR_NVFP4) {
+        float *hv = (float *)malloc(sizeof(float) * P * N);
+        for (int e = 0; e < P * N; ++e) hv[e] = (float)h[e];
+        encode_head_nvfp4(c, slot, hh, hv);
+        if (c->recur)
+          for (int p = 0; p < P; ++p) encode_recur_row(c, slot, hh, p, hv + (int64_t)p * N, seed);
+        free(hv);
       } else {
         for (int p = 0; p < P; ++p) {
           for (int q = 0; q < N; ++q) row[q] = (float)h[p * N + q];
@@ -632,6 +762,10 @@ void or_init_state(const or_cache *c, const float *states, int64_t states_stride
         for (int e = 0; e < P * N; ++e) h[e] = src[(int64_t)hh * P * N + e];
         store_state_f64(c, slot, hh, h);
         free(h);
+      } else if (c->state_dtype == OR_NVFP4) {
+        encode_head_nvfp4(c, slot, hh, src + (int64_t)hh * P * N);
+        if (c->recur)
+          for (int p = 0; p < P; ++p) encode_recur_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N, seed);
       } else {
         for (int p = 0; p < P; ++p) {
           encode_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N);
@@ -664,6 +798,19 @@ void or_bf16_value_array(const uint16_t *b, double *out, int64_t n) {
 }
 void or_f16_value_array(const uint16_t *b, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = or_f16_value(b[i]);
+}
+void or_e2m1_value_array(const uint8_t *b, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_e2m1_value(b[i]);
+}
+void or_enc_e2m1_array(const double *v, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_enc_e2m1_sat(v[i]);
+}
+/* Decode one (slot, head) checkpoint into out[P*N] (any state dtype). */
+void or_decode_head(const or_cache *c, int slot, int head, double *out) { decode_state(c, slot, head, out); }
+/* Encode one head of fp32 values into an NVFP4 checkpoint. */
+void or_encode_head_nvfp4(const or_cache *c, int slot, int head, const float *hv) {
+  build_tables();
+  encode_head_nvfp4(c, slot, head, hv);
 }
 void or_e4m3_value_array(const uint8_t *b, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = or_e4m3_value(b[i]);

@@ -29,7 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "libssu_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-_DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "f64": 4}
+_DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "f64": 4, "nvfp4": 5}
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +55,7 @@ class _OrCache(ctypes.Structure):
         ("dt_cache", ctypes.c_void_p), ("dt_stride", ctypes.c_int64),
         ("ring_start", ctypes.c_void_p),
         ("recur", ctypes.c_void_p), ("recur_stride", ctypes.c_int64),
+        ("gscale", ctypes.c_void_p), ("gscale_stride", ctypes.c_int64),
     ]
 
 
@@ -77,9 +78,13 @@ def lib():
             L.or_sr_f16_array.argtypes = [P, P, P, I64]
             L.or_sr_bits_array.restype = None
             L.or_sr_bits_array.argtypes = [ctypes.c_uint64, I, I, P, I64]
+            L.or_decode_head.restype = None
+            L.or_decode_head.argtypes = [ctypes.POINTER(_OrCache), I, I, P]
+            L.or_encode_head_nvfp4.restype = None
+            L.or_encode_head_nvfp4.argtypes = [ctypes.POINTER(_OrCache), I, I, P]
             for name in ("or_enc_bf16_array", "or_enc_f16_array", "or_enc_e4m3_array",
                          "or_bf16_value_array", "or_f16_value_array", "or_e4m3_value_array",
-                         "or_softplus_array"):
+                         "or_e2m1_value_array", "or_enc_e2m1_array", "or_softplus_array"):
                 f = getattr(L, name)
                 f.restype = None
                 f.argtypes = [P, P, I64]
@@ -109,6 +114,8 @@ def _as_orcache(cache) -> _OrCache:
     assert cache.ring_start.dtype == np.int32
     recur = getattr(cache, "recur", None)
     assert recur is None or recur.flags["C_CONTIGUOUS"]
+    gscale = getattr(cache, "gscale", None)
+    assert gscale is None or gscale.flags["C_CONTIGUOUS"]
     return _OrCache(
         s.num_slots, s.nheads, s.ngroups, s.headdim, s.dstate, s.ring_len,
         _DTYPE_CODE[s.state_dtype], {"rowmajor": 0, "tiled": 1}[s.state_layout],
@@ -118,7 +125,8 @@ def _as_orcache(cache) -> _OrCache:
         cache.B_cache.ctypes.data, cache.B_cache.shape[1],
         cache.dt_cache.ctypes.data, cache.dt_cache.shape[1],
         cache.ring_start.ctypes.data,
-        None if recur is None else recur.ctypes.data, 0 if recur is None else recur.shape[1])
+        None if recur is None else recur.ctypes.data, 0 if recur is None else recur.shape[1],
+        None if gscale is None else gscale.ctypes.data, 0 if gscale is None else gscale.shape[1])
 
 
 _STATUS_BAD_FOLD = 2
@@ -270,6 +278,21 @@ def sr_bits(seed, slot, head, n):
     return out
 
 
+def encode_head_nvfp4(cache, slot, head, values):
+    """Encode fp32 [P, N] values into head `head` of an NVFP4 checkpoint."""
+    v = np.ascontiguousarray(values, np.float32)
+    oc = _as_orcache(cache)
+    lib().or_encode_head_nvfp4(ctypes.byref(oc), int(slot), int(head), v.ctypes.data)
+
+
+def e2m1_value(b):
+    return _arr("or_e2m1_value_array", b, np.uint8, np.float64)
+
+
+def enc_e2m1(v):
+    return _arr("or_enc_e2m1_array", v, np.float64, np.uint8)
+
+
 def decode_recur(cache, slot):
     """fp64 [H, P, N] value of one slot's FP16 recurrence checkpoint."""
     return f16_value(cache.recur_logical(slot))
@@ -313,6 +336,12 @@ def softplus(v):
 def decode_state(cache, slot):
     """fp64 [H, P, N] value of one slot's checkpoint (decode rule of the oracle)."""
     s = cache.spec
+    if s.state_dtype == "nvfp4":
+        oc = _as_orcache(cache)
+        out = np.empty((s.nheads, s.headdim, s.dstate), np.float64)
+        for h in range(s.nheads):
+            lib().or_decode_head(ctypes.byref(oc), int(slot), h, out[h].ctypes.data)
+        return out
     raw = cache.state_logical(slot)
     if s.state_dtype in ("f32", "f64"):
         return raw.astype(np.float64)

@@ -22,13 +22,20 @@ def upload_cache(cache: CacheArrays, device) -> Dict[str, torch.Tensor]:
     t = {f: torch.from_numpy(getattr(cache, f)).to(device) for f in CACHE_FIELDS}
     t["ring_start"] = torch.from_numpy(cache.ring_start).to(device)
     t["recur"] = None if cache.recur is None else torch.from_numpy(cache.recur).to(device)
+    t["gscale"] = None if cache.gscale is None else torch.from_numpy(cache.gscale).to(device)
     return t
 
 
+def _opt(t, key, idx=None):
+    a = t.get(key)
+    if a is None:
+        return None
+    return (a if idx is None else a.index_select(0, idx)).cpu().numpy()
+
+
 def download_cache(spec: CacheSpec, t: Dict[str, torch.Tensor]) -> CacheArrays:
-    recur = t.get("recur")
     return CacheArrays(spec, *(t[f].cpu().numpy() for f in CACHE_FIELDS),
-                       t["ring_start"].cpu().numpy(), None if recur is None else recur.cpu().numpy())
+                       t["ring_start"].cpu().numpy(), _opt(t, "recur"), _opt(t, "gscale"))
 
 
 def download_subset(spec: CacheSpec, t: Dict[str, torch.Tensor], slots: Sequence[int]):
@@ -41,9 +48,8 @@ def download_subset(spec: CacheSpec, t: Dict[str, torch.Tensor], slots: Sequence
     sub = CacheSpec(**{**spec.__dict__, "num_slots": len(slots) + 1})
     arrs = [t[f].index_select(0, idx).cpu().numpy() for f in CACHE_FIELDS]
     rs = t["ring_start"].index_select(0, idx).cpu().numpy()
-    recur = t.get("recur")
-    recur = None if recur is None else recur.index_select(0, idx).cpu().numpy()
-    return CacheArrays(sub, *arrs, rs, recur), {s: i + 1 for i, s in enumerate(slots)}
+    return (CacheArrays(sub, *arrs, rs, _opt(t, "recur", idx), _opt(t, "gscale", idx)),
+            {s: i + 1 for i, s in enumerate(slots)})
 
 
 def _bf16_bytes(x: torch.Tensor) -> torch.Tensor:
@@ -60,11 +66,21 @@ def make_cache_device(spec: CacheSpec, seed: int, device, h0_std: float = 0.1,
     st = spec.strides()
     t = {f: torch.full((S, st[_STRIDE_KEY[f]]), CANARY, dtype=torch.uint8, device=device)
          for f in CACHE_FIELDS}
+    t["gscale"] = (torch.full((S, st["gscale"]), CANARY, dtype=torch.uint8, device=device)
+                   if "gscale" in st else None)
     dt = spec.state_dtype
     for s0 in range(0, S, chunk_slots):
         n = min(chunk_slots, S - s0)
         sl = slice(s0, s0 + n)
-        if dt == "fp8":
+        if dt == "nvfp4":  # the law of workloads.random_nvfp4
+            t["state"][sl, : spec.state_bytes()] = torch.randint(
+                0, 256, (n, H * P * N // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+            e = torch.randint(5, 9, (n, H * P * N // 16), generator=g, device=device, dtype=torch.int32)
+            m = torch.randint(0, 8, (n, H * P * N // 16), generator=g, device=device, dtype=torch.int32)
+            t["scale"][sl, : spec.scale_bytes()] = (e * 8 + m).to(torch.uint8)
+            gs = (h0_std / 3.0) * (0.5 + torch.rand(n, H, generator=g, device=device))
+            t["gscale"][sl, : spec.gscale_bytes()] = gs.view(torch.uint8).reshape(n, -1)
+        elif dt == "fp8":
             codes = (torch.randn(n, H, P, N, generator=g, device=device) * 32.0).clamp(-448, 448)
             t["state"][sl, : spec.state_bytes()] = codes.to(torch.float8_e4m3fn).view(
                 torch.uint8).reshape(n, -1)

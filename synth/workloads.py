@@ -39,8 +39,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-DTYPES = ("f32", "bf16", "f16", "fp8", "f64")
-ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "f64": 8}
+DTYPES = ("f32", "bf16", "f16", "fp8", "f64", "nvfp4")
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "f64": 8, "nvfp4": 0.5}
 CANARY = 0xA5
 
 
@@ -71,13 +71,20 @@ class CacheSpec:
 
     # packed per-slot byte sizes
     def state_bytes(self):
-        return self.nheads * self.headdim * self.dstate * ELEM_BYTES[self.state_dtype]
+        return int(self.nheads * self.headdim * self.dstate * ELEM_BYTES[self.state_dtype])
 
     def recur_bytes(self):
         return self.nheads * self.headdim * self.dstate * 2
 
     def scale_bytes(self):
+        """fp8: an f32 scale per row; nvfp4: an e4m3 scale per 16 values."""
+        if self.state_dtype == "nvfp4":
+            return self.nheads * self.headdim * self.dstate // 16
         return self.nheads * self.headdim * 4
+
+    def gscale_bytes(self):
+        """nvfp4: the f32 second-level scale of each head."""
+        return self.nheads * 4
 
     def x_bytes(self):
         return self.nheads * self.ring_len * self.headdim * 2
@@ -100,6 +107,8 @@ class CacheSpec:
         )
         if self.separate:
             d["recur"] = _round16(self.recur_bytes()) + p
+        if self.state_dtype == "nvfp4":
+            d["gscale"] = _round16(self.gscale_bytes()) + p
         return d
 
 
@@ -130,11 +139,13 @@ class CacheArrays:
     dt_cache: np.ndarray
     ring_start: np.ndarray  # int32 [num_slots]
     recur: Optional[np.ndarray] = None  # uint8 [num_slots, stride]: FP16 recurrence checkpoint
+    gscale: Optional[np.ndarray] = None  # uint8 [num_slots, stride]: nvfp4 second-level scales
 
     def copy(self) -> "CacheArrays":
         return CacheArrays(self.spec, *(a.copy() for a in (
             self.state, self.scale, self.x_cache, self.B_cache, self.dt_cache,
-            self.ring_start)), None if self.recur is None else self.recur.copy())
+            self.ring_start)), None if self.recur is None else self.recur.copy(),
+            None if self.gscale is None else self.gscale.copy())
 
     def recur_view(self, slot):
         """Recurrence checkpoint (fp16 bits) of one slot in storage order, [H, P * N]."""
@@ -152,17 +163,19 @@ class CacheArrays:
     # typed views of the packed part of one slot (for tests)
     def _state_np_dtype(self):
         return {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16,
-                "fp8": np.uint8, "f64": np.float64}[self.spec.state_dtype]
+                "fp8": np.uint8, "f64": np.float64, "nvfp4": np.uint8}[self.spec.state_dtype]
 
     def state_view(self, slot):
         """Checkpoint elements of one slot in storage order, [H, P * N] (a view)."""
         s = self.spec
         raw = self.state[slot, : s.state_bytes()]
-        return raw.view(self._state_np_dtype()).reshape(s.nheads, s.headdim * s.dstate)
+        return raw.view(self._state_np_dtype()).reshape(s.nheads, -1)
 
     def state_logical(self, slot):
         """Checkpoint elements of one slot as [H, P, N] (a copy, logical order)."""
         s = self.spec
+        if s.state_dtype == "nvfp4":
+            raise NotImplementedError("nvfp4 packs two codes per byte; decode with the oracle")
         v = self.state_view(slot)
         if s.state_layout == "rowmajor":
             return v.reshape(s.nheads, s.headdim, s.dstate).copy()
@@ -180,7 +193,13 @@ class CacheArrays:
 
     def scale_view(self, slot):
         s = self.spec
+        if s.state_dtype == "nvfp4":  # e4m3 block scales in storage order
+            return self.scale[slot, : s.scale_bytes()].reshape(s.nheads, -1)
         return self.scale[slot, : s.scale_bytes()].view(np.float32).reshape(s.nheads, s.headdim)
+
+    def gscale_view(self, slot):
+        s = self.spec
+        return self.gscale[slot, : s.gscale_bytes()].view(np.float32)
 
     def x_view(self, slot):
         s = self.spec
@@ -238,11 +257,26 @@ def _fill_slots(arr: np.ndarray, packed: np.ndarray):
     arr[:, : packed.shape[1]] = packed
 
 
+def random_nvfp4(n: int, H: int, P: int, N: int, g: torch.Generator, h0_std: float = 0.1):
+    """Random nvfp4 checkpoints: every code byte uniform (all 16 e2m1 codes in
+    both nibbles), block-scale codes with exponent field 5..8 and a random
+    mantissa (e4m3 values 0.25 .. 3.75), second-level scales
+    h0_std / 3 * U(0.5, 1.5): codes, block scales and second-level scales as
+    byte arrays [n, ...]."""
+    codes = torch.randint(0, 256, (n, H * P * N // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    e = torch.randint(5, 9, (n, H * P * N // 16), generator=g, dtype=torch.int32)
+    m = torch.randint(0, 8, (n, H * P * N // 16), generator=g, dtype=torch.int32)
+    sf = (e * 8 + m).to(torch.uint8)
+    gs = (h0_std / 3.0) * (0.5 + torch.rand(n, H, generator=g))
+    return codes.numpy(), sf.numpy(), gs.to(torch.float32).numpy().view(np.uint8).reshape(n, -1)
+
+
 def random_state_bytes(spec: CacheSpec, n: int, g: torch.Generator, h0_std: float = 0.1):
     """Random checkpoints for n slots: (state bytes [n, state_bytes], scale bytes)."""
     H, P, N = spec.nheads, spec.headdim, spec.dstate
     dt = spec.state_dtype
     scale = np.zeros((n, H * P * 4), np.uint8)
+    assert dt != "nvfp4", "nvfp4 checkpoints come from random_nvfp4"
     if dt == "fp8":
         codes = (torch.randn(n, H, P, N, generator=g) * 32.0).clamp(-448, 448)
         codes = codes.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
@@ -268,9 +302,15 @@ def make_cache(spec: CacheSpec, seed: int, h0_std: float = 0.1) -> CacheArrays:
                         spec.dstate, spec.ring_len)
     st = spec.strides()
     arrs = {k: np.full((S, st[k]), CANARY, np.uint8) for k in st}
-    state, scale = random_state_bytes(spec, S, g, h0_std)
+    gscale = None
+    if spec.state_dtype == "nvfp4":
+        state, scale, gs = random_nvfp4(S, H, P, N, g, h0_std)
+        gscale = arrs["gscale"]
+        _fill_slots(gscale, gs)
+    else:
+        state, scale = random_state_bytes(spec, S, g, h0_std)
     _fill_slots(arrs["state"], state)
-    if spec.state_dtype == "fp8":
+    if spec.state_dtype in ("fp8", "nvfp4"):
         _fill_slots(arrs["scale"], scale)
     xr = _bf16_bits(torch.randn(S, H, L, P, generator=g)).view(np.uint8).reshape(S, -1)
     Br = _bf16_bits(torch.randn(S, G, L, N, generator=g)).view(np.uint8).reshape(S, -1)
@@ -287,7 +327,7 @@ def make_cache(spec: CacheSpec, seed: int, h0_std: float = 0.1) -> CacheArrays:
         h0r = torch.randn(S, H, P, N, generator=g, dtype=torch.float64) * h0_std
         _fill_slots(recur, _f16_bits(h0r.to(torch.float32)).view(np.uint8).reshape(S, -1))
     return CacheArrays(spec, arrs["state"], arrs["scale"], arrs["x"], arrs["B"], arrs["dt"],
-                       ring_start.copy(), recur)
+                       ring_start.copy(), recur, gscale)
 
 
 def make_params(spec: CacheSpec, seed: int):
