@@ -1,6 +1,6 @@
 """Benchmark of the ReplaySSM hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload fp8|prod|mtp|large|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload fp8|nvfp4|prod|mtp|large|tiny]
                     [--algo auto|monolith|split] [--batch B] [--no-cpu-baseline]
                     [--no-fuse] [--separate]
 
@@ -49,6 +49,11 @@ METRIC = "replayed SSU tokens/sec and achieved HBM GB/s (% of MI355X peak) at 1 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 
 WORKLOADS = {
+    "nvfp4": dict(nheads=128, ngroups=8, state_dtype="nvfp4", batch=256, T=4, pnat_max=0, out="bf16",
+                  flush=(1, 4), varlen=False, slot_pad=0, separate=True,
+                  desc="NVFP4 read checkpoint (e2m1, e4m3 block scales, f32 head scale) + FP16 recurrence "
+                       "checkpoint with stochastic rounding, batch 256, H128 G8, P64 N128, T=4, fold "
+                       "k~U{1..4} every step, L=16"),
     "fp8": dict(nheads=128, ngroups=8, state_dtype="fp8", batch=256, T=4, pnat_max=0, out="bf16",
                 flush=(1, 4), varlen=False, slot_pad=0,
                 desc="fp8 e4m3 checkpoint + f32 row scales, batch 256, H128 G8, P64 N128, T=4, "
@@ -69,7 +74,17 @@ WORKLOADS = {
                  desc="tiny reference, fp32 checkpoint, batch 2, H8 G1, T=1"),
 }
 
-ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
+ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "nvfp4": 0.5}
+
+
+def scale_bytes(spec, H):
+    """Scale bytes read or written with one slot's checkpoint: fp8 an f32 per
+    row, nvfp4 an e4m3 per 16 values and an f32 per head."""
+    if spec.state_dtype == "fp8":
+        return H * 64 * 4
+    if spec.state_dtype == "nvfp4":
+        return H * (64 * 128 // 16 + 4)
+    return 0
 
 
 def step_bytes(spec, H, G, pnat, Tb, out_bytes=2):
@@ -77,7 +92,7 @@ def step_bytes(spec, H, G, pnat, Tb, out_bytes=2):
     (+ fp8 row scales) read, live-ring x/B/dt' read, new x/B/C/dt read, out
     written, x/B/dt' appended.  Scratch traffic of the split is excluded."""
     P, N = 64, 128
-    per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
+    per_state = int(H * P * N * ELEM[spec.state_dtype]) + scale_bytes(spec, H)
     tot = 0
     for p, t in zip(pnat, Tb):
         p, t = int(p), int(t)
@@ -91,7 +106,7 @@ def step_bytes(spec, H, G, pnat, Tb, out_bytes=2):
 
 def state_bytes(spec, H):
     """Checkpoint (+ fp8 row scales) bytes of one slot."""
-    return H * 64 * 128 * ELEM[spec.state_dtype] + (H * 64 * 4 if spec.state_dtype == "fp8" else 0)
+    return int(H * 64 * 128 * ELEM[spec.state_dtype]) + scale_bytes(spec, H)
 
 
 def fused_bytes(spec, H, G, k, Tb, out_bytes=2):
@@ -118,7 +133,7 @@ def flush_bytes(spec, H, G, k):
     """Algorithmic bytes of one flush: checkpoint read + write and the k ring
     tokens (x, B, dt') read, per entry with k > 0."""
     P, N = 64, 128
-    per_state = H * P * N * ELEM[spec.state_dtype] + (H * P * 4 if spec.state_dtype == "fp8" else 0)
+    per_state = int(H * P * N * ELEM[spec.state_dtype]) + scale_bytes(spec, H)
     return int(sum(2 * per_state + int(kk) * (H * P * 2 + G * N * 2 + H * 4) for kk in k if kk > 0))
 
 
@@ -159,7 +174,9 @@ def main():
     wl = dict(WORKLOADS[args.workload])
     wl_batch = wl["batch"]
     fused = bool(wl["flush"]) and args.fuse
-    if args.separate and (not wl["flush"] or wl["state_dtype"] != "fp8"):
+    if wl.get("separate"):
+        args.separate = True  # an nvfp4 read checkpoint always has the recurrence checkpoint
+    if args.separate and (not wl["flush"] or wl["state_dtype"] not in ("fp8", "nvfp4")):
         print("--separate needs a workload with flushes and an fp8 checkpoint (fp8)", file=sys.stderr)
         sys.exit(2)
     if args.batch:
@@ -185,7 +202,7 @@ def main():
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     dc = ssu.DeviceCache(num_slots, H, G, spec.ring_len, spec.state_dtype, tcache["state"],
                          tcache["scale"], tcache["x_cache"], tcache["B_cache"], tcache["dt_cache"],
-                         tcache["ring_start"], status, recur=tcache.get("recur"))
+                         tcache["ring_start"], status, recur=tcache.get("recur"), gscale=tcache.get("gscale"))
 
     rng = np.random.default_rng(args.seed)
     perm = rng.permutation(np.arange(1, num_slots, dtype=np.int32))
@@ -345,7 +362,8 @@ def main():
             "batch": batch, "nheads": H, "ngroups": G, "headdim": 64, "dstate": 128, "ring_len": 16,
             "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "algo": algo_used,
             "separate_checkpoints": (None if not args.separate else
-                                     "FP16 recurrence checkpoint, stochastic rounding, fp8 read checkpoint"),
+                                     "FP16 recurrence checkpoint, stochastic rounding, %s read checkpoint"
+                                     % wl["state_dtype"]),
             "flush": (None if not wl["flush"] else
                       "fused into the replay step (ssu_replay_step with num_fold = pnat = k)" if fused
                       else "separate ssu_flush after the step"),

@@ -62,7 +62,8 @@ typedef enum ssu_dtype {
   SSU_F32 = 0,
   SSU_BF16 = 1,
   SSU_F16 = 2,
-  SSU_FP8_E4M3 = 3 /* OCP e4m3fn codes (max 448) with an fp32 scale per state row */
+  SSU_FP8_E4M3 = 3, /* OCP e4m3fn codes (max 448) with an fp32 scale per state row */
+  SSU_NVFP4 = 4     /* e2m1 codes, an e4m3 scale per 16 values, an fp32 scale per head */
 } ssu_dtype;
 
 typedef enum ssu_algo {
@@ -94,6 +95,8 @@ enum {
  *   state       [slot][nheads][64 * 128]         state_dtype, MFMA-tiled (below)
  *   state_scale [slot][nheads][headdim]          f32, fp8 state only: the row's
  *                                                value is code * scale
+ *               [slot][nheads][512]              u8, nvfp4 state: e4m3 block scales
+ *   state_head_scale [slot][nheads]              f32, nvfp4 state only
  *   x_cache     [slot][nheads][ring_len][headdim] io_dtype
  *   B_cache     [slot][ngroups][ring_len][dstate] io_dtype
  *   dt_cache    [slot][nheads][ring_len]          f32, holds dt' = softplus(dt + dt_bias)
@@ -120,8 +123,19 @@ enum {
  * past 65504), else toward zero; u is the low 7 bits of byte e % 16 of
  * Philox4x32-10 at counter (e / 16, head, slot, 0) keyed by the call's
  * 64-bit sr_seed (e = p * 128 + n); a caller passes a different seed on
- * every call.  recur_state requires
- * state_dtype == SSU_FP8_E4M3 (else SSU_ERR_UNSUPPORTED).
+ * every call.  recur_state requires state_dtype SSU_FP8_E4M3 or SSU_NVFP4
+ * (else SSU_ERR_UNSUPPORTED).
+ * NVFP4 read checkpoint [VP Claims; VD init] (requires recur_state): value =
+ * e2m1(code) * e4m3(block scale) * g, blocks of 16 consecutive n of a row, g
+ * per (slot, head).  Written with nearest encoding from the fp32 fold:
+ * g = fp32(max |v| / 2688) (1 if not positive), block scale =
+ * e4m3(fp32(a / fp32(6 g))) for a block's max |v| (saturating), code =
+ * e2m1(v * fp32(1 / fp32(e4m3 * g))) (nearest even, saturating at 6; a zero
+ * block scale gives signed zeros).  Layout of one head: row block rb, lane
+ * l = 16 q + m (row 16 rb + m, values n = 32 q + t): codes of t = 0..31 in
+ * the 16 bytes at rb * 1024 + l * 16 (value t in byte t / 2, even t in the
+ * low nibble); block scales (t < 16, t >= 16) in state_scale bytes
+ * l * 8 + rb * 2 + 0 / 1 of the head's 512.
  * Requirements: headdim == 64, dstate == 128, nheads % ngroups == 0,
  * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer and slot stride
  * 16-byte aligned.  status may be NULL.
@@ -132,7 +146,7 @@ typedef struct ssu_cache {
   ssu_dtype io_dtype;
   void *state;
   int64_t state_slot_stride;
-  float *state_scale;
+  void *state_scale;
   int64_t scale_slot_stride;
   void *x_cache;
   int64_t x_slot_stride;
@@ -144,6 +158,8 @@ typedef struct ssu_cache {
   int32_t *status;
   void *recur_state;
   int64_t recur_slot_stride;
+  float *state_head_scale; /* nvfp4 only, else NULL */
+  int64_t head_scale_slot_stride;
 } ssu_cache;
 
 /*

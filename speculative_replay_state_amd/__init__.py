@@ -29,12 +29,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ssu_dtype / ssu_algo / return codes / status bits (include/ssu.h)
-SSU_F32, SSU_BF16, SSU_F16, SSU_FP8_E4M3 = 0, 1, 2, 3
+SSU_F32, SSU_BF16, SSU_F16, SSU_FP8_E4M3, SSU_NVFP4 = 0, 1, 2, 3, 4
 SSU_ALGO_AUTO, SSU_ALGO_MONOLITH, SSU_ALGO_SPLIT = 0, 1, 2
 SSU_OK, SSU_ERR_INVALID, SSU_ERR_UNSUPPORTED, SSU_ERR_HIP, SSU_ERR_WORKSPACE = 0, -1, -2, -3, -4
 SSU_STATUS_BAD_PNAT, SSU_STATUS_BAD_FOLD, SSU_STATUS_BAD_SEQLEN, SSU_STATUS_BAD_RING = 1, 2, 4, 8
 
-DTYPE_CODES = {"f32": SSU_F32, "bf16": SSU_BF16, "f16": SSU_F16, "fp8": SSU_FP8_E4M3}
+DTYPE_CODES = {"f32": SSU_F32, "bf16": SSU_BF16, "f16": SSU_F16, "fp8": SSU_FP8_E4M3, "nvfp4": SSU_NVFP4}
 ALGO_CODES = {"auto": SSU_ALGO_AUTO, "monolith": SSU_ALGO_MONOLITH, "split": SSU_ALGO_SPLIT}
 
 _P = ctypes.c_void_p
@@ -54,6 +54,7 @@ class SsuCache(ctypes.Structure):
         ("dt_cache", _P), ("dt_slot_stride", _I64),
         ("ring_start", _P), ("status", _P),
         ("recur_state", _P), ("recur_slot_stride", _I64),
+        ("state_head_scale", _P), ("head_scale_slot_stride", _I64),
     ]
 
 
@@ -180,19 +181,22 @@ class DeviceCache:
     headdim: int = 64
     dstate: int = 128
     recur: object = None  # FP16 recurrence checkpoint (separate checkpoints) or None
+    gscale: object = None  # nvfp4: uint8 [num_slots, stride] holding the f32 head scales
 
     def desc(self) -> SsuCache:
-        fp8 = self.state_dtype == "fp8"
+        scaled = self.state_dtype in ("fp8", "nvfp4")
+        nvfp4 = self.state_dtype == "nvfp4"
         return SsuCache(
             self.num_slots, self.nheads, self.ngroups, self.headdim, self.dstate, self.ring_len,
             DTYPE_CODES[self.state_dtype], SSU_BF16,
             _ptr(self.state), self.state.stride(0),
-            _ptr(self.scale) if fp8 else None, self.scale.stride(0) if fp8 else 0,
+            _ptr(self.scale) if scaled else None, self.scale.stride(0) if scaled else 0,
             _ptr(self.x_cache), self.x_cache.stride(0),
             _ptr(self.B_cache), self.B_cache.stride(0),
             _ptr(self.dt_cache), self.dt_cache.stride(0),
             _ptr(self.ring_start), _ptr(self.status),
-            _ptr(self.recur), 0 if self.recur is None else self.recur.stride(0))
+            _ptr(self.recur), 0 if self.recur is None else self.recur.stride(0),
+            _ptr(self.gscale) if nvfp4 else None, self.gscale.stride(0) if nvfp4 else 0)
 
 
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,

@@ -49,8 +49,8 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="ssu_build_") as tmp:
         objs, jobs = [], []
-        # the kernels once per state type (fp32, bf16, fp16, fp8), compiled in parallel
-        for st in range(4):
+        # the kernels once per state type (fp32, bf16, fp16, fp8, nvfp4), compiled in parallel
+        for st in range(5):
             o = os.path.join(tmp, "ssu_kernels_%d.o" % st)
             objs.append(o)
             jobs.append([hipcc, "--offload-arch=" + ARCH, *COMMON, "-DSSU_INST_ST=%d" % st, "-c",

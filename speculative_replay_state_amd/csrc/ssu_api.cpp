@@ -37,12 +37,15 @@ int ok() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int64_t state_elem_bytes(ssu_dtype t) {
+// Bytes of one head's checkpoint.
+int64_t state_head_bytes(ssu_dtype t) {
+  const int64_t e = (int64_t)ssu::kHeadDim * ssu::kDState;
   switch (t) {
-    case SSU_F32: return 4;
-    case SSU_BF16: return 2;
-    case SSU_F16: return 2;
-    case SSU_FP8_E4M3: return 1;
+    case SSU_F32: return 4 * e;
+    case SSU_BF16: return 2 * e;
+    case SSU_F16: return 2 * e;
+    case SSU_FP8_E4M3: return e;
+    case SSU_NVFP4: return e / 2;
   }
   return 0;
 }
@@ -53,6 +56,7 @@ int state_type_of(ssu_dtype t) {
     case SSU_BF16: return ssu::kBF16;
     case SSU_F16: return ssu::kF16;
     case SSU_FP8_E4M3: return ssu::kFP8;
+    case SSU_NVFP4: return ssu::kNVFP4;
   }
   return -1;
 }
@@ -76,10 +80,17 @@ int check_cache(const ssu_cache *c) {
     return fail(SSU_ERR_UNSUPPORTED, "io_dtype must be SSU_BF16 (x, B, C and the x/B rings)");
   if (!c->state || !c->x_cache || !c->B_cache || !c->dt_cache || !c->ring_start)
     return fail(SSU_ERR_INVALID, "cache tensors must not be NULL");
-  if (c->state_dtype == SSU_FP8_E4M3 && !c->state_scale)
-    return fail(SSU_ERR_INVALID, "fp8 state requires state_scale");
-  if (c->recur_state && c->state_dtype != SSU_FP8_E4M3)
-    return fail(SSU_ERR_UNSUPPORTED, "recur_state (separate checkpoints) requires an fp8 state");
+  const bool nvfp4 = c->state_dtype == SSU_NVFP4;
+  if ((c->state_dtype == SSU_FP8_E4M3 || nvfp4) && !c->state_scale)
+    return fail(SSU_ERR_INVALID, "fp8 and nvfp4 states require state_scale");
+  if (nvfp4 && !c->state_head_scale)
+    return fail(SSU_ERR_INVALID, "nvfp4 state requires state_head_scale");
+  if (nvfp4 && !c->recur_state)
+    return fail(SSU_ERR_UNSUPPORTED, "an nvfp4 read checkpoint requires recur_state (separate checkpoints)");
+  if (c->recur_state && c->state_dtype != SSU_FP8_E4M3 && !nvfp4)
+    return fail(SSU_ERR_UNSUPPORTED, "recur_state (separate checkpoints) requires an fp8 or nvfp4 state");
+  if (c->state_head_scale && !aligned16(c->state_head_scale))
+    return fail(SSU_ERR_INVALID, "state_head_scale must be 16-byte aligned");
   if (c->recur_state && !aligned16(c->recur_state))
     return fail(SSU_ERR_INVALID, "recur_state must be 16-byte aligned");
   if (!aligned16(c->state) || !aligned16(c->x_cache) || !aligned16(c->B_cache) || !aligned16(c->dt_cache) ||
@@ -87,14 +98,16 @@ int check_cache(const ssu_cache *c) {
       (c->status && !aligned4(c->status)))
     return fail(SSU_ERR_INVALID, "cache pointers must be 16-byte aligned (ring_start, status: 4-byte)");
   const int64_t H = c->nheads, G = c->ngroups, L = c->ring_len;
-  const int64_t need_state = H * ssu::kHeadDim * ssu::kDState * state_elem_bytes(c->state_dtype);
+  const int64_t need_state = H * state_head_bytes(c->state_dtype);
   struct {
     const char *name;
     int64_t stride, need;
     bool used;
   } s[] = {
       {"state", c->state_slot_stride, need_state, true},
-      {"state_scale", c->scale_slot_stride, H * ssu::kHeadDim * 4, c->state_dtype == SSU_FP8_E4M3},
+      {"state_scale", c->scale_slot_stride, nvfp4 ? H * ssu::kHeadDim * ssu::kDState / 16 : H * ssu::kHeadDim * 4,
+       c->state_dtype == SSU_FP8_E4M3 || nvfp4},
+      {"state_head_scale", c->head_scale_slot_stride, H * 4, nvfp4},
       {"x_cache", c->x_slot_stride, H * L * ssu::kHeadDim * 2, true},
       {"B_cache", c->B_slot_stride, G * L * ssu::kDState * 2, true},
       {"dt_cache", c->dt_slot_stride, H * L * 4, true},
@@ -135,6 +148,8 @@ ssu::KCache kcache(const ssu_cache *c, uint64_t seed) {
   k.recur_stride = c->recur_slot_stride;
   k.seed_lo = (uint32_t)seed;
   k.seed_hi = (uint32_t)(seed >> 32);
+  k.hscale = reinterpret_cast<uint8_t *>(c->state_head_scale);
+  k.hscale_stride = c->head_scale_slot_stride;
   return k;
 }
 

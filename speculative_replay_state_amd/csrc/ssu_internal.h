@@ -18,7 +18,7 @@ constexpr int kMaxRing = 32;   // L <= 32: the combined window fits one 32-deep 
 constexpr int kMaxTokens = 16; // T <= 16: new tokens are the 16 columns of the readout MFMA
 constexpr int kCbStride = 32;  // floats per (entry, group, token) row of the split scratch
 
-enum StateType { kF32 = 0, kBF16 = 1, kF16 = 2, kFP8 = 3 };
+enum StateType { kF32 = 0, kBF16 = 1, kF16 = 2, kFP8 = 3, kNVFP4 = 4 };
 enum OutType { kOutF32 = 0, kOutBF16 = 1 };
 
 // Cache description as the kernels see it (byte strides between slots).
@@ -39,6 +39,8 @@ struct KCache {
   uint8_t *recur;        // NULL, or the FP16 recurrence checkpoint (separate checkpoints)
   int64_t recur_stride;
   uint32_t seed_lo, seed_hi;  // this call's stochastic-rounding seed
+  uint8_t *hscale;       // nvfp4: the f32 second-level scale of each head
+  int64_t hscale_stride;
 };
 
 // One replay step.

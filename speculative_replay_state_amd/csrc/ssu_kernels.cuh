@@ -135,6 +135,20 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
   return r;
 }
 
+// 8 e2m1 codes (one dword, value 2 i in the low nibble of byte i) times the
+// block scale s -> 8 bf16, exact: an e2m1 value has at most 2 significant
+// bits and an e4m3 value 4.  The conversion's own scale operand applies a
+// power of two only, so it gets 1 and s is multiplied in fp32.
+__device__ __forceinline__ bf16x8 nvfp4_word_to_bf16(uint32_t w, float s) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  const u32x4 r = {pack_bf16(a[0] * s, a[1] * s), pack_bf16(b[0] * s, b[1] * s), pack_bf16(c[0] * s, c[1] * s),
+                   pack_bf16(d[0] * s, d[1] * s)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // fp8 row scale: max|h| / 448, 1 when that is not positive (zero row).
 __device__ __forceinline__ float fp8_row_scale(float m) {
   float sc = m / 448.0f;
@@ -149,6 +163,14 @@ __device__ __forceinline__ float fp8_row_scale(float m) {
 // contiguous that is directly the lanes' MFMA operand.
 __device__ __forceinline__ int tile_chunk(int rb, int u, int lane, int eb) {
   return rb * 2048 * eb + (u * 64 + lane) * 16;
+}
+
+// 16-byte chunks per lane per row block (32 values) and bytes per head of a
+// state type: fp32 8, bf16 / fp16 4, fp8 2, nvfp4 1 (two e2m1 codes a byte).
+constexpr int st_chunks(int ST) { return ST == kF32 ? 8 : (ST == kFP8 ? 2 : (ST == kNVFP4 ? 1 : 4)); }
+constexpr int st_head_bytes(int ST) { return st_chunks(ST) * 4096; }
+__device__ __forceinline__ int tile_off(int rb, int u, int lane, int chunks) {
+  return (rb * chunks + u) * 1024 + lane * 16;
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs; remap so that runs of
@@ -605,9 +627,9 @@ __device__ __forceinline__ void encode_quarter(const f32x4 *acc, float sc, float
 
 template <int ST>
 __device__ __forceinline__ void store_chunks(uint8_t *hp, int rb, int lane, const u32x4 *ch) {
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
+  constexpr int kC = st_chunks(ST);
 #pragma unroll
-  for (int u = 0; u < 2 * kEB; ++u) st16_nt(hp + tile_chunk(rb, u, lane, kEB), ch[u]);
+  for (int u = 0; u < kC; ++u) st16_nt(hp + tile_off(rb, u, lane, kC), ch[u]);
 }
 
 // ---------------------------------------------------------------------------
@@ -874,6 +896,110 @@ __device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW> &fo, co
   return sc;
 }
 
+// NVFP4 encoding of a quarter row block: the lane's 32 values (two blocks of
+// 16) times y0 (block t < 16) or y1 (t >= 16), as e2m1 codes, value 2 i in the
+// low nibble of byte i.  The conversion rounds to nearest even and saturates
+// at 6; its scale operand (a power of two) gets 1.
+__device__ __forceinline__ u32x4 nvfp4_encode_quarter(const f32x4 *acc, float y0, float y1) {
+  u32x4 cw;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // values t = 8 w .. 8 w + 7
+    const float y = w < 2 ? y0 : y1;
+    uint32_t word = 0;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, QV(acc, 8 * w + 0) * y, QV(acc, 8 * w + 1) * y, 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, QV(acc, 8 * w + 2) * y, QV(acc, 8 * w + 3) * y, 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, QV(acc, 8 * w + 4) * y, QV(acc, 8 * w + 5) * y, 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, QV(acc, 8 * w + 6) * y, QV(acc, 8 * w + 7) * y, 1.0f, 3);
+    cw[w] = word;
+  }
+  return cw;
+}
+
+// The lane's maxima |v| of its two blocks of 16 in a row block.
+__device__ __forceinline__ f32x2 block_max2(const f32x4 *acc) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    a = max3_abs(a, acc[nb][0], acc[nb][1]);  // values t < 16
+    b = max3_abs(b, acc[nb][2], acc[nb][3]);  // values t >= 16
+  }
+  return f32x2{a, b};
+}
+
+// The NVFP4 scales from the lane's eight block maxima bm (row blocks 0..3,
+// two each): the head maximum over the wave gives g = fp32(m / 2688) (1 if
+// not positive); block i gets the e4m3 code of fp32(bm[i] / fp32(6 g))
+// (nearest, saturating at 448) in byte i of sfw, and y[i] = fp32(1 / (e4m3
+// value * g)), 0 for a zero block scale (its values encode as signed zeros).
+__device__ __forceinline__ float wave_max(float v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = fmaxf(v, lane_xor(v, lane, d));
+  return v;
+}
+__device__ __forceinline__ float nvfp4_gscale(float head_max) {
+  const float g = head_max / 2688.0f;
+  return g > 0.0f ? g : 1.0f;
+}
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float &y) {
+  const float t = fminf(a / (6.0f * g), 448.0f);
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xFFu;
+  const float es = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0] * g;
+  y = es > 0.0f ? 1.0f / es : 0.0f;
+  return code;
+}
+__device__ __forceinline__ void nvfp4_scales(const float *bm, int lane, float &g, u32x2 &sfw, float *y) {
+  float mx = bm[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, bm[i]);
+  g = nvfp4_gscale(wave_max(mx, lane));
+  uint32_t sb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sb[i] = nvfp4_block_scale(bm[i], g, y[i]);
+  sfw = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24), sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
+}
+
+// Separate checkpoints with an NVFP4 read checkpoint: fold the FP16
+// recurrence tile rch.  The scales need the whole head's maximum, so the fold
+// runs twice: pass 1 keeps the block maxima, pass 2 (the same instructions on
+// the same operands, hence the same values) writes the new recurrence chunks
+// over rch (stochastic rounding) and the e2m1 codes into codes.
+template <int KW>
+__device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW> &fo, const uint16_t *xT, int lane,
+                                                const KCache &c, int slot, int head, u32x4 (*rch)[4],
+                                                u32x4 (*codes)[1], u32x2 &sfw, float &g) {
+  const int m = lane & 15, q = lane >> 4;
+  float bm[8];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc[8];
+    decode_quarter<kF16>(rch[rb], fo.D0, acc);
+    fold_update<kNVFP4, KW>(fo, xT, rb, lane, acc);
+    const f32x2 b2 = block_max2(acc);
+    bm[2 * rb] = b2[0];
+    bm[2 * rb + 1] = b2[1];
+  }
+  float y[8];
+  nvfp4_scales(bm, lane, g, sfw, y);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc[8];
+    decode_quarter<kF16>(rch[rb], fo.D0, acc);
+    fold_update<kNVFP4, KW>(fo, xT, rb, lane, acc);
+    encode_quarter_sr(acc, c, slot, head, 16 * rb + m, q, rch[rb]);
+    codes[rb][0] = nvfp4_encode_quarter(acc, y[2 * rb], y[2 * rb + 1]);
+  }
+}
+
+// Stores an NVFP4 tile with its block and head scales.
+__device__ __forceinline__ void store_nvfp4(const KCache &c, int slot, int h, int lane, const u32x4 (*codes)[1],
+                                            u32x2 sfw, float g) {
+  uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(kNVFP4);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) store_chunks<kNVFP4>(hp, rb, lane, codes[rb]);
+  st8(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) + lane * 8, sfw);
+  if (lane == 0) *reinterpret_cast<float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4) = g;
+}
+
 // ---------------------------------------------------------------------------
 // The replay of one (entry, head) by one wave, in two phases so that a wave
 // can have the next head's loads in flight while this one computes:
@@ -887,11 +1013,12 @@ __device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW> &fo, co
 // the bytes), the dt and x windows, and the fp8 row scales.
 template <int ST, int KW>
 struct HeadLoads {
-  static constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  static constexpr int kNLD = 2 * kEB;  // 16-byte chunks per lane per 16-row block
+  static constexpr int kNLD = st_chunks(ST);  // 16-byte chunks per lane per 16-row block
   u32x4 raw[4][kNLD];                   // lane l = 16 q + m: chunk u of quarter q of row 16 rb + m
   u32x4 xw[Win<KW>::kRounds];                // x window chunks
   f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
+  u32x2 sfw;                                 // nvfp4: the lane's 8 block scales (rb 0..3, 2 each)
+  float gs;                                  // nvfp4: the head's second-level scale
   float dtv;                                 // lane s: stored dt' (s < pnat) or raw dt (new)
   float dtb, Ah, Dh;                         // dt_bias[h], A[h], D[h]
   u32x4 zw[2];                               // output gate chunks (gated variant only)
@@ -910,11 +1037,15 @@ struct ItemLoads {
 template <int ST, int KW>
 __device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int lane, HeadLoads<ST, KW> &ld) {
   using T = HeadLoads<ST, KW>;
-  const uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * T::kEB);
+  const uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(ST);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, T::kEB));
+    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_off(rb, u, lane, T::kNLD));
+  if constexpr (ST == kNVFP4) {  // the block scales and the head scale belong to the tile
+    ld.sfw = ld8(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) + lane * 8);
+    ld.gs = *reinterpret_cast<const float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4);
+  }
 }
 
 // The readout window of (entry, h): dt in lane s (ring dt' or raw dt), the
@@ -979,7 +1110,7 @@ __device__ __forceinline__ void load_item_c(const KCache &c, const KStep &s, con
   // k step kk of the readout takes values t = 8 kk .. 8 kk + 7 of the lane's
   // quarter q, i.e. n = 32 q + 8 kk + e (fp32 tile: k step t, n = 32 q + t).
   const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState + 32 * q;
-  if constexpr (ST == kBF16 || ST == kFP8) {
+  if constexpr (ST == kBF16 || ST == kFP8 || ST == kNVFP4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) il.craw[u] = tok_ok ? ld16(Crow + 8 * u) : zero4;
   } else if constexpr (ST == kF16) {
@@ -1084,6 +1215,13 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         a = mfma_f16(__builtin_bit_cast(f16x8, ld.raw[rb][u]), __builtin_bit_cast(f16x8, il.craw[u]), a);
+    } else if constexpr (ST == kNVFP4) {
+      const f32x2 sfv = (rb & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(ld.sfw[rb >> 1], true)
+                                 : __builtin_amdgcn_cvt_pk_f32_fp8(ld.sfw[rb >> 1], false);  // blocks t < 16, t >= 16
+#pragma unroll
+      for (int w = 0; w < 4; ++w)  // k step w: values t = 8 w .. 8 w + 7
+        a = mfma_bf16(nvfp4_word_to_bf16(ld.raw[rb][0][w], w < 2 ? sfv[0] : sfv[1]),
+                      __builtin_bit_cast(bf16x8, il.craw[w]), a);
     } else if constexpr (ST == kFP8) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1110,6 +1248,8 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
     for (int j = 0; j < 4; ++j) {
       if constexpr (ST == kFP8)
         acc[rb][j] = (acc[rb][j] * ld.rscale[rb][j]) * beta;
+      else if constexpr (ST == kNVFP4)
+        acc[rb][j] = (acc[rb][j] * ld.gs) * beta;
       else
         acc[rb][j] = acc[rb][j] * beta;
     }
@@ -1235,8 +1375,8 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
                                                             int htiles) {
   using WC = Win<KW>;
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  constexpr int kNLD = 2 * kEB;
+  constexpr int kNLD = st_chunks(ST);
+  static_assert(ST != kNVFP4 || SEP, "an nvfp4 read checkpoint needs the recurrence checkpoint");
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
@@ -1256,7 +1396,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   }
   const int m = lane & 15, q = lane >> 4;
   uint16_t *xT = xT_all[wave];
-  uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
+  uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(ST);
 
   // 1. loads, issued before any arithmetic (fp32: the checkpoint per row
   //    block, below)
@@ -1272,7 +1412,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int u = 0; u < kNLD; ++u) raw[rb][u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
+      for (int u = 0; u < kNLD; ++u) raw[rb][u] = ld16_nt(hp + tile_off(rb, u, lane, kNLD));
   }
   FoldHeadLoads<ST, KW> fl;
   FoldBLoads<KW> fb;
@@ -1284,6 +1424,15 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   fold_setup<ST, KW>(A[h], k, fl, fb, xT, lane, fo);
   wave_sync();  // xT written by this wave -> read below
 
+  if constexpr (ST == kNVFP4) {  // the whole head at once: its scales need the head's maximum
+    u32x4 codes[4][1];
+    u32x2 sfw;
+    float g;
+    fold_head_nvfp4<KW>(fo, xT, lane, c, slot, h, rraw, codes, sfw, g);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) store_chunks<kF16>(rp, rb, lane, rraw[rb]);
+    store_nvfp4(c, slot, h, lane, codes, sfw, g);
+  } else {
   // 3. row block by row block: decode and decay, rank-k update, encode, store
   float scs[4];
 #pragma unroll
@@ -1296,7 +1445,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 #pragma unroll
       for (int u = 0; u < kNLD; ++u) {
         if constexpr (ST == kF32)
-          ch[u] = ld16_nt(hp + tile_chunk(rb, u, lane, kEB));
+          ch[u] = ld16_nt(hp + tile_off(rb, u, lane, kNLD));
         else
           ch[u] = raw[rb][u];
       }
@@ -1307,6 +1456,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   // new row scales: lane l holds row l's (row 16 q + m is in rb = q)
   if constexpr (ST == kFP8)
     (reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(scs[0], scs[1], scs[2], scs[3], q);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1333,7 +1483,6 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
   constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
   __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.x / htiles;
   const int h = (blockIdx.x - b * htiles) * kHeadWaves + wave;
@@ -1383,12 +1532,16 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     FoldOps<ST, KW> fo;
     fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, lane, fo);
     wave_sync();  // xT written by this wave -> read below
+    if constexpr (ST == kNVFP4) {
+      fold_head_nvfp4<KW>(fo, xT, lane, c, e.slot, h, rraw, ld.raw, ld.sfw, ld.gs);
+    } else {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if constexpr (SEP)
-        fl.osc[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, e.slot, h, rraw[rb], ld.raw[rb]);
-      else
-        fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+      for (int rb = 0; rb < 4; ++rb) {
+        if constexpr (SEP)
+          fl.osc[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, e.slot, h, rraw[rb], ld.raw[rb]);
+        else
+          fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+      }
     }
     wave_sync();  // the fold's xT reads done before the readout rewrites xT
   }
@@ -1402,9 +1555,13 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   CbLoads<KW> cl;
   load_cb<KW>(c, s, e, g, lane, cl);
   if (e.k > 0) {
-    uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
+    if constexpr (ST == kNVFP4) {
+      store_nvfp4(c, e.slot, h, lane, ld.raw, ld.sfw, ld.gs);
+    } else {
+      uint8_t *hp = c.state + (int64_t)e.slot * c.state_stride + (int64_t)h * st_head_bytes(ST);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) store_chunks<ST>(hp, rb, lane, ld.raw[rb]);
+      for (int rb = 0; rb < 4; ++rb) store_chunks<ST>(hp, rb, lane, ld.raw[rb]);
+    }
     if constexpr (SEP) {
       uint8_t *rp = c.recur + (int64_t)e.slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
 #pragma unroll
@@ -1472,8 +1629,7 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
   const int slot = slot_idx[j];
   if (slot <= 0 || slot >= c.num_slots) return;
   const int rb = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
-  constexpr int kEB = ST == kF32 ? 4 : (ST == kFP8 ? 1 : 2);
-  uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * (kHeadElems * kEB);
+  uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(ST);
   const float *src = states + (int64_t)j * states_stride + (int64_t)h * kHeadElems +
                      (16 * rb + m) * kDState + 32 * q;
   f32x4 acc[8];
@@ -1483,18 +1639,35 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
 #pragma unroll
     for (int e = 0; e < 4; ++e) QV(acc, 4 * u + e) = a[e];
   }
-  float sc = 1.f, y = 1.f;
-  bool fast = true;
-  if constexpr (ST == kFP8) {
-    sc = fp8_row_scale(quarter_row_max(acc));
-    y = 1.0f / sc;
-    fast = __all(scale_fast(sc));
-    if (q == 0) reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + 16 * rb + m] = sc;
+  if constexpr (ST == kNVFP4) {
+    // the head's maximum over the four waves (one row block each)
+    __shared__ float wmax[kWaves];
+    const f32x2 b2 = block_max2(acc);
+    const float mx = wave_max(fmaxf(b2[0], b2[1]), lane);
+    if (lane == 0) wmax[rb] = mx;
+    __syncthreads();
+    const float g = nvfp4_gscale(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    float y0, y1;
+    const uint32_t s0 = nvfp4_block_scale(b2[0], g, y0), s1 = nvfp4_block_scale(b2[1], g, y1);
+    u32x4 ch[1] = {nvfp4_encode_quarter(acc, y0, y1)};
+    store_chunks<ST>(hp, rb, lane, ch);
+    *reinterpret_cast<uint16_t *>(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) +
+                                  lane * 8 + rb * 2) = (uint16_t)(s0 | (s1 << 8));
+    if (threadIdx.x == 0) *reinterpret_cast<float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4) = g;
+  } else {
+    float sc = 1.f, y = 1.f;
+    bool fast = true;
+    if constexpr (ST == kFP8) {
+      sc = fp8_row_scale(quarter_row_max(acc));
+      y = 1.0f / sc;
+      fast = __all(scale_fast(sc));
+      if (q == 0) reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride)[h * kHeadDim + 16 * rb + m] = sc;
+    }
+    u32x4 ch[st_chunks(ST)];
+    encode_quarter<ST>(acc, sc, y, fast, ch);
+    store_chunks<ST>(hp, rb, lane, ch);
   }
-  u32x4 ch[2 * kEB];
-  encode_quarter<ST>(acc, sc, y, fast, ch);
-  store_chunks<ST>(hp, rb, lane, ch);
-  if constexpr (ST == kFP8) {
+  if constexpr (ST == kFP8 || ST == kNVFP4) {
     if (c.recur) {  // separate checkpoints: the FP16 recurrence one, stochastically rounded
       u32x4 rch[4];
       encode_quarter_sr(acc, c, slot, h, 16 * rb + m, q, rch);
@@ -1585,10 +1758,14 @@ hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
 // rejects recur_state with any other state type).
 template <int ST, int OT, bool HAS_Z>
 hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
-  if constexpr (ST == kFP8) {
-    if (c.recur) return fused_zs<ST, OT, HAS_Z, true>(c, s, st);
+  if constexpr (ST == kNVFP4) {  // an nvfp4 read checkpoint always comes with the recurrence checkpoint
+    return fused_zs<ST, OT, HAS_Z, true>(c, s, st);
+  } else {
+    if constexpr (ST == kFP8) {
+      if (c.recur) return fused_zs<ST, OT, HAS_Z, true>(c, s, st);
+    }
+    return fused_zs<ST, OT, HAS_Z, false>(c, s, st);
   }
-  return fused_zs<ST, OT, HAS_Z, false>(c, s, st);
 }
 
 template <int ST, int OT, bool SPLIT, bool HAS_Z>
@@ -1614,20 +1791,22 @@ hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_
                    int n, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
   const dim3 grid((unsigned)((int64_t)n * htiles)), block(kHeadWaves * 64);
-  bool sep = false;
+  bool sep = ST == kNVFP4;
   if constexpr (ST == kFP8) sep = c.recur != nullptr;
   if (sep) {
-    if constexpr (ST == kFP8) {
+    if constexpr (ST == kFP8 || ST == kNVFP4) {
       if (c.L <= 16)
         flush_kernel<ST, 16, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
       else
         flush_kernel<ST, 32, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
     }
   } else {
-    if (c.L <= 16)
-      flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
-    else
-      flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+    if constexpr (ST != kNVFP4) {
+      if (c.L <= 16)
+        flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+      else
+        flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -1,5 +1,5 @@
 // One state type's kernels and launchers (SSU_INST_ST = 0 fp32, 1 bf16,
-// 2 fp16, 3 fp8 e4m3): the build compiles this file once per state type.
+// 2 fp16, 3 fp8 e4m3, 4 nvfp4): the build compiles this file once per state type.
 #include "ssu_kernels.cuh"
 
 #ifndef SSU_INST_ST

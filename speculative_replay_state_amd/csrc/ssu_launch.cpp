@@ -10,6 +10,7 @@ namespace ssu {
     case kBF16: return FN<kBF16>(__VA_ARGS__);         \
     case kF16: return FN<kF16>(__VA_ARGS__);           \
     case kFP8: return FN<kFP8>(__VA_ARGS__);           \
+    case kNVFP4: return FN<kNVFP4>(__VA_ARGS__);       \
     default: return hipErrorInvalidValue;              \
   }
 

@@ -16,7 +16,7 @@ def device_cache(spec: synth.CacheSpec, t: dict, with_status: bool = True) -> ss
     status = torch.zeros(1, dtype=torch.int32, device=DEV) if with_status else None
     return ssu.DeviceCache(spec.num_slots, spec.nheads, spec.ngroups, spec.ring_len, spec.state_dtype,
                            t["state"], t["scale"], t["x_cache"], t["B_cache"], t["dt_cache"],
-                           t["ring_start"], status, spec.headdim, spec.dstate, t.get("recur"))
+                           t["ring_start"], status, spec.headdim, spec.dstate, t.get("recur"), t.get("gscale"))
 
 
 def out_tensor(step: synth.StepInputs, spec, out_dtype: str):
