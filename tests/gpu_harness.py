@@ -123,7 +123,10 @@ def check_state(spec, gpu, ref, before, touched, fold=None):
     fp8 codes >= 99.9 % equal and otherwise one code apart; fp8 row scales
     within what the fold error moves the row maximum (fold = (slots, k, A) of
     the fold from `before`; without it 1e-5 relative); other dtypes within
-    their relative bounds."""
+    their relative bounds; nvfp4 as check_nvfp4."""
+    if spec.state_dtype == "nvfp4":
+        assert fold is not None
+        return check_nvfp4(spec, gpu, ref, before, touched, fold)
     untouched = [s for s in range(spec.num_slots) if s not in touched]
     assert np.array_equal(gpu.state[untouched], before.state[untouched])
     assert np.array_equal(gpu.state[:, spec.state_bytes():], before.state[:, spec.state_bytes():])
@@ -180,3 +183,97 @@ def bf16_bits_to_f64(bits):
 def _decode_state(cache, slot):
     from oracle import ssu_oracle as O
     return O.decode_state(cache, slot)
+
+
+def _f16_ordinal(bits):
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_recur(spec, gpu, before, slots, k, A, seed, min_equal=0.98, bits_slot=None):
+    """Recurrence checkpoints after a fold of k tokens from `before`:
+    untouched slots and slot padding bit for bit, folded ones bracketed by
+    stochastic rounding of the exact fold +- the fp32 error bound.  The
+    random bits of cache slot s are those of slot bits_slot[s] (the slot the
+    GPU saw, when `before` is a renumbered subset)."""
+    from oracle import ssu_oracle as O
+    touched = sorted({int(sl) for sl, kk in zip(slots, k) if kk > 0 and 0 < sl < spec.num_slots})
+    untouched = [sl for sl in range(spec.num_slots) if sl not in touched]
+    assert np.array_equal(gpu.recur[untouched], before.recur[untouched])
+    nb = spec.recur_bytes()
+    assert np.array_equal(gpu.recur[:, nb:], before.recur[:, nb:])  # slot padding
+    if not touched:
+        return
+    v_ref = f64_fold(spec, before, slots, k, A, absolute=False)
+    s_abs = f64_fold(spec, before, slots, k, A, absolute=True)
+    P, N = spec.headdim, spec.dstate
+    equal = total = 0
+    for sl in touched:
+        bs = sl if bits_slot is None else bits_slot[sl]
+        u = np.stack([O.sr_bits(seed, bs, h, P * N).reshape(P, N) for h in range(spec.nheads)])
+        v, S = v_ref[sl], s_abs[sl]
+        E = FOLD_REL * S + 2.0 ** -23 * np.abs(v)
+        lo = _f16_ordinal(O.sr_f16(v - E, u))
+        hi = _f16_ordinal(O.sr_f16(v + E, u))
+        g = _f16_ordinal(gpu.recur_logical(sl))
+        bad = (g < lo) | (g > hi)
+        assert not bad.any(), "slot %d: %d values outside the bracket, first at %s" % (
+            sl, int(bad.sum()), np.argwhere(bad)[0])
+        equal += int((g == _f16_ordinal(O.sr_f16(v, u))).sum())
+        total += g.size
+    assert equal >= min_equal * total, equal / total
+
+
+
+
+def _e4m3(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def block_scale_values(cache, slot):
+    """The e4m3 block-scale values of one slot as [H, P, N / 16], read with
+    the tiled layout (lane l = 16 q + m of row 16 rb + m: byte l * 8 + rb * 2
+    + j for the block of values 32 q + 16 j .. + 15)."""
+    raw = cache.scale_view(slot)  # [H, 512] bytes in storage order
+    p = np.arange(64)[:, None]
+    blk = np.arange(8)[None, :]
+    rb, m, q, j = p // 16, p % 16, blk // 2, blk % 2
+    idx = (16 * q + m) * 8 + rb * 2 + j
+    return _e4m3(raw[:, idx])
+
+
+def check_nvfp4(spec, gpu, ref, before, touched, fold, min_equal=0.995):
+    """NVFP4 read checkpoints after a fold of `fold` = (slots, k, A) from
+    `before`: untouched slots bit for bit; head scales within the fold bound;
+    every decoded value within one element step of the GPU's own grid plus
+    the fold bound of the exact fold; codes and block scales mostly equal to
+    the oracle's (a head scale one ulp apart moves every value by an ulp while
+    leaving the encoding alone)."""
+    from oracle import ssu_oracle as O
+    untouched = [s for s in range(spec.num_slots) if s not in touched]
+    for f in ("state", "scale", "gscale"):
+        assert np.array_equal(getattr(gpu, f)[untouched], getattr(before, f)[untouched]), f
+    v_ex = f64_fold(spec, before, *fold, absolute=False)
+    s_abs = f64_fold(spec, before, *fold, absolute=True)
+    equal = total = sf_equal = sf_total = 0
+    for sl in touched:
+        gg, gr = gpu.gscale_view(sl).astype(np.float64), ref.gscale_view(sl).astype(np.float64)
+        smax = s_abs[sl].reshape(spec.nheads, -1).max(axis=1)
+        assert np.all(np.abs(gg - gr) <= FOLD_REL * smax / 2688.0 + 2.0 ** -22 * gr), (sl, gg, gr)
+        dec_g, dec_r = O.decode_state(gpu, sl), O.decode_state(ref, sl)
+        es = block_scale_values(gpu, sl) * gg[:, None, None]  # [H, P, 8]
+        es = np.where(es == 0, 6.0 * gg[:, None, None] * 2.0 ** -10, es)
+        bound = np.repeat(es, 16, axis=2) + FOLD_REL * s_abs[sl] + 1e-30
+        over = np.abs(dec_g - v_ex[sl]) - bound
+        assert np.all(over <= 0), (sl, float(np.max(over)))
+        # codes and block scales, not values: a head scale one ulp apart
+        # changes every value by an ulp while leaving the encoding alone
+        cg, cr = gpu.state_view(sl), ref.state_view(sl)
+        equal += int(((cg & 15) == (cr & 15)).sum() + ((cg >> 4) == (cr >> 4)).sum())
+        total += 2 * cg.size
+        sf_equal += int((gpu.scale_view(sl) == ref.scale_view(sl)).sum())
+        sf_total += gpu.scale_view(sl).size
+    assert equal >= min_equal * total, equal / total
+    assert sf_equal >= min_equal * sf_total, sf_equal / sf_total

@@ -37,11 +37,17 @@ FULL = {
     "prod_b512": dict(nheads=128, ngroups=8, state="f16", batch=512, slots=1025, T=8, pnat_max=8, out="bf16"),
     "fp8_b256": dict(nheads=128, ngroups=8, state="fp8", batch=256, slots=513, T=4, pnat_max=0, out="bf16",
                      flush=(1, 4)),
+    # separate checkpoints: an FP16 recurrence checkpoint beside the read checkpoint
+    "fp8sep_b256": dict(nheads=128, ngroups=8, state="fp8", batch=256, slots=513, T=4, pnat_max=0, out="bf16",
+                        flush=(1, 4), sep=True),
+    "nvfp4_b256": dict(nheads=128, ngroups=8, state="nvfp4", batch=256, slots=513, T=4, pnat_max=0,
+                       out="bf16", flush=(1, 4), sep=True),
     "large_b1024": dict(nheads=128, ngroups=8, state="bf16", batch=1024, slots=2048, T=8, pnat_max=8,
                         out="bf16", varlen=True, pad=256),
 }
 RUNS = [("tiny_b2", "monolith"), ("mtp_b64", "monolith"), ("mtp_b64", "split"), ("prod_b256", "monolith"),
         ("prod_b256", "split"), ("prod_b512", "monolith"), ("fp8_b256", "fused"), ("fp8_b256", "separate"),
+        ("fp8sep_b256", "fused"), ("nvfp4_b256", "fused"), ("nvfp4_b256", "separate"),
         ("large_b1024", "monolith")]
 
 
@@ -51,7 +57,8 @@ def test_full_size_sampled(name, algo):
     seed = 9000 + len(name) * 7 + len(algo)
     print("case", name, algo, flush=True)
     spec = synth.CacheSpec(num_slots=cfg["slots"], nheads=cfg["nheads"], ngroups=cfg["ngroups"],
-                           state_dtype=cfg["state"], slot_pad=cfg.get("pad", 0))
+                           state_dtype=cfg["state"], slot_pad=cfg.get("pad", 0), separate=cfg.get("sep", False))
+    sr_seed = 0x5A5A0000 + seed
     t = sd.make_cache_device(spec, seed, gh.DEV)
     rng = np.random.default_rng(seed)
     B = cfg["batch"]
@@ -74,12 +81,12 @@ def test_full_size_sampled(name, algo):
     if algo == "fused":
         desc = ssu.make_step_desc(B, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"], st["B"],
                                   st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, cfg["out"], None,
-                                  "auto", num_fold=kt)
+                                  "auto", num_fold=kt, sr_seed=sr_seed)
         ssu.replay_step(dc, desc)
     else:
         gh.run_step(dc, st, step, out, cfg["out"], "split" if algo == "split" else "monolith")
         if algo == "separate":
-            ssu.flush(dc, st["slot_idx"], kt, st["A"])
+            ssu.flush(dc, st["slot_idx"], kt, st["A"], sr_seed=sr_seed)
     torch.cuda.synchronize()
     assert int(dc.status.item()) == 0
     after, _ = sd.download_subset(spec, t, [int(slots[b]) for b in sample])
@@ -87,12 +94,12 @@ def test_full_size_sampled(name, algo):
     ref_cache = before.copy()
     ks = None if k is None else k[sample].astype(np.int32)
     if algo == "fused":
-        ref, status = O.replay_step(ref_cache, sub, num_fold=ks)
+        ref, status = O.replay_step(ref_cache, sub, num_fold=ks, seed=sr_seed)
     else:
         ref, status = O.replay_step(ref_cache, sub)
         if algo == "separate":
             mid = ref_cache.copy()  # the state the flush folds from (the step leaves checkpoints alone)
-            assert O.flush(ref_cache, sub.slot_idx, ks, sub.A) == 0
+            assert O.flush(ref_cache, sub.slot_idx, ks, sub.A, sr_seed) == 0
     assert status == 0
 
     rows = []
@@ -117,4 +124,8 @@ def test_full_size_sampled(name, algo):
     assert gh.rel_err(g, r) <= 1e-6
     touched = [i + 1 for i, b in enumerate(sample) if k is not None and k[b] > 0]
     fold = None if ks is None else (sub.slot_idx, ks, sub.A)
-    gh.check_state(after.spec, after, ref_cache, mid if algo == "separate" else before, touched, fold)
+    src = mid if algo == "separate" else before
+    gh.check_state(after.spec, after, ref_cache, src, touched, fold)
+    if spec.separate:  # the recurrence checkpoints, with the random bits of the slots the GPU folded
+        bits_slot = {i + 1: int(slots[b]) for i, b in enumerate(sample)}
+        gh.check_recur(after.spec, after, src, *fold, sr_seed, bits_slot=bits_slot)

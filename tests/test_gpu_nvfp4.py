@@ -27,7 +27,6 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from tests import gpu_harness as gh
-    from tests.test_gpu_separate import _check_recur
     import speculative_replay_state_amd as ssu
 from oracle import ssu_oracle as O
 
@@ -36,52 +35,6 @@ from oracle import ssu_oracle as O
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def _e4m3(codes):
-    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
-    return t.to(torch.float64).numpy()
-
-
-def block_scale_values(cache, slot):
-    """The e4m3 block-scale values of one slot as [H, P, N / 16], read with
-    the tiled layout (lane l = 16 q + m of row 16 rb + m: byte l * 8 + rb * 2
-    + j for the block of values 32 q + 16 j .. + 15)."""
-    raw = cache.scale_view(slot)  # [H, 512] bytes in storage order
-    p = np.arange(64)[:, None]
-    blk = np.arange(8)[None, :]
-    rb, m, q, j = p // 16, p % 16, blk // 2, blk % 2
-    idx = (16 * q + m) * 8 + rb * 2 + j
-    return _e4m3(raw[:, idx])
-
-
-def check_nvfp4(spec, gpu, ref, before, touched, fold, min_equal=0.995):
-    """Read checkpoints after a fold of `fold` = (slots, k, A) from `before`."""
-    untouched = [s for s in range(spec.num_slots) if s not in touched]
-    for f in ("state", "scale", "gscale"):
-        assert np.array_equal(getattr(gpu, f)[untouched], getattr(before, f)[untouched]), f
-    v_ex = gh.f64_fold(spec, before, *fold, absolute=False)
-    s_abs = gh.f64_fold(spec, before, *fold, absolute=True)
-    equal = total = sf_equal = sf_total = 0
-    for sl in touched:
-        gg, gr = gpu.gscale_view(sl).astype(np.float64), ref.gscale_view(sl).astype(np.float64)
-        smax = s_abs[sl].reshape(spec.nheads, -1).max(axis=1)
-        assert np.all(np.abs(gg - gr) <= gh.FOLD_REL * smax / 2688.0 + 2.0 ** -22 * gr), (sl, gg, gr)
-        dec_g, dec_r = O.decode_state(gpu, sl), O.decode_state(ref, sl)
-        es = block_scale_values(gpu, sl) * gg[:, None, None]  # [H, P, 8]
-        es = np.where(es == 0, 6.0 * gg[:, None, None] * 2.0 ** -10, es)
-        bound = np.repeat(es, 16, axis=2) + gh.FOLD_REL * s_abs[sl] + 1e-30
-        over = np.abs(dec_g - v_ex[sl]) - bound
-        assert np.all(over <= 0), (sl, float(np.max(over)))
-        # codes and block scales, not values: a head scale one ulp apart
-        # changes every value by an ulp while leaving the encoding alone
-        cg, cr = gpu.state_view(sl), ref.state_view(sl)
-        equal += int(((cg & 15) == (cr & 15)).sum() + ((cg >> 4) == (cr >> 4)).sum())
-        total += 2 * cg.size
-        sf_equal += int((gpu.scale_view(sl) == ref.scale_view(sl)).sum())
-        sf_total += gpu.scale_view(sl).size
-    assert equal >= min_equal * total, equal / total
-    assert sf_equal >= min_equal * sf_total, sf_equal / sf_total
 
 
 def _spec(ring_len=16, num_slots=40, nheads=32, ngroups=4):
@@ -161,8 +114,8 @@ def test_nvfp4_flush_parity(ring_len):
     gpu = sd.download_cache(spec, t)
     assert np.array_equal(gpu.ring_start, ref.ring_start)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0})
-    check_nvfp4(spec, gpu, ref, before, touched, (step.slot_idx, k, step.A))
-    _check_recur(spec, gpu, before, step.slot_idx, k, step.A, seed)
+    gh.check_nvfp4(spec, gpu, ref, before, touched, (step.slot_idx, k, step.A))
+    gh.check_recur(spec, gpu, before, step.slot_idx, k, step.A, seed)
 
 
 def _run_fused(spec, cache, step, k, seed, with_z=False):
@@ -204,8 +157,8 @@ def test_nvfp4_fused_step_parity(ring_len, with_z):
     assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
-    check_nvfp4(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
-    _check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
+    gh.check_nvfp4(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
+    gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
 
 
 def test_nvfp4_fused_equals_gpu_flush_then_step():

@@ -54,36 +54,6 @@ def f16_agreement(got, ref):
     return float((og == orf).mean()), int(np.max(np.abs(og - orf))) if og.size else 0
 
 
-def _check_recur(spec, gpu, before, slots, k, A, seed, min_equal=0.98):
-    """Recurrence checkpoints after a fold of k tokens from `before`:
-    untouched slots and slot padding bit for bit, folded ones bracketed by
-    stochastic rounding of the exact fold +- the fp32 error bound."""
-    touched = sorted({int(sl) for sl, kk in zip(slots, k) if kk > 0 and 0 < sl < spec.num_slots})
-    untouched = [sl for sl in range(spec.num_slots) if sl not in touched]
-    assert np.array_equal(gpu.recur[untouched], before.recur[untouched])
-    nb = spec.recur_bytes()
-    assert np.array_equal(gpu.recur[:, nb:], before.recur[:, nb:])  # slot padding
-    if not touched:
-        return
-    v_ref = gh.f64_fold(spec, before, slots, k, A, absolute=False)
-    s_abs = gh.f64_fold(spec, before, slots, k, A, absolute=True)
-    P, N = spec.headdim, spec.dstate
-    equal = total = 0
-    for sl in touched:
-        u = np.stack([O.sr_bits(seed, sl, h, P * N).reshape(P, N) for h in range(spec.nheads)])
-        v, S = v_ref[sl], s_abs[sl]
-        E = gh.FOLD_REL * S + 2.0 ** -23 * np.abs(v)
-        lo = _f16_ordinal(O.sr_f16(v - E, u))
-        hi = _f16_ordinal(O.sr_f16(v + E, u))
-        g = _f16_ordinal(gpu.recur_logical(sl))
-        bad = (g < lo) | (g > hi)
-        assert not bad.any(), "slot %d: %d values outside the bracket, first at %s" % (
-            sl, int(bad.sum()), np.argwhere(bad)[0])
-        equal += int((g == _f16_ordinal(O.sr_f16(v, u))).sum())
-        total += g.size
-    assert equal >= min_equal * total, equal / total
-
-
 SPECS = {
     "fp8_L16": dict(num_slots=40, nheads=32, ngroups=4),
     "fp8_L32": dict(num_slots=24, nheads=16, ngroups=2, ring_len=32),
@@ -167,7 +137,7 @@ def test_separate_flush_parity(name):
     assert np.array_equal(gpu.ring_start, ref.ring_start)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0})
     gh.check_state(spec, gpu, ref, before, touched, (step.slot_idx, k, step.A))
-    _check_recur(spec, gpu, before, step.slot_idx, k, step.A, seed)
+    gh.check_recur(spec, gpu, before, step.slot_idx, k, step.A, seed)
 
 
 def _run_fused(spec, cache, step, k, seed, with_z=False):
@@ -208,7 +178,7 @@ def test_separate_fused_step_parity(name, with_z):
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
-    _check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
+    gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
 
 
 @pytest.mark.parametrize("name", list(SPECS))
