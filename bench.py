@@ -302,6 +302,8 @@ def main():
     flush_ms = [e[1].elapsed_time(e[2]) for e in evs] if (wl["flush"] and not fused) else []
 
     tokens_per_step = float(np.mean([s.tokens for s in steps_in]))
+    # replayed positions: live ring tokens plus new tokens of every entry (the folded prefix included)
+    positions_per_step = float(np.mean([int(np.sum(s.pnat)) + s.tokens for s in steps_in]))
     ob = 4 if wl["out"] == "f32" else 2
     tbs = [np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch for s in steps_in]
     if fused:
@@ -343,6 +345,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused)
+        # the oracle's effective rate in the same algorithmic bytes per token as the GPU line
+        cpu["effective_GBps"] = cpu["value"] * (sbytes + fbytes) / tokens_per_step / 1e9
 
     line = {
         "metric": METRIC,
@@ -369,6 +373,7 @@ def main():
                       else "separate ssu_flush after the step"),
             "arenas": arenas, "cache_slots": num_slots, "graph": graph is not None,
             "tokens_per_step": tokens_per_step,
+            "replayed_positions_per_s": positions_per_step * K / (ms_total * 1e-3),
             "algorithmic_bytes_per_step": sbytes + fbytes,
             "achieved_GBps_step": (sbytes + fbytes) / (ms_per_step * 1e6),
             "wall_s_timed": wall1 - wall0,
