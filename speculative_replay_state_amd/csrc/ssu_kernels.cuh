@@ -274,6 +274,15 @@ struct Win<32> {
   typedef bf16x8 V;
 };
 
+// Readout window loads: round jj of lane l holds the 16-byte chunk l % 8 of
+// window position s = l / 8 + 8 jj, so one wave instruction reads 8 whole
+// 128-byte rows (ring rows side by side, new-token rows H * 128 bytes apart).
+// The fold's window (its k ring rows) keeps the kSigBits mapping above: its
+// LDS transposition then has half the bank conflicts, which matters more
+// there than whole-row loads.
+__device__ __forceinline__ int xw_pos(int lane, int jj) { return (lane >> 3) + 8 * jj; }
+__device__ __forceinline__ int xw_chunk(int lane) { return lane & 7; }
+
 template <int KW>
 __device__ __forceinline__ f32x4 mfma_win(typename Win<KW>::V a, typename Win<KW>::V b, f32x4 c) {
   if constexpr (KW == 16)
@@ -1076,7 +1085,7 @@ __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, con
                           (int64_t)h * L * kHeadDim;
 #pragma unroll
   for (int jj = 0; jj < WC::kRounds; ++jj) {
-    const int sig = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    const int sig = xw_pos(lane, jj), pc = xw_chunk(lane);
     ld.xw[jj] = zero4;
     if (sig < S)
       ld.xw[jj] = sig < e.pnat
@@ -1168,7 +1177,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
                     (int64_t)h * L * kHeadDim;
 #pragma unroll
   for (int jj = 0; jj < WC::kRounds; ++jj) {
-    const int sig = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
+    const int sig = xw_pos(lane, jj), pc = xw_chunk(lane);
     const u32x4 v = ld.xw[jj];
     if (sig >= e.pnat && sig < S) st16(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8, v);
 #pragma unroll

@@ -141,3 +141,56 @@ def test_fused_invalid_fold_is_skipped_and_reported():
     touched = sorted({int(step.slot_idx[b]) for b in (0, 4, 5)})
     k_valid = np.where((k >= 0) & (k <= step.pnat), k, 0).astype(np.int32)
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k_valid, step.A))
+
+
+def _scaled_bf16(bits, factor):
+    """bf16 bits times a power of two (exact while in range)."""
+    v = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["flush", "fused"])
+def test_fp8_fold_extreme_rows(kind):
+    """fp8 folds far from unit scale, against the oracle.  With f = D0 *
+    old_scale the per-row decay of the old codes: slot 2 (row scales 2^-70)
+    has f < 2^-60 and new scales near 2^-10; slot 3 (scales 2^-40, ring x
+    and B times 2^50) folds values near 2^100 into rows whose old values are
+    below 2^-30; slot 4 (scales 2^59, ring x and B times 2^58) gets new
+    scales above 2^100, outside the fast reciprocal encode's range.  Slots 1
+    and 5 are ordinary."""
+    spec = synth.CacheSpec(num_slots=8, nheads=16, ngroups=2, state_dtype="fp8")
+    cache = synth.make_cache(spec, 97)
+    cache.scale_view(2)[:] = np.float32(2.0 ** -70)
+    cache.scale_view(3)[:] = np.float32(2.0 ** -40)
+    cache.scale_view(4)[:] = np.float32(2.0 ** 59)
+    for sl, e in ((3, 50), (4, 58)):
+        cache.x_view(sl)[:] = _scaled_bf16(cache.x_view(sl), 2.0 ** e)
+        cache.B_view(sl)[:] = _scaled_bf16(cache.B_view(sl), 2.0 ** e)
+    slots = np.array([1, 2, 3, 4, 5], np.int32)
+    step = synth.make_step(spec, 5, 4, 98, 8, slots=slots)
+    step.pnat[:] = [6, 8, 8, 8, 5]
+    k = step.pnat.copy()
+    print("fp8 extreme rows", kind, flush=True)
+    ref_cache = cache.copy()
+    if kind == "flush":
+        t = sd.upload_cache(cache, gh.DEV)
+        st = sd.upload_step(step, gh.DEV)
+        dc = gh.device_cache(spec, t)
+        ssu.flush(dc, st["slot_idx"], torch.from_numpy(k).to(gh.DEV), st["A"])
+        torch.cuda.synchronize()
+        assert int(dc.status.item()) == 0
+        gpu = sd.download_cache(spec, t)
+        assert O.flush(ref_cache, step.slot_idx, k, step.A) == 0
+    else:
+        out, gpu, status = _run_fused(spec, cache, step, "bf16", k)
+        assert status == 0
+        ref, st_ = O.replay_step(ref_cache, step, num_fold=k)
+        assert st_ == 0
+        got = gh.to_f64(out)
+        extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
+        excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, "bf16") * (1.0 + np.abs(ref)) - extra
+        assert np.all(excess <= 1e-12 * (1.0 + np.abs(ref))), "max excess %g" % np.max(excess)
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
+    sc = [gpu.scale_view(s).astype(np.float64) for s in (2, 3, 4)]
+    assert np.min(sc[1]) > 2.0 ** 70 and np.median(sc[2]) > 2.0 ** 100, (np.min(sc[1]), np.median(sc[2]))
+    gh.check_state(spec, gpu, ref_cache, cache, [1, 2, 3, 4, 5], (step.slot_idx, k, step.A))
