@@ -49,7 +49,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
 #ifndef SSU_FUSED_WPE
-#define SSU_FUSED_WPE(ST, KW, SEP) (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))
+// Waves per SIMD the fused kernel is compiled for.  The kernel is latency
+// bound (each wave streams its tile only between compute phases), so it runs
+// as many waves as fit: the fp8 step with bf16 output folds in 96 registers
+// (5 waves, no spills); the other forms need more and get 3, 2 or 1.
+#define SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP) \
+  (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
 #endif
 constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
@@ -334,23 +339,31 @@ __device__ __forceinline__ float scan_win(float v, int lane) {
 // step's B rows to the group's ring (one writer per (entry, group)).
 // ---------------------------------------------------------------------------
 
-// Operands of the C.B MFMA tiles: C of new token m (k order n = 32 u + 8 q + e)
-// and B of combined index s = 16 nb + m (ring or new token).
+// Operands of the C.B MFMA tiles: C of new token m and B of combined index
+// s = 16 nb + m (ring or new token), both in k order n = 32 q + 8 u + e (k
+// step u, lane quarter q) -- the order of the readout's C chunks
+// (ItemLoads::craw), so a kernel that holds those as bf16 passes them in as
+// the A operand instead of loading C again (own_c = false).
 template <int KW>
 struct CbLoads {
   bf16x8 ca[4];
   u32x4 bw[KW / 16][4];
 };
 
+// The state types whose readout keeps C as raw bf16 chunks.
+constexpr bool craw_is_bf16(int ST) { return ST == kBF16 || ST == kFP8 || ST == kNVFP4; }
+
 template <int KW>
 __device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
-                                        CbLoads<KW> &cl) {
+                                        CbLoads<KW> &cl, bool own_c = true) {
   const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
   const bf16x8 zero8 = {};
   const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
+  if (own_c) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    cl.ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + 32 * u + 8 * q)) : zero8;
+    for (int u = 0; u < 4; ++u)
+      cl.ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + 32 * q + 8 * u)) : zero8;
+  }
   const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
                           (int64_t)g * L * kDState;
 #pragma unroll
@@ -362,7 +375,7 @@ __device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const E
       const uint16_t *rp = sig < e.pnat ? Bring + ring_pos(e.r, sig, L) * kDState
                                         : s.B + ((int64_t)(e.bos + sig - e.pnat) * c.G + g) * kDState;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + 32 * u + 8 * q);
+      for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + 32 * q + 8 * u);
     }
   }
 }
@@ -379,29 +392,33 @@ __device__ __forceinline__ void append_B_rows(const KCache &c, const Entry &e, i
     if (sig >= e.pnat && sig < S) {
       uint16_t *rp = Bring + ring_pos(e.r, sig, L) * kDState;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) st16(rp + 32 * u + 8 * q, cl.bw[nb][u]);
+      for (int u = 0; u < 4; ++u) st16(rp + 32 * q + 8 * u, cl.bw[nb][u]);
     }
   }
 }
 
+// ca_ext: C chunks in the same k order (the readout's), or null for cl.ca.
 template <int KW>
-__device__ __forceinline__ void cb_tiles(const CbLoads<KW> &cl, f32x4 cb[KW / 16]) {
+__device__ __forceinline__ void cb_tiles(const CbLoads<KW> &cl, f32x4 cb[KW / 16], const u32x4 *ca_ext = nullptr) {
 #pragma unroll
   for (int nb = 0; nb < KW / 16; ++nb) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a = mfma_bf16(cl.ca[u], __builtin_bit_cast(bf16x8, cl.bw[nb][u]), a);
+    for (int u = 0; u < 4; ++u)
+      a = mfma_bf16(ca_ext ? __builtin_bit_cast(bf16x8, ca_ext[u]) : cl.ca[u], __builtin_bit_cast(bf16x8, cl.bw[nb][u]),
+                    a);
     cb[nb] = a;
   }
 }
 
 template <int KW>
 __device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, const Entry &e, int g,
-                                           bool append_B, int lane, f32x4 cb[KW / 16]) {
+                                           bool append_B, int lane, f32x4 cb[KW / 16],
+                                           const u32x4 *ca_ext = nullptr) {
   CbLoads<KW> cl;
-  load_cb<KW>(c, s, e, g, lane, cl);
+  load_cb<KW>(c, s, e, g, lane, cl, ca_ext == nullptr);
   if (append_B) append_B_rows<KW>(c, e, g, lane, cl);
-  cb_tiles<KW>(cl, cb);
+  cb_tiles<KW>(cl, cb, ca_ext);
 }
 
 // ---------------------------------------------------------------------------
@@ -583,6 +600,18 @@ __device__ __forceinline__ float max3_abs(float m, float x, float y) {
   return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(fabsf(x), fabsf(y)));
 }
 
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four quarters of a row).
+// gfx950's lane swaps exchange rows 16 lanes apart (permlane16_swap) and
+// halves 32 lanes apart (permlane32_swap) between two registers; given v
+// twice, the two results hold v of the lane and of its partner, in some order,
+// so their maximum is the pair's maximum.  No LDS and no address registers.
+__device__ __forceinline__ float quad_max(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 __device__ __forceinline__ float quarter_row_max(const f32x4 *acc) {
   float a = 0.f, b = 0.f;
 #pragma unroll
@@ -590,10 +619,7 @@ __device__ __forceinline__ float quarter_row_max(const f32x4 *acc) {
     a = max3_abs(a, acc[nb][0], acc[nb][1]);
     b = max3_abs(b, acc[nb][2], acc[nb][3]);
   }
-  float mx = fmaxf(a, b);
-  const int lane = __lane_id();
-  mx = fmaxf(mx, lane_xor(mx, lane, 16));
-  return fmaxf(mx, lane_xor(mx, lane, 32));
+  return quad_max(fmaxf(a, b));
 }
 
 // Encodes a quarter row into the lane's 16-byte chunks of a row block
@@ -792,29 +818,38 @@ __device__ __forceinline__ void load_fold_B(const KCache &c, int slot, int g, in
 
 // The fold's operands: A operands of the 8 tiles, ab[nb][e] =
 // B_s[32 (m / 4) + 8 (m % 4) + nb] for s = kE q + e (bf16, exact), the
-// coefficients cf[e] = coef_s of those positions, and the checkpoint decay D0.
+// coefficient coef_s of lane s (each row block gathers the kE of its lane's
+// positions s = kE q + e, four permutes, instead of holding them across the
+// fold), and the checkpoint decay D0 (wave-uniform: a scalar register).
 // The coefficients go into the B operand (coef_s x_s[p], split into bf16
 // parts per row block), which has half as many values per lane as the A side.
+// The A operands are the same for all four row blocks; they wait in the
+// wave's LDS (ab[nb][lane], 512 contiguous bytes per tile) rather than in 16
+// (KW 32: 32) registers across the fold, whose register peak (checkpoint tile
+// + a row block's accumulators) sets the occupancy of the folding kernels.
 template <int ST, int KW>
 struct FoldOps {
-  typename Win<KW>::V ab[8];
-  float cf[Win<KW>::kE];
+  const typename Win<KW>::V *ab;  // LDS, [8][64]
+  float coef;
   float D0;
 };
+template <int KW>
+constexpr int fold_ab_words() { return 8 * 64 * (int)sizeof(typename Win<KW>::V) / 4; }
 
 // Decay prefix and coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s,
 // D0 = exp(cumA_{k-1}); the x window goes to LDS transposed, xT[p][s] (zero
 // for s >= k).  The caller orders the LDS writes before the MFMA reads.
 template <int ST, int KW>
 __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<ST, KW> &fl,
-                                           const FoldBLoads<KW> &fb, uint16_t *xT, int lane, FoldOps<ST, KW> &fo) {
+                                           const FoldBLoads<KW> &fb, uint16_t *xT, typename Win<KW>::V *ab,
+                                           int lane, FoldOps<ST, KW> &fo) {
   using WC = Win<KW>;
   constexpr int kE = WC::kE;
   const int q = lane >> 4;
   const float cum = scan_win<KW>(Ah * fl.dtp, lane);
   const float ctot = lane_get_uniform(cum, k - 1);
   const float coef = lane < k ? expf(ctot - cum) * fl.dtp : 0.f;
-  fo.D0 = expf(ctot);
+  fo.D0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(expf(ctot))));
 #pragma unroll
   for (int jj = 0; jj < WC::kRounds; ++jj) {
     const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
@@ -823,14 +858,16 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
       xT[(pc * 8 + tt) * WC::kXS + sg] =
           (uint16_t)((tt & 1) ? (fl.xw[jj][tt >> 1] >> 16) : (fl.xw[jj][tt >> 1] & 0xFFFFu));
   }
+  fo.coef = coef;
 #pragma unroll
-  for (int e = 0; e < kE; ++e) {
-    fo.cf[e] = lane_get(coef, kE * q + e);
+  for (int nb = 0; nb < 8; ++nb) {
+    typename WC::V a;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      fo.ab[nb][e] = __builtin_bit_cast(
-          __bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
+    for (int e = 0; e < kE; ++e)
+      a[e] = __builtin_bit_cast(__bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
+    ab[nb * 64 + lane] = a;
   }
+  fo.ab = ab;
 }
 
 // The rank-k update of row block rb into the lane's quarter row:
@@ -846,7 +883,7 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uin
   V bhi, blo, blo2;
 #pragma unroll
   for (int e = 0; e < WC::kE; ++e) {
-    const float w = fo.cf[e] * (float)xb[e];
+    const float w = lane_get(fo.coef, WC::kE * q + e) * (float)xb[e];
     const __bf16 hi = (__bf16)w;
     const float r1 = w - (float)hi;
     const __bf16 lo = (__bf16)r1;
@@ -856,9 +893,10 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uin
   }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    acc[nb] = mfma_win<KW>(fo.ab[nb], bhi, acc[nb]);
-    acc[nb] = mfma_win<KW>(fo.ab[nb], blo, acc[nb]);
-    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(fo.ab[nb], blo2, acc[nb]);
+    const V a = fo.ab[nb * 64 + (lane & 63)];
+    acc[nb] = mfma_win<KW>(a, bhi, acc[nb]);
+    acc[nb] = mfma_win<KW>(a, blo, acc[nb]);
+    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(a, blo2, acc[nb]);
   }
 }
 
@@ -1153,7 +1191,7 @@ __device__ __forceinline__ void load_cb_row(const Entry &e, const float *cb, int
 template <int ST, int OT, int KW, bool HAS_Z>
 __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, const Entry &e, int h,
                                              const HeadLoads<ST, KW> &ld, const ItemLoads<ST, KW> &il,
-                                             uint16_t *xT, uint32_t *ot, int lane) {
+                                             uint16_t *xT, uint32_t *ot, int lane, const float *osc = nullptr) {
   using WC = Win<KW>;
   using V = typename WC::V;
   const int m = lane & 15, q = lane >> 4;
@@ -1255,8 +1293,8 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if constexpr (ST == kFP8)
-        acc[rb][j] = (acc[rb][j] * ld.rscale[rb][j]) * beta;
+      if constexpr (ST == kFP8)  // row 16 rb + 4 q + j: loaded, or held by lane 4 q + j in osc[rb]
+        acc[rb][j] = (acc[rb][j] * (osc ? lane_get(osc[rb], 4 * q + j) : ld.rscale[rb][j])) * beta;
       else if constexpr (ST == kNVFP4)
         acc[rb][j] = (acc[rb][j] * ld.gs) * beta;
       else
@@ -1316,7 +1354,7 @@ void replay_kernel(KCache c, KStep s, int d) {
     } else {
       float *cbw = cbw_all[wave];
       f32x4 cb[KW / 16];
-      compute_cb<KW>(c, s, e, g, chunk == 0, lane, cb);
+      compute_cb<KW>(c, s, e, g, chunk == 0, lane, cb, craw_is_bf16(ST) ? il.craw : nullptr);
 #pragma unroll
       for (int nb = 0; nb < KW / 16; ++nb)
 #pragma unroll
@@ -1387,6 +1425,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   constexpr int kNLD = st_chunks(ST);
   static_assert(ST != kNVFP4 || SEP, "an nvfp4 read checkpoint needs the recurrence checkpoint");
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
+  __shared__ __align__(16) typename WC::V ab_all[kHeadWaves][8 * 64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
   const int h = (blockIdx.x - j * htiles) * kHeadWaves + wave;
@@ -1430,7 +1469,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 
   // 2. coefficients, xT, A operands
   FoldOps<ST, KW> fo;
-  fold_setup<ST, KW>(A[h], k, fl, fb, xT, lane, fo);
+  fold_setup<ST, KW>(A[h], k, fl, fb, xT, ab_all[wave], lane, fo);
   wave_sync();  // xT written by this wave -> read below
 
   if constexpr (ST == kNVFP4) {  // the whole head at once: its scales need the head's maximum
@@ -1485,12 +1524,15 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // ---------------------------------------------------------------------------
 
 template <int ST, int OT, int KW, bool HAS_Z, bool SEP>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(SSU_FUSED_WPE(ST, KW, SEP))))
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP))))
 void fused_kernel(KCache c, KStep s, int htiles) {
-  // LDS per wave: the transposed x window and the C.B table, and later (once
-  // both have been read) the output staging tile in the same words.
+  // LDS per wave: the transposed x window, then the fold's A operands and
+  // later (once the fold is done) the C.B table in the same words, and last
+  // (once both have been read) the output staging tile.
   constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
-  constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
+  constexpr int kAbWords = fold_ab_words<KW>();
+  constexpr int kMid = kCbWords > kAbWords ? kCbWords : kAbWords;
+  constexpr int kWords = kXTWords + kMid > kOutTile ? kXTWords + kMid : kOutTile;
   __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.x / htiles;
@@ -1539,7 +1581,8 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     FoldBLoads<KW> fb;
     load_fold_B<KW>(c, e.slot, g, e.r0, e.k, lane, fb);
     FoldOps<ST, KW> fo;
-    fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, lane, fo);
+    fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, reinterpret_cast<typename Win<KW>::V *>(lds_all[wave] + kXTWords),
+                       lane, fo);
     wave_sync();  // xT written by this wave -> read below
     if constexpr (ST == kNVFP4) {
       fold_head_nvfp4<KW>(fo, xT, lane, c, e.slot, h, rraw, ld.raw, ld.sfw, ld.gs);
@@ -1550,6 +1593,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
           fl.osc[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, e.slot, h, rraw[rb], ld.raw[rb]);
         else
           fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
+        __builtin_amdgcn_sched_barrier(0);  // one row block's values live at a time
       }
     }
     wave_sync();  // the fold's xT reads done before the readout rewrites xT
@@ -1562,7 +1606,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   ItemLoads<ST, KW> il;
   load_item_c<ST, KW>(c, s, e, g, lane, il);
   CbLoads<KW> cl;
-  load_cb<KW>(c, s, e, g, lane, cl);
+  load_cb<KW>(c, s, e, g, lane, cl, !craw_is_bf16(ST));
   if (e.k > 0) {
     if constexpr (ST == kNVFP4) {
       store_nvfp4(c, e.slot, h, lane, ld.raw, ld.sfw, ld.gs);
@@ -1579,18 +1623,12 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     if constexpr (ST == kFP8)  // lane l holds row l's new scale (row 16 q + m is in rb = q)
       (reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(fl.osc[0], fl.osc[1], fl.osc[2], fl.osc[3], q);
   }
-  if constexpr (ST == kFP8) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ld.rscale[rb][j] = lane_get(fl.osc[rb], 4 * q + j);  // row 16 rb + 4 q + j
-  }
 
   // 4. C.B of the group, then the replay of the head from the (new) tile
   if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl);
   {
     f32x4 cb[KW / 16];
-    cb_tiles<KW>(cl, cb);
+    cb_tiles<KW>(cl, cb, craw_is_bf16(ST) ? il.craw : nullptr);
 #pragma unroll
     for (int nb = 0; nb < KW / 16; ++nb)
 #pragma unroll
@@ -1598,7 +1636,8 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     wave_sync();
     load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   }
-  head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, lds_all[wave], lane);
+  head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, lds_all[wave], lane,
+                                  ST == kFP8 ? fl.osc : nullptr);  // row scales of the (new) tile
 }
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
