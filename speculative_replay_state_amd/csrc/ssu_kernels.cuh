@@ -340,29 +340,35 @@ __device__ __forceinline__ float scan_win(float v, int lane) {
 // ---------------------------------------------------------------------------
 
 // Operands of the C.B MFMA tiles: C of new token m and B of combined index
-// s = 16 nb + m (ring or new token), both in k order n = 32 q + 8 u + e (k
-// step u, lane quarter q) -- the order of the readout's C chunks
-// (ItemLoads::craw), so a kernel that holds those as bf16 passes them in as
-// the A operand instead of loading C again (own_c = false).
+// s = 16 nb + m (ring or new token), in k order n = 32 u + 8 q + e (k step u,
+// lane quarter q: one load instruction reads 64 contiguous bytes of each
+// row), or (qorder) in the order of the readout's C chunks (ItemLoads::craw),
+// n = 32 q + 8 u + e, so that a caller holding those can pass them as the A
+// operand instead of loading C again (own_c = false).  The k order changes the
+// MFMA's summation grouping, so every path of one state type uses the same
+// order (cb_qorder): the fp8 paths q order, the others u order.
 template <int KW>
 struct CbLoads {
   bf16x8 ca[4];
   u32x4 bw[KW / 16][4];
 };
 
-// The state types whose readout keeps C as raw bf16 chunks.
-constexpr bool craw_is_bf16(int ST) { return ST == kBF16 || ST == kFP8 || ST == kNVFP4; }
+// Element offset, in a row of 128, of k step u's chunk for lane quarter q.
+__device__ __forceinline__ int cb_k(bool qorder, int u, int q) { return qorder ? 32 * q + 8 * u : 32 * u + 8 * q; }
+
+// The C.B k order of a state type (the fp8 fused step shares the readout's C).
+constexpr bool cb_qorder(int ST) { return ST == kFP8; }
 
 template <int KW>
 __device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
-                                        CbLoads<KW> &cl, bool own_c = true) {
+                                        CbLoads<KW> &cl, bool own_c, bool qorder) {
   const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
   const bf16x8 zero8 = {};
   const uint16_t *Crow = s.C + ((int64_t)(e.bos + m) * c.G + g) * kDState;
   if (own_c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      cl.ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + 32 * q + 8 * u)) : zero8;
+      cl.ca[u] = m < e.Tb ? __builtin_bit_cast(bf16x8, ld16(Crow + cb_k(qorder, u, q))) : zero8;
   }
   const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
                           (int64_t)g * L * kDState;
@@ -375,15 +381,16 @@ __device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const E
       const uint16_t *rp = sig < e.pnat ? Bring + ring_pos(e.r, sig, L) * kDState
                                         : s.B + ((int64_t)(e.bos + sig - e.pnat) * c.G + g) * kDState;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + 32 * q + 8 * u);
+      for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + cb_k(qorder, u, q));
     }
   }
 }
 
-// This step's B rows -> the group's ring (one writer per (entry, group)).
+// This step's B rows -> the group's ring (one writer per (entry, group));
+// qorder as for the load_cb that filled cl.
 template <int KW>
 __device__ __forceinline__ void append_B_rows(const KCache &c, const Entry &e, int g, int lane,
-                                              const CbLoads<KW> &cl) {
+                                              const CbLoads<KW> &cl, bool qorder) {
   const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
   uint16_t *Bring = reinterpret_cast<uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) + (int64_t)g * L * kDState;
 #pragma unroll
@@ -392,7 +399,7 @@ __device__ __forceinline__ void append_B_rows(const KCache &c, const Entry &e, i
     if (sig >= e.pnat && sig < S) {
       uint16_t *rp = Bring + ring_pos(e.r, sig, L) * kDState;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) st16(rp + 32 * q + 8 * u, cl.bw[nb][u]);
+      for (int u = 0; u < 4; ++u) st16(rp + cb_k(qorder, u, q), cl.bw[nb][u]);
     }
   }
 }
@@ -411,13 +418,14 @@ __device__ __forceinline__ void cb_tiles(const CbLoads<KW> &cl, f32x4 cb[KW / 16
   }
 }
 
+// ca_ext (C chunks in q order) or null; qorder must be true with ca_ext.
 template <int KW>
 __device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, const Entry &e, int g,
-                                           bool append_B, int lane, f32x4 cb[KW / 16],
+                                           bool append_B, int lane, f32x4 cb[KW / 16], bool qorder,
                                            const u32x4 *ca_ext = nullptr) {
   CbLoads<KW> cl;
-  load_cb<KW>(c, s, e, g, lane, cl, ca_ext == nullptr);
-  if (append_B) append_B_rows<KW>(c, e, g, lane, cl);
+  load_cb<KW>(c, s, e, g, lane, cl, ca_ext == nullptr, qorder);
+  if (append_B) append_B_rows<KW>(c, e, g, lane, cl, qorder);
   cb_tiles<KW>(cl, cb, ca_ext);
 }
 
@@ -818,19 +826,23 @@ __device__ __forceinline__ void load_fold_B(const KCache &c, int slot, int g, in
 
 // The fold's operands: A operands of the 8 tiles, ab[nb][e] =
 // B_s[32 (m / 4) + 8 (m % 4) + nb] for s = kE q + e (bf16, exact), the
-// coefficient coef_s of lane s (each row block gathers the kE of its lane's
-// positions s = kE q + e, four permutes, instead of holding them across the
-// fold), and the checkpoint decay D0 (wave-uniform: a scalar register).
+// coefficients cf[e] = coef_s of those positions, and the checkpoint decay D0
+// (wave-uniform: a scalar register).
 // The coefficients go into the B operand (coef_s x_s[p], split into bf16
 // parts per row block), which has half as many values per lane as the A side.
-// The A operands are the same for all four row blocks; they wait in the
-// wave's LDS (ab[nb][lane], 512 contiguous bytes per tile) rather than in 16
-// (KW 32: 32) registers across the fold, whose register peak (checkpoint tile
-// + a row block's accumulators) sets the occupancy of the folding kernels.
-template <int ST, int KW>
+// LEAN (register-lean) form: the A operands, the same for all four row
+// blocks, wait in the wave's LDS (abl[nb][lane], 512 contiguous bytes per
+// tile) instead of 16 (KW 32: 32) registers, and each row block gathers its
+// lane's kE coefficients from coef (kE permutes) instead of holding cf across
+// the fold.  The fold's register peak (checkpoint tile + a row block's
+// accumulators) sets the occupancy of the folding kernels; the lean form pays
+// off where it lifts occupancy, and costs time at low occupancy.
+template <int ST, int KW, bool LEAN = false>
 struct FoldOps {
-  const typename Win<KW>::V *ab;  // LDS, [8][64]
-  float coef;
+  typename Win<KW>::V ab[LEAN ? 1 : 8];
+  float cf[LEAN ? 1 : Win<KW>::kE];
+  const typename Win<KW>::V *abl;  // LEAN: LDS [8][64]
+  float coef;                      // LEAN: coef_s of lane s
   float D0;
 };
 template <int KW>
@@ -839,17 +851,16 @@ constexpr int fold_ab_words() { return 8 * 64 * (int)sizeof(typename Win<KW>::V)
 // Decay prefix and coefficients coef_s = exp(cumA_{k-1} - cumA_s) dt'_s,
 // D0 = exp(cumA_{k-1}); the x window goes to LDS transposed, xT[p][s] (zero
 // for s >= k).  The caller orders the LDS writes before the MFMA reads.
-template <int ST, int KW>
+template <int ST, int KW, bool LEAN>
 __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<ST, KW> &fl,
-                                           const FoldBLoads<KW> &fb, uint16_t *xT, typename Win<KW>::V *ab,
-                                           int lane, FoldOps<ST, KW> &fo) {
+                                           const FoldBLoads<KW> &fb, uint16_t *xT, typename Win<KW>::V *abl,
+                                           int lane, FoldOps<ST, KW, LEAN> &fo) {
   using WC = Win<KW>;
   constexpr int kE = WC::kE;
   const int q = lane >> 4;
   const float cum = scan_win<KW>(Ah * fl.dtp, lane);
   const float ctot = lane_get_uniform(cum, k - 1);
   const float coef = lane < k ? expf(ctot - cum) * fl.dtp : 0.f;
-  fo.D0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(expf(ctot))));
 #pragma unroll
   for (int jj = 0; jj < WC::kRounds; ++jj) {
     const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
@@ -858,23 +869,36 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
       xT[(pc * 8 + tt) * WC::kXS + sg] =
           (uint16_t)((tt & 1) ? (fl.xw[jj][tt >> 1] >> 16) : (fl.xw[jj][tt >> 1] & 0xFFFFu));
   }
-  fo.coef = coef;
+  if constexpr (LEAN) {  // D0 in a scalar register, operands to LDS, coef gathered per row block
+    fo.D0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(expf(ctot))));
+    fo.coef = coef;
+    fo.abl = abl;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    typename WC::V a;
+    for (int nb = 0; nb < 8; ++nb) {
+      typename WC::V a;
 #pragma unroll
-    for (int e = 0; e < kE; ++e)
-      a[e] = __builtin_bit_cast(__bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
-    ab[nb * 64 + lane] = a;
+      for (int e = 0; e < kE; ++e)
+        a[e] = __builtin_bit_cast(__bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
+      abl[nb * 64 + lane] = a;
+    }
+  } else {
+    fo.D0 = expf(ctot);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      fo.cf[e] = lane_get(coef, kE * q + e);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        fo.ab[nb][e] = __builtin_bit_cast(
+            __bf16, (uint16_t)((nb & 1) ? (fb.bw[e][nb >> 1] >> 16) : (fb.bw[e][nb >> 1] & 0xFFFFu)));
+    }
   }
-  fo.ab = ab;
 }
 
 // The rank-k update of row block rb into the lane's quarter row:
 // acc[nb] += sum_s B_s[n] (coef_s x_s[p]) for p = 16 rb + m, with coef_s x_s[p]
 // split into bf16 hi + lo (+ lo2 for fp32 state).
-template <int ST, int KW>
-__device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb, int lane,
+template <int ST, int KW, bool LEAN>
+__device__ __forceinline__ void fold_update(const FoldOps<ST, KW, LEAN> &fo, const uint16_t *xT, int rb, int lane,
                                             f32x4 *acc) {
   using WC = Win<KW>;
   using V = typename WC::V;
@@ -883,7 +907,7 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uin
   V bhi, blo, blo2;
 #pragma unroll
   for (int e = 0; e < WC::kE; ++e) {
-    const float w = lane_get(fo.coef, WC::kE * q + e) * (float)xb[e];
+    const float w = (LEAN ? lane_get(fo.coef, WC::kE * q + e) : fo.cf[LEAN ? 0 : e]) * (float)xb[e];
     const __bf16 hi = (__bf16)w;
     const float r1 = w - (float)hi;
     const __bf16 lo = (__bf16)r1;
@@ -893,7 +917,7 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uin
   }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    const V a = fo.ab[nb * 64 + (lane & 63)];
+    const V a = LEAN ? fo.abl[nb * 64 + (lane & 63)] : fo.ab[LEAN ? 0 : nb];
     acc[nb] = mfma_win<KW>(a, bhi, acc[nb]);
     acc[nb] = mfma_win<KW>(a, blo, acc[nb]);
     if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(a, blo2, acc[nb]);
@@ -903,8 +927,8 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW> &fo, const uin
 // One row block of the fold: decode and decay the lane's chunks ch (old
 // checkpoint), add the rank-k update, re-encode into ch (new checkpoint) and
 // return the fp8 row scale of row 16 rb + m (1 for other dtypes).
-template <int ST, int KW>
-__device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb, int lane,
+template <int ST, int KW, bool LEAN>
+__device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW, LEAN> &fo, const uint16_t *xT, int rb, int lane,
                                                float old_scale, u32x4 *ch) {
   f32x4 acc[8];
   decode_quarter<ST>(ch, ST == kFP8 ? fo.D0 * old_scale : fo.D0, acc);
@@ -923,8 +947,8 @@ __device__ __forceinline__ float fold_rowblock(const FoldOps<ST, KW> &fo, const 
 // The same with separate checkpoints: decode the FP16 recurrence chunks rch,
 // fold, write the read checkpoint chunks ch (nearest encoding in ST) and the
 // new recurrence chunks into rch (stochastic rounding).
-template <int ST, int KW>
-__device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW> &fo, const uint16_t *xT, int rb,
+template <int ST, int KW, bool LEAN>
+__device__ __forceinline__ float fold_rowblock_sep(const FoldOps<ST, KW, LEAN> &fo, const uint16_t *xT, int rb,
                                                    int lane, const KCache &c, int slot, int head, u32x4 *rch,
                                                    u32x4 *ch) {
   const int m = lane & 15, q = lane >> 4;
@@ -1010,8 +1034,8 @@ __device__ __forceinline__ void nvfp4_scales(const float *bm, int lane, float &g
 // runs twice: pass 1 keeps the block maxima, pass 2 (the same instructions on
 // the same operands, hence the same values) writes the new recurrence chunks
 // over rch (stochastic rounding) and the e2m1 codes into codes.
-template <int KW>
-__device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW> &fo, const uint16_t *xT, int lane,
+template <int KW, bool LEAN>
+__device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW, LEAN> &fo, const uint16_t *xT, int lane,
                                                 const KCache &c, int slot, int head, u32x4 (*rch)[4],
                                                 u32x4 (*codes)[1], u32x2 &sfw, float &g) {
   const int m = lane & 15, q = lane >> 4;
@@ -1354,7 +1378,7 @@ void replay_kernel(KCache c, KStep s, int d) {
     } else {
       float *cbw = cbw_all[wave];
       f32x4 cb[KW / 16];
-      compute_cb<KW>(c, s, e, g, chunk == 0, lane, cb, craw_is_bf16(ST) ? il.craw : nullptr);
+      compute_cb<KW>(c, s, e, g, chunk == 0, lane, cb, cb_qorder(ST), cb_qorder(ST) ? il.craw : nullptr);
 #pragma unroll
       for (int nb = 0; nb < KW / 16; ++nb)
 #pragma unroll
@@ -1394,7 +1418,7 @@ void replay_kernel(KCache c, KStep s, int d) {
 // SPLIT precompute (one wave per (entry, group)): C.B -> scratch, B append.
 // ---------------------------------------------------------------------------
 
-template <int KW>
+template <int KW, bool QORDER>
 __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int item = blockIdx.x * kWaves + wave;
@@ -1403,7 +1427,7 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
   const Entry e = load_entry(c, s, b, false);
   if (e.mode != 2) return;
   f32x4 cb[KW / 16];
-  compute_cb<KW>(c, s, e, g, true, lane, cb);
+  compute_cb<KW>(c, s, e, g, true, lane, cb, QORDER);
   const int m = lane & 15, q = lane >> 4;
   float *dst = s.cb + ((int64_t)b * c.G + g) * s.T * kCbStride;
 #pragma unroll
@@ -1425,7 +1449,6 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   constexpr int kNLD = st_chunks(ST);
   static_assert(ST != kNVFP4 || SEP, "an nvfp4 read checkpoint needs the recurrence checkpoint");
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
-  __shared__ __align__(16) typename WC::V ab_all[kHeadWaves][8 * 64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = blockIdx.x / htiles;
   const int h = (blockIdx.x - j * htiles) * kHeadWaves + wave;
@@ -1469,7 +1492,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 
   // 2. coefficients, xT, A operands
   FoldOps<ST, KW> fo;
-  fold_setup<ST, KW>(A[h], k, fl, fb, xT, ab_all[wave], lane, fo);
+  fold_setup<ST, KW>(A[h], k, fl, fb, xT, nullptr, lane, fo);
   wave_sync();  // xT written by this wave -> read below
 
   if constexpr (ST == kNVFP4) {  // the whole head at once: its scales need the head's maximum
@@ -1530,7 +1553,8 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   // later (once the fold is done) the C.B table in the same words, and last
   // (once both have been read) the output staging tile.
   constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
-  constexpr int kAbWords = fold_ab_words<KW>();
+  constexpr bool kAbLds = SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP) >= 5;  // register-lean form
+  constexpr int kAbWords = kAbLds ? fold_ab_words<KW>() : 0;
   constexpr int kMid = kCbWords > kAbWords ? kCbWords : kAbWords;
   constexpr int kWords = kXTWords + kMid > kOutTile ? kXTWords + kMid : kOutTile;
   __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
@@ -1580,9 +1604,10 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   if (e.k > 0) {
     FoldBLoads<KW> fb;
     load_fold_B<KW>(c, e.slot, g, e.r0, e.k, lane, fb);
-    FoldOps<ST, KW> fo;
-    fold_setup<ST, KW>(Ah, e.k, fl, fb, xT, reinterpret_cast<typename Win<KW>::V *>(lds_all[wave] + kXTWords),
-                       lane, fo);
+    FoldOps<ST, KW, kAbLds> fo;
+    fold_setup<ST, KW>(Ah, e.k, fl, fb, xT,
+                       kAbLds ? reinterpret_cast<typename Win<KW>::V *>(lds_all[wave] + kXTWords) : nullptr, lane,
+                       fo);
     wave_sync();  // xT written by this wave -> read below
     if constexpr (ST == kNVFP4) {
       fold_head_nvfp4<KW>(fo, xT, lane, c, e.slot, h, rraw, ld.raw, ld.sfw, ld.gs);
@@ -1593,7 +1618,7 @@ void fused_kernel(KCache c, KStep s, int htiles) {
           fl.osc[rb] = fold_rowblock_sep<ST, KW>(fo, xT, rb, lane, c, e.slot, h, rraw[rb], ld.raw[rb]);
         else
           fl.osc[rb] = fold_rowblock<ST, KW>(fo, xT, rb, lane, fl.osc[rb], ld.raw[rb]);
-        __builtin_amdgcn_sched_barrier(0);  // one row block's values live at a time
+        if constexpr (kAbLds) __builtin_amdgcn_sched_barrier(0);  // one row block's values live at a time
       }
     }
     wave_sync();  // the fold's xT reads done before the readout rewrites xT
@@ -1605,8 +1630,9 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   load_window<ST, OT, KW, HAS_Z>(c, s, e, h, lane, ld);
   ItemLoads<ST, KW> il;
   load_item_c<ST, KW>(c, s, e, g, lane, il);
+  constexpr bool kShareC = cb_qorder(ST);  // C.B takes the readout's C chunks
   CbLoads<KW> cl;
-  load_cb<KW>(c, s, e, g, lane, cl, !craw_is_bf16(ST));
+  load_cb<KW>(c, s, e, g, lane, cl, !kShareC, kShareC);
   if (e.k > 0) {
     if constexpr (ST == kNVFP4) {
       store_nvfp4(c, e.slot, h, lane, ld.raw, ld.sfw, ld.gs);
@@ -1625,10 +1651,10 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   }
 
   // 4. C.B of the group, then the replay of the head from the (new) tile
-  if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl);
+  if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl, kShareC);
   {
     f32x4 cb[KW / 16];
-    cb_tiles<KW>(cl, cb, craw_is_bf16(ST) ? il.craw : nullptr);
+    cb_tiles<KW>(cl, cb, kShareC ? il.craw : nullptr);
 #pragma unroll
     for (int nb = 0; nb < KW / 16; ++nb)
 #pragma unroll
@@ -1636,8 +1662,15 @@ void fused_kernel(KCache c, KStep s, int htiles) {
     wave_sync();
     load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   }
+  if constexpr (ST == kFP8 && !kAbLds) {  // row scales of the (new) tile, rows 16 rb + 4 q + j
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ld.rscale[rb][j] = lane_get(fl.osc[rb], 4 * q + j);
+  }
+  // the lean form gathers them where the epilogue uses them
   head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, lds_all[wave], lane,
-                                  ST == kFP8 ? fl.osc : nullptr);  // row scales of the (new) tile
+                                  (ST == kFP8 && kAbLds) ? fl.osc : nullptr);
 }
 
 // Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
@@ -1776,7 +1809,7 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
   if (resident == 0) resident = resident_blocks(replay_kernel<ST, OT, KW, SPLIT, HAS_Z>, 0);
   if (SPLIT) {
     const int64_t pre_items = (int64_t)s.batch * c.G;
-    precompute_kernel<KW><<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
+    precompute_kernel<KW, cb_qorder(ST)><<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
