@@ -1440,18 +1440,28 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
   }
 }
 
+// Workgroups of a launch go to the 8 XCDs round-robin by ID, and each XCD
+// has its own L2.  The one-head-per-wave kernels take their (entry, head tile)
+// from xcd_tile, so XCD x runs the contiguous tiles [x per, (x + 1) per): the
+// heads of one group, which read the same B and C rows, read them through
+// one L2.  The grid is rounded up to a multiple of 8 (tiles >= ntiles idle).
+__device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t ngrid) { return (id & 7) * (ngrid >> 3) + (id >> 3); }
+inline unsigned xcd_grid(int64_t ntiles) { return (unsigned)((ntiles + 7) / 8 * 8); }
+
 template <int ST, int KW, bool SEP>
 __global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
 void flush_kernel(KCache c, const int32_t *slot_idx,
                                                             const int32_t *num_fold, const float *A,
-                                                            int htiles) {
+                                                            int htiles, int64_t ntiles) {
   using WC = Win<KW>;
   constexpr int kNLD = st_chunks(ST);
   static_assert(ST != kNVFP4 || SEP, "an nvfp4 read checkpoint needs the recurrence checkpoint");
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int j = blockIdx.x / htiles;
-  const int h = (blockIdx.x - j * htiles) * kHeadWaves + wave;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= ntiles) return;
+  const int j = (int)(tile / htiles);
+  const int h = (int)(tile - (int64_t)j * htiles) * kHeadWaves + wave;
   if (h >= c.H) return;
   const int slot = slot_idx[j], k = num_fold[j], L = c.L;
   if (slot <= 0 || slot >= c.num_slots) return;
@@ -1548,7 +1558,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 
 template <int ST, int OT, int KW, bool HAS_Z, bool SEP>
 __global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP))))
-void fused_kernel(KCache c, KStep s, int htiles) {
+void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
   // LDS per wave: the transposed x window, then the fold's A operands and
   // later (once the fold is done) the C.B table in the same words, and last
   // (once both have been read) the output staging tile.
@@ -1559,8 +1569,10 @@ void fused_kernel(KCache c, KStep s, int htiles) {
   constexpr int kWords = kXTWords + kMid > kOutTile ? kXTWords + kMid : kOutTile;
   __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int b = blockIdx.x / htiles;
-  const int h = (blockIdx.x - b * htiles) * kHeadWaves + wave;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= ntiles) return;
+  const int b = (int)(tile / htiles);
+  const int h = (int)(tile - (int64_t)b * htiles) * kHeadWaves + wave;
   if (h >= c.H) return;
   const int g = h / c.hpg, m = lane & 15, q = lane >> 4;
   uint16_t *xT = reinterpret_cast<uint16_t *>(lds_all[wave]);
@@ -1824,11 +1836,12 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
 template <int ST, int OT, bool HAS_Z, bool SEP>
 hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
-  const dim3 grid((unsigned)((int64_t)s.batch * htiles)), block(kHeadWaves * 64);
+  const int64_t ntiles = (int64_t)s.batch * htiles;
+  const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
   if (c.L <= 16)
-    fused_kernel<ST, OT, 16, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 16, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles, ntiles);
   else
-    fused_kernel<ST, OT, 32, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles);
+    fused_kernel<ST, OT, 32, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   step_ring_advance_kernel<ST><<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
@@ -1871,22 +1884,23 @@ template <int ST>
 hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                    int n, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
-  const dim3 grid((unsigned)((int64_t)n * htiles)), block(kHeadWaves * 64);
+  const int64_t ntiles = (int64_t)n * htiles;
+  const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
   bool sep = ST == kNVFP4;
   if constexpr (ST == kFP8) sep = c.recur != nullptr;
   if (sep) {
     if constexpr (ST == kFP8 || ST == kNVFP4) {
       if (c.L <= 16)
-        flush_kernel<ST, 16, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+        flush_kernel<ST, 16, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
       else
-        flush_kernel<ST, 32, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+        flush_kernel<ST, 32, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
     }
   } else {
     if constexpr (ST != kNVFP4) {
       if (c.L <= 16)
-        flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+        flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
       else
-        flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles);
+        flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
     }
   }
   hipError_t err = hipGetLastError();
