@@ -4,7 +4,7 @@ update (ReplaySSM / MTP-replay SSU) on AMD MI355X.
 This module only marshals arguments: it builds the C descriptors from device
 tensors and calls the library.  Every step of the computation runs in the
 library's HIP kernels.  Importing fails loudly when libssu.so has not been
-built (python -m speculative_replay_state_amd.build); there is no fallback.
+built (python speculative_replay_state_amd/build.py); there is no fallback.
 
 Names follow the C ABI: ssu_init_state, ssu_replay_step, ssu_flush,
 ssu_workspace_size, ssu_resolve_algo, ssu_last_error, plus DeviceCache (the
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libssu.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libssu.so is not built at %s; run `python -m speculative_replay_state_amd.build` "
+        "libssu.so is not built at %s; run `python speculative_replay_state_amd/build.py` "
         "(needs ROCm hipcc)" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)

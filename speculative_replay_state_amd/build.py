@@ -1,6 +1,8 @@
 """Build libssu.so (gfx950) in-tree with hipcc.
 
-    python -m speculative_replay_state_amd.build
+    python speculative_replay_state_amd/build.py
+
+(run as a script: importing the package fails until the library exists)
 
 Compiles the device code (csrc/ssu_kernels.cuh through ssu_kernels_inst.hip,
 once per state type, in parallel), the dispatch (csrc/ssu_launch.cpp) and the
