@@ -200,6 +200,81 @@ struct Entry {
   int mode;  // 0: skip entirely, 1: zero the output rows only, 2: replay
 };
 
+// The per-entry words of a fused step, loaded without branches so that they
+// go out together: a word that does not apply is read from another valid
+// address and ignored (the fused step always has num_fold).
+struct EntryIn {
+  int bos, eos, pnat, fold, ring_word;
+};
+
+__device__ __forceinline__ EntryIn load_entry_in(const KCache &c, const KStep &s, int b, int slot, bool slot_ok) {
+  const bool varlen = s.cu != nullptr;
+  const int32_t *cu0 = varlen ? s.cu + b : s.pnat + b;
+  const int32_t *cu1 = varlen ? s.cu + b + 1 : s.pnat + b;
+  const int32_t *rs = c.ring_start + (slot_ok ? slot : 0);
+  int w0 = *cu0, w1 = *cu1, pn = s.pnat[b], kf = s.fold[b], rw = *rs;
+  // an empty statement that takes and gives back the five words: the loads
+  // cannot be moved into the branches that use them, so they are issued
+  // together and waited for once
+  asm volatile("" : "+s"(w0), "+s"(w1), "+s"(pn), "+s"(kf), "+s"(rw));
+  EntryIn in;
+  in.pnat = pn;
+  in.fold = kf;
+  in.ring_word = rw;
+  in.bos = varlen ? w0 : b * s.T;
+  in.eos = varlen ? w1 : in.bos + s.T;
+  return in;
+}
+
+// Validates an entry of a fused step from its words (the same checks as
+// load_entry).
+__device__ __forceinline__ Entry make_entry(const KCache &c, const KStep &s, int slot, const EntryIn &in,
+                                            bool report) {
+  Entry e;
+  e.bos = in.bos;
+  e.Tb = in.eos - in.bos;
+  e.slot = slot;
+  e.pnat = 0;
+  e.r = 0;
+  e.k = 0;
+  e.r0 = 0;
+  e.mode = 2;
+  int bit = 0;
+  if (e.Tb < 0 || e.Tb > s.T) {
+    e.mode = 0;
+    bit = SSU_STATUS_BAD_SEQLEN;
+  } else if (e.slot <= 0 || e.slot >= c.num_slots) {
+    e.mode = 1;  // padding entry
+  } else {
+    e.pnat = in.pnat;
+    if (e.pnat < 0 || e.pnat + e.Tb > c.L) {
+      e.mode = 1;
+      bit = SSU_STATUS_BAD_PNAT;
+    } else {
+      e.r = in.ring_word;
+      e.r0 = e.r;
+      if (e.r < 0 || e.r >= c.L) {
+        e.mode = 1;
+        bit = SSU_STATUS_BAD_RING;
+      } else if (s.fold) {
+        const int k = in.fold;
+        if (k < 0 || k > e.pnat) {
+          e.mode = 1;
+          bit = SSU_STATUS_BAD_FOLD;
+        } else {
+          e.k = k;
+          e.r = ring_pos(e.r0, k, c.L);
+          e.pnat -= k;
+        }
+      }
+    }
+  }
+  if (bit && report && c.status && (threadIdx.x & 63) == 0) atomicOr(c.status, bit);
+  return e;
+}
+
+// The same checks, loading each word only where it is needed (the replay and
+// flush kernels, whose waves do not start with a tile load).
 __device__ __forceinline__ Entry load_entry(const KCache &c, const KStep &s, int b, bool report) {
   Entry e;
   if (s.cu) {
@@ -790,7 +865,6 @@ __device__ __forceinline__ void load_fold_head(const KCache &c, int slot, int h,
                                                FoldHeadLoads<ST, KW> &fl) {
   using WC = Win<KW>;
   const int m = lane & 15, L = c.L;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) fl.osc[rb] = 1.f;
   if constexpr (ST == kFP8) {
@@ -802,10 +876,15 @@ __device__ __forceinline__ void load_fold_head(const KCache &c, int slot, int h,
   fl.dtp = lane < k ? dtring[ring_pos(r, lane, L)] : 0.f;
   const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)slot * c.x_stride) +
                           (int64_t)h * L * kHeadDim;
+  // Rows past the k folded tokens load row k - 1 again instead of being
+  // branched around (a load behind a lane branch is waited for at the branch's
+  // end): their fold coefficient is exactly zero, so a finite copy of a live
+  // row adds nothing.  The repeated addresses merge inside the instruction.
+  const int klast = k > 0 ? k - 1 : 0;
 #pragma unroll
   for (int jj = 0; jj < WC::kRounds; ++jj) {
     const int sg = lane & (KW - 1), pc = (lane >> WC::kSigBits) + (64 >> WC::kSigBits) * jj;
-    fl.xw[jj] = sg < k ? ld16(xring + ring_pos(r, sg, L) * kHeadDim + pc * 8) : zero4;
+    fl.xw[jj] = ld16(xring + ring_pos(r, sg < k ? sg : klast, L) * kHeadDim + pc * 8);
   }
 }
 
@@ -814,13 +893,13 @@ __device__ __forceinline__ void load_fold_B(const KCache &c, int slot, int g, in
                                             FoldBLoads<KW> &fb) {
   using WC = Win<KW>;
   const int m = lane & 15, q = lane >> 4, L = c.L;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)slot * c.B_stride) +
                           (int64_t)g * L * kDState;
+  const int klast = k > 0 ? k - 1 : 0;  // rows past k: row k - 1 again (see load_fold_head)
 #pragma unroll
   for (int e = 0; e < WC::kE; ++e) {
     const int sg = WC::kE * q + e;
-    fb.bw[e] = sg < k ? ld16(Bring + ring_pos(r, sg, L) * kDState + 32 * (m >> 2) + 8 * (m & 3)) : zero4;
+    fb.bw[e] = ld16(Bring + ring_pos(r, sg < k ? sg : klast, L) * kDState + 32 * (m >> 2) + 8 * (m & 3));
   }
 }
 
@@ -1578,30 +1657,40 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
   uint16_t *xT = reinterpret_cast<uint16_t *>(lds_all[wave]);
   float *cbw = reinterpret_cast<float *>(lds_all[wave] + kXTWords);
 
-  // 1. the checkpoint as soon as the slot is known (in bounds for any valid
-  //    slot; discarded if the entry turns out to be skipped).  Separate
+  // 1. the checkpoint as soon as the slot is known (discarded if the entry
+  //    turns out to be skipped).  Separate
   //    checkpoints: an entry that asks for a fold reads the FP16 recurrence
   //    tile (the fold writes the read tile from it), any other the read tile.
   //    A replayed entry folds exactly the k it asks for, so the choice holds.
   HeadLoads<ST, KW> ld;
   u32x4 rraw[SEP ? 4 : 1][4];
+  // The tile loads go out as soon as the slot is known; the entry's other
+  // words (the slot's ring start among them) follow as scalar loads.  One
+  // counter tracks a wave's vector loads in issue order, so words loaded as
+  // vector loads after the tile could only be used once the tile had arrived;
+  // as scalar loads they arrive on their own, and the fold's window loads that
+  // need them go out while the tile is still in flight.
+  const int slot0 = s.slot_idx[b];
+  const bool slot_ok = slot0 > 0 && slot0 < c.num_slots;
   {
-    const int slot = s.slot_idx[b];
-    if (slot > 0 && slot < c.num_slots) {
-      bool recur_tile = false;
-      if constexpr (SEP) recur_tile = s.fold[b] > 0;
-      if (recur_tile) {
-        const uint8_t *rp = c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
+    // An entry whose slot is out of range loads slot 0's tile (in bounds,
+    // never used), so that the tile loads are not behind a branch.
+    const int slot = slot_ok ? slot0 : 0;
+    bool recur_tile = false;
+    if constexpr (SEP) recur_tile = slot_ok && s.fold[b] > 0;
+    if (recur_tile) {
+      const uint8_t *rp = c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) rraw[rb][u] = ld16_nt(rp + tile_chunk(rb, u, lane, 2));
-      } else {
-        load_state<ST, KW>(c, slot, h, lane, ld);
-      }
+        for (int u = 0; u < 4; ++u) rraw[rb][u] = ld16_nt(rp + tile_chunk(rb, u, lane, 2));
+    } else {
+      load_state<ST, KW>(c, slot, h, lane, ld);
     }
   }
-  const Entry e = load_entry(c, s, b, h == 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const EntryIn ein = load_entry_in(c, s, b, slot0, slot_ok);
+  const Entry e = make_entry(c, s, slot0, ein, h == 0);
   if (e.mode == 0) return;
   if (e.mode == 1) {
     zero_out_head<OT>(s, c.H, e, h, lane);
@@ -1683,16 +1772,6 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
   // the lean form gathers them where the epilogue uses them
   head_compute<ST, OT, KW, HAS_Z>(c, s, e, h, ld, il, xT, lds_all[wave], lane,
                                   (ST == kFP8 && kAbLds) ? fl.osc : nullptr);
-}
-
-// Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
-// entry the step folded (same validity rules as the step itself).
-template <int ST>
-__global__ void step_ring_advance_kernel(KCache c, KStep s) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= s.batch) return;
-  const Entry e = load_entry(c, s, b, false);
-  if (e.mode == 2 && e.k > 0) c.ring_start[e.slot] = e.r;
 }
 
 // Ring bookkeeping after a flush: ring_start <- (ring_start + k) mod L.
@@ -1831,6 +1910,19 @@ hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
   const int64_t blocks = need < resident ? need : resident;
   replay_kernel<ST, OT, KW, SPLIT, HAS_Z><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, st>>>(c, s, d);
   return hipGetLastError();
+}
+
+// Ring bookkeeping after a fused step: ring_start <- ring_start + k for every
+// entry the step folded (same validity rules as the step itself).  A separate
+// launch on the same stream: counting the heads of a slot with an atomic
+// inside the step (one address per slot, hit by every head at once) measured
+// ~15 % slower than this launch inside a captured graph.
+template <int ST>
+__global__ void step_ring_advance_kernel(KCache c, KStep s) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= s.batch) return;
+  const Entry e = load_entry(c, s, b, false);
+  if (e.mode == 2 && e.k > 0) c.ring_start[e.slot] = e.r;
 }
 
 template <int ST, int OT, bool HAS_Z, bool SEP>
