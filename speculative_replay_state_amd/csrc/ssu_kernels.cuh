@@ -500,8 +500,11 @@ __device__ __forceinline__ void compute_cb(const KCache &c, const KStep &s, cons
                                            const u32x4 *ca_ext = nullptr) {
   CbLoads<KW> cl;
   load_cb<KW>(c, s, e, g, lane, cl, ca_ext == nullptr, qorder);
-  if (append_B) append_B_rows<KW>(c, e, g, lane, cl, qorder);
+  // The MFMAs before the append: after the append's branch the compiler can
+  // no longer count which loads are still in flight, so a use of the B rows
+  // there waits for every load and store the wave has issued.
   cb_tiles<KW>(cl, cb, ca_ext);
+  if (append_B) append_B_rows<KW>(c, e, g, lane, cl, qorder);
 }
 
 // ---------------------------------------------------------------------------
@@ -1203,12 +1206,44 @@ __device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int
 // loaded here is used before the head's compute phase: one counter tracks a
 // wave's loads in issue order, so using a value loaded here right away would
 // also wait for every load issued before it, including a prefetched tile.
-template <int ST, int OT, int KW, bool HAS_Z>
+// FLAT: no load sits behind a lane branch (a load behind one is waited for at
+// the branch's end, before the loads after it are issued).  Positions past
+// the window (s >= S) then load the window's last token again instead of
+// zeros: their replay coefficient is exactly zero, so a finite copy of a
+// token adds nothing; an empty window (S = 0) loads ring row 0, which no
+// output uses.  Each position picks its ring or new-token address with a
+// select, so each position is one load.
+template <int ST, int OT, int KW, bool HAS_Z, bool FLAT = false>
 __device__ __forceinline__ void load_window(const KCache &c, const KStep &s, const Entry &e, int h, int lane,
                                             HeadLoads<ST, KW> &ld) {
   if constexpr (HAS_Z) load_gate<OT>(s, c.H, e, h, lane, ld.zw);
   using WC = Win<KW>;
   const int H = c.H, L = c.L, S = e.pnat + e.Tb;
+  if constexpr (FLAT) {
+    const float *dtring = reinterpret_cast<const float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
+    const uint16_t *xring = reinterpret_cast<const uint16_t *>(c.xc + (int64_t)e.slot * c.x_stride) +
+                            (int64_t)h * L * kHeadDim;
+    const int slast = S > 0 ? S - 1 : 0;
+    {
+      const int sg = lane < S ? lane : slast;
+      const bool ring = sg < e.pnat || S == 0;
+      const float *p = ring ? dtring + ring_pos(e.r, sg, L) : s.dt + (int64_t)(e.bos + sg - e.pnat) * H + h;
+      ld.dtv = *p;
+    }
+    ld.dtb = s.dt_bias[h];
+    ld.Ah = s.A[h];
+    ld.Dh = s.D[h];
+#pragma unroll
+    for (int jj = 0; jj < WC::kRounds; ++jj) {
+      const int sig = xw_pos(lane, jj), pc = xw_chunk(lane);
+      const int sg = sig < S ? sig : slast;
+      const bool ring = sg < e.pnat || S == 0;
+      const uint16_t *p = ring ? xring + ring_pos(e.r, sg, L) * kHeadDim + pc * 8
+                               : s.x + ((int64_t)(e.bos + sg - e.pnat) * H + h) * kHeadDim + pc * 8;
+      ld.xw[jj] = ld16_nt(p);
+    }
+    return;
+  }
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   ld.dtv = 0.f;
   if (lane < S) {
@@ -1664,15 +1699,17 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
   //    A replayed entry folds exactly the k it asks for, so the choice holds.
   HeadLoads<ST, KW> ld;
   u32x4 rraw[SEP ? 4 : 1][4];
-  // The tile loads go out as soon as the slot is known; the entry's other
-  // words (the slot's ring start among them) follow as scalar loads.  One
-  // counter tracks a wave's vector loads in issue order, so words loaded as
-  // vector loads after the tile could only be used once the tile had arrived;
-  // as scalar loads they arrive on their own, and the fold's window loads that
-  // need them go out while the tile is still in flight.
+  // 8- and 4-bit checkpoints: the tile loads go out as soon as the slot is
+  // known; the entry's other words (the slot's ring start among them) follow
+  // as scalar loads.  One counter tracks a wave's vector loads in issue order,
+  // so words loaded as vector loads after the tile could only be used once
+  // the tile had arrived; as scalar loads they arrive on their own, and the
+  // fold's window loads that need them go out while the tile is in flight.
+  // (The 16- and 32-bit tiles hold too many registers for this: it spills.)
+  constexpr bool kEarly = ST == kFP8 || ST == kNVFP4;
   const int slot0 = s.slot_idx[b];
   const bool slot_ok = slot0 > 0 && slot0 < c.num_slots;
-  {
+  if (kEarly || slot_ok) {
     // An entry whose slot is out of range loads slot 0's tile (in bounds,
     // never used), so that the tile loads are not behind a branch.
     const int slot = slot_ok ? slot0 : 0;
@@ -1688,9 +1725,13 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
       load_state<ST, KW>(c, slot, h, lane, ld);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-  const EntryIn ein = load_entry_in(c, s, b, slot0, slot_ok);
-  const Entry e = make_entry(c, s, slot0, ein, h == 0);
+  Entry e;
+  if constexpr (kEarly) {
+    __builtin_amdgcn_sched_barrier(0);
+    e = make_entry(c, s, slot0, load_entry_in(c, s, b, slot0, slot_ok), h == 0);
+  } else {
+    e = load_entry(c, s, b, h == 0);
+  }
   if (e.mode == 0) return;
   if (e.mode == 1) {
     zero_out_head<OT>(s, c.H, e, h, lane);
@@ -1725,15 +1766,32 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
     wave_sync();  // the fold's xT reads done before the readout rewrites xT
   }
 
-  // 3. the readout's loads, then the new tile's stores (in this order: one
-  //    counter tracks a wave's loads and stores in issue order, so loads
-  //    issued after the stores would wait for the writes)
-  load_window<ST, OT, KW, HAS_Z>(c, s, e, h, lane, ld);
+  // 3. the readout's loads, C.B of the group and the new tile's stores.  One
+  //    counter tracks a wave's loads and stores in issue order: loads issued
+  //    after the stores would wait for the writes, and once the stores sit
+  //    behind a branch (k > 0) the compiler can no longer count which loads
+  //    are still in flight, so a use of loaded values after them waits for
+  //    the stores too.  For 8- and 4-bit checkpoints the C.B MFMAs (which need
+  //    the last of the loads) therefore go before the stores and the window
+  //    loads are unbranched; the 16- and 32-bit tiles hold too many registers
+  //    for that order (it spills), so they store first.
+  constexpr bool kCbFirst = kEarly;
+  load_window<ST, OT, KW, HAS_Z, kCbFirst>(c, s, e, h, lane, ld);
   ItemLoads<ST, KW> il;
   load_item_c<ST, KW>(c, s, e, g, lane, il);
   constexpr bool kShareC = cb_qorder(ST);  // C.B takes the readout's C chunks
   CbLoads<KW> cl;
   load_cb<KW>(c, s, e, g, lane, cl, !kShareC, kShareC);
+  auto cb_to_lds = [&]() {
+    if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl, kShareC);
+    f32x4 cb[KW / 16];
+    cb_tiles<KW>(cl, cb, kShareC ? il.craw : nullptr);
+#pragma unroll
+    for (int nb = 0; nb < KW / 16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cbw[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
+  };
+  if constexpr (kCbFirst) cb_to_lds();
   if (e.k > 0) {
     if constexpr (ST == kNVFP4) {
       store_nvfp4(c, e.slot, h, lane, ld.raw, ld.sfw, ld.gs);
@@ -1750,19 +1808,11 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
     if constexpr (ST == kFP8)  // lane l holds row l's new scale (row 16 q + m is in rb = q)
       (reinterpret_cast<float *>(c.scale + (int64_t)e.slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(fl.osc[0], fl.osc[1], fl.osc[2], fl.osc[3], q);
   }
+  if constexpr (!kCbFirst) cb_to_lds();
 
-  // 4. C.B of the group, then the replay of the head from the (new) tile
-  if (h % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl, kShareC);
-  {
-    f32x4 cb[KW / 16];
-    cb_tiles<KW>(cl, cb, kShareC ? il.craw : nullptr);
-#pragma unroll
-    for (int nb = 0; nb < KW / 16; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cbw[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
-    wave_sync();
-    load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
-  }
+  // 4. the replay of the head from the (new) tile
+  wave_sync();  // C.B rows written by this wave -> read below
+  load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
   if constexpr (ST == kFP8 && !kAbLds) {  // row scales of the (new) tile, rows 16 rb + 4 q + j
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
