@@ -194,3 +194,62 @@ def test_fp8_fold_extreme_rows(kind):
     sc = [gpu.scale_view(s).astype(np.float64) for s in (2, 3, 4)]
     assert np.min(sc[1]) > 2.0 ** 70 and np.median(sc[2]) > 2.0 ** 100, (np.min(sc[1]), np.median(sc[2]))
     gh.check_state(spec, gpu, ref_cache, cache, [1, 2, 3, 4, 5], (step.slot_idx, k, step.A))
+
+
+def _with_empty_entries(step, empty):
+    """The varlen step with the entries in `empty` given no new tokens."""
+    cu = step.cu_seqlens
+    tb = np.diff(cu).astype(np.int32)
+    tb[empty] = 0
+    rows = np.concatenate([np.arange(cu[b], cu[b] + tb[b]) for b in range(step.batch)]).astype(np.int64)
+    cu2 = np.zeros(step.batch + 1, np.int32)
+    cu2[1:] = np.cumsum(tb)
+    return synth.StepInputs(**{**step.__dict__, "cu_seqlens": cu2, "x": step.x[rows], "B": step.B[rows],
+                               "C": step.C[rows], "dt": step.dt[rows]})
+
+
+@pytest.mark.parametrize("state_dtype", ["fp8", "f16"])
+def test_fused_empty_windows(state_dtype):
+    """Varlen entries without new tokens: some fold their whole live prefix
+    (an empty readout window after the fold), some have nothing live either,
+    one is the last entry (its first row is the end of the packed inputs).
+    Against the oracle, and bit for bit against the GPU's flush then step."""
+    spec = synth.CacheSpec(num_slots=40, nheads=32, ngroups=4, state_dtype=state_dtype)
+    cache = synth.make_cache(spec, 6100)
+    step = synth.make_step(spec, 12, 4, 6101, 6, varlen=True)
+    step.pnat[[1, 4, 11]] = [5, 3, 2]
+    step.pnat[7] = 0
+    step = _with_empty_entries(step, [1, 4, 7, 11])
+    k = _fold_counts(step, 6102)
+    k[[1, 4, 11]] = step.pnat[[1, 4, 11]]  # fold everything live: nothing left to read out
+    k[7] = 0
+    print("case empty windows", state_dtype, "Tb", np.diff(step.cu_seqlens), "pnat", step.pnat, "k", k, flush=True)
+    out, gpu, status = _run_fused(spec, cache, step, "bf16", k)
+    assert status == 0
+    ref_cache = cache.copy()
+    ref, st = O.replay_step(ref_cache, step, num_fold=k)
+    assert st == 0
+    got = gh.to_f64(out)
+    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
+    excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, "bf16") * (1.0 + np.abs(ref)) - extra
+    assert np.all(excess <= 1e-12), "max excess %g" % np.max(excess)
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
+    assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
+    assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
+    touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
+    # the same bits as the flush kernel followed by the plain step
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    st_in = sd.upload_step(step, gh.DEV)
+    ssu.flush(dc, st_in["slot_idx"], torch.from_numpy(k).to(gh.DEV), st_in["A"])
+    step2 = synth.StepInputs(**{**step.__dict__, "pnat": (step.pnat - k).astype(np.int32)})
+    st2 = sd.upload_step(step2, gh.DEV)
+    out_s = gh.out_tensor(step, spec, "bf16")
+    gh.run_step(dc, st2, step2, out_s, "bf16", "monolith")
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == 0
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+    gpu_s = sd.download_cache(spec, t)
+    for f in sd.CACHE_FIELDS:
+        assert np.array_equal(getattr(gpu, f), getattr(gpu_s, f)), f

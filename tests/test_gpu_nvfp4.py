@@ -209,3 +209,36 @@ def test_nvfp4_plain_step_parity(varlen):
     assert st_ == 0
     got = gh.to_f64(outs[0])
     assert gh.rel_err(got, ref) <= 2e-2, gh.rel_err(got, ref)
+
+
+def test_nvfp4_fused_empty_windows_equal_flush_then_step():
+    """Varlen entries without new tokens, some folding their whole live prefix
+    (empty readout window): the fused step gives the GPU's flush-then-step bits."""
+    from tests.test_gpu_fused import _with_empty_entries
+    spec = _spec(16, num_slots=24, nheads=16, ngroups=2)
+    cache = synth.make_cache(spec, 81)
+    step = synth.make_step(spec, 11, 4, 82, 6, varlen=True)
+    step.pnat[[0, 5, 10]] = [4, 2, 6]
+    step.pnat[3] = 0
+    step = _with_empty_entries(step, [0, 3, 5, 10])
+    k = _fold_counts(step, 83)
+    k[[0, 5, 10]] = step.pnat[[0, 5, 10]]
+    k[3] = 0
+    seed = 87
+    print("nvfp4 empty windows Tb", np.diff(step.cu_seqlens), "pnat", step.pnat, "k", k, flush=True)
+    out_f, gpu_f, st_f = _run_fused(spec, cache, step, k, seed)
+    assert st_f == 0
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    st = sd.upload_step(step, gh.DEV)
+    ssu.flush(dc, st["slot_idx"], torch.from_numpy(k).to(gh.DEV), st["A"], sr_seed=seed)
+    step2 = synth.StepInputs(**{**step.__dict__, "pnat": (step.pnat - k).astype(np.int32)})
+    st2 = sd.upload_step(step2, gh.DEV)
+    out_s = gh.out_tensor(step, spec, "bf16")
+    gh.run_step(dc, st2, step2, out_s, "bf16", "monolith")
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == 0
+    gpu_s = sd.download_cache(spec, t)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    for f in sd.CACHE_FIELDS + ("recur", "gscale", "ring_start"):
+        assert np.array_equal(getattr(gpu_f, f), getattr(gpu_s, f)), f
