@@ -57,6 +57,8 @@ constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
   (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
 #endif
 constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
+// (entry, head) pairs from which a plain bf16 step runs one head per wave
+constexpr int64_t kPerHeadPlainUnits = 32768;
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
 constexpr int kCbLds = 36;       // LDS row stride (fp32) of C.B in the monolith
 constexpr int kHeadElems = kHeadDim * kDState;
@@ -1985,7 +1987,7 @@ hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
   else
     fused_kernel<ST, OT, 32, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles, ntiles);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || !s.fold) return err;  // nothing folded: ring_start stays
   step_ring_advance_kernel<ST><<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
   return hipGetLastError();
 }
@@ -2013,6 +2015,15 @@ template <int ST, int OT>
 hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
   if (s.fold) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
+  // A plain step with a bf16 checkpoint and enough (entry, head) pairs runs in
+  // the one-head-per-wave kernel with nothing to fold (its readout is the same
+  // arithmetic, bit for bit): at 3 waves per SIMD it measured 1-3 % faster
+  // than the persistent kernel from 32768 pairs up (batch 256-1024 of 128
+  // heads, varlen or not), 1.5-5 % slower for fp16 (2 waves per SIMD there).
+  if constexpr (ST == kBF16) {
+    if ((int64_t)s.batch * c.H >= kPerHeadPlainUnits)
+      return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
+  }
   return s.z ? replay_z<ST, OT, false, true>(c, s, st) : replay_z<ST, OT, false, false>(c, s, st);
 }
 
