@@ -57,7 +57,7 @@ constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
   (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
 #endif
 constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
-// (entry, head) pairs from which a plain bf16 step runs one head per wave
+// (entry, head) pairs from which a plain bf16 or fp8 step runs one head per wave
 constexpr int64_t kPerHeadPlainUnits = 32768;
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
 constexpr int kCbLds = 36;       // LDS row stride (fp32) of C.B in the monolith
@@ -202,9 +202,9 @@ struct Entry {
   int mode;  // 0: skip entirely, 1: zero the output rows only, 2: replay
 };
 
-// The per-entry words of a fused step, loaded without branches so that they
-// go out together: a word that does not apply is read from another valid
-// address and ignored (the fused step always has num_fold).
+// The per-entry words of a step in the one-head-per-wave kernel, loaded
+// without branches so that they go out together: a word that does not apply
+// (no varlen, no num_fold) is read from another valid address and ignored.
 struct EntryIn {
   int bos, eos, pnat, fold, ring_word;
 };
@@ -214,14 +214,15 @@ __device__ __forceinline__ EntryIn load_entry_in(const KCache &c, const KStep &s
   const int32_t *cu0 = varlen ? s.cu + b : s.pnat + b;
   const int32_t *cu1 = varlen ? s.cu + b + 1 : s.pnat + b;
   const int32_t *rs = c.ring_start + (slot_ok ? slot : 0);
-  int w0 = *cu0, w1 = *cu1, pn = s.pnat[b], kf = s.fold[b], rw = *rs;
+  const int32_t *kp = s.fold ? s.fold + b : s.pnat + b;
+  int w0 = *cu0, w1 = *cu1, pn = s.pnat[b], kf = *kp, rw = *rs;
   // an empty statement that takes and gives back the five words: the loads
   // cannot be moved into the branches that use them, so they are issued
   // together and waited for once
   asm volatile("" : "+s"(w0), "+s"(w1), "+s"(pn), "+s"(kf), "+s"(rw));
   EntryIn in;
   in.pnat = pn;
-  in.fold = kf;
+  in.fold = s.fold ? kf : 0;
   in.ring_word = rw;
   in.bos = varlen ? w0 : b * s.T;
   in.eos = varlen ? w1 : in.bos + s.T;
@@ -1716,7 +1717,7 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
     // never used), so that the tile loads are not behind a branch.
     const int slot = slot_ok ? slot0 : 0;
     bool recur_tile = false;
-    if constexpr (SEP) recur_tile = slot_ok && s.fold[b] > 0;
+    if constexpr (SEP) recur_tile = slot_ok && s.fold && s.fold[b] > 0;
     if (recur_tile) {
       const uint8_t *rp = c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
 #pragma unroll
@@ -2015,13 +2016,15 @@ template <int ST, int OT>
 hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
   if (s.fold) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
-  // A plain step with a bf16 checkpoint and enough (entry, head) pairs runs in
-  // the one-head-per-wave kernel with nothing to fold (its readout is the same
-  // arithmetic, bit for bit): at 3 waves per SIMD it measured 1-3 % faster
-  // than the persistent kernel from 32768 pairs up (batch 256-1024 of 128
-  // heads, varlen or not), 1.5-5 % slower for fp16 (2 waves per SIMD there).
-  if constexpr (ST == kBF16) {
-    if ((int64_t)s.batch * c.H >= kPerHeadPlainUnits)
+  // A plain step with enough (entry, head) pairs and a bf16 checkpoint, or an
+  // fp8 one without the recurrence checkpoint, runs in the one-head-per-wave
+  // kernel with nothing to fold (its readout is the same arithmetic, bit for
+  // bit).  Measured against the persistent kernel from 32768 pairs up: bf16
+  // 1-3 % faster (batch 256-1024 of 128 heads, varlen or not), fp8 10 %
+  // faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint 20 % and
+  // nvfp4 57 % slower (those forms of it hold more registers).
+  if constexpr (ST == kBF16 || ST == kFP8) {
+    if ((ST == kBF16 || !c.recur) && (int64_t)s.batch * c.H >= kPerHeadPlainUnits)
       return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
   }
   return s.z ? replay_z<ST, OT, false, true>(c, s, st) : replay_z<ST, OT, false, false>(c, s, st);

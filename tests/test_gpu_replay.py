@@ -49,9 +49,11 @@ CASES = {
                         batch=5, T=16, pnat_max=16, out="f32"),
     "f16_hpg1": dict(spec=dict(num_slots=12, nheads=6, ngroups=6, state_dtype="f16", ring_len=12),
                      batch=7, T=5, pnat_max=7, out="bf16"),
-    # 256 x 128 = 32768 (entry, head) pairs: a plain bf16 monolith step runs one head per wave
+    # 256 x 128 = 32768 (entry, head) pairs: a plain bf16 or fp8 monolith step runs one head per wave
     "bf16_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="bf16"), batch=256, T=4,
                           pnat_max=8, out="bf16", varlen=True, n_padding=3),
+    "fp8_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="fp8"), batch=256, T=4,
+                         pnat_max=12, out="bf16", n_padding=2),
 }
 
 
