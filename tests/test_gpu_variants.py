@@ -79,6 +79,15 @@ def test_variant_parity(case, with_z, dt_softplus):
     assert torch.equal(outs[0].view(view), outs[1].view(view))
 
 
+@pytest.mark.parametrize("with_z,dt_softplus", [(True, True), (True, False)])
+@pytest.mark.parametrize("case", ["bf16_per_head", "fp8_per_head"])
+def test_variant_parity_one_head_per_wave(case, with_z, dt_softplus):
+    """At 256 x 128 (entry, head) pairs a plain bf16 / fp8 monolith step runs
+    one head per wave: the variants there, against the oracle and bit for bit
+    against the split (persistent) kernel."""
+    test_variant_parity(case, with_z, dt_softplus)
+
+
 @pytest.mark.parametrize("case", ["fp8", "prod_f16"])
 def test_variants_with_fused_flush(case):
     spec, cache, step, out_dtype = _setup(case, 6100 + len(case), True, False)
