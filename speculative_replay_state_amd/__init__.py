@@ -202,12 +202,17 @@ class DeviceCache:
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
                    out_dtype="bf16", workspace=None, algo="auto", num_fold=None, z=None,
                    dt_softplus=True, sr_seed=0) -> SsuStep:
-    return SsuStep(
+    desc = SsuStep(
         batch, max_seqlen, _ptr(slot_idx), _ptr(pnat), _ptr(cu_seqlens),
         _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
         _ptr(out), SSU_F32 if out_dtype == "f32" else SSU_BF16,
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         ALGO_CODES[algo], _ptr(num_fold), _ptr(z), 0 if dt_softplus else 1, int(sr_seed))
+    # The descriptor holds raw device pointers: it keeps the tensors they point
+    # into alive, so that memory a kernel (or a captured graph) writes is never
+    # handed to another tensor while the descriptor is in use.
+    desc._tensors = (slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out, workspace, num_fold, z)
+    return desc
 
 
 def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:

@@ -165,3 +165,21 @@ def test_product_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h", ".cuh")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.lower(), f
+
+
+def test_step_desc_keeps_its_tensors_alive(ssu):
+    """The step descriptor holds raw pointers; it must keep the tensors behind
+    them (the split workspace among them) alive until it is dropped."""
+    import gc
+    import weakref
+    import torch
+    ws = torch.empty(16)
+    t = torch.zeros(4, dtype=torch.int32)
+    ref = weakref.ref(ws)
+    d = ssu.make_step_desc(1, 1, t, t, None, t, t, t, t, t, t, t, t, workspace=ws)
+    del ws
+    gc.collect()
+    assert ref() is not None and d.workspace_bytes == 64
+    del d
+    gc.collect()
+    assert ref() is None

@@ -1,0 +1,90 @@
+"""HIP-graph capture of the library's calls.
+
+The entry points enqueue kernels only (no allocation, no synchronisation, no
+memset), so a sequence of them can be captured once and replayed.  Checked on
+the GPU through the C ABI: a captured sequence (a fused fold-and-step, a plain
+monolith step, a plain split step with its workspace, a flush) is replayed
+three times on one copy of a cache, with the same calls run eagerly on a
+second copy between the replays; outputs, caches and status words must match
+bit for bit after every replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import device as sd
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import gpu_harness as gh
+    import speculative_replay_state_amd as ssu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# (num_slots, nheads, ngroups, batch): the second is large enough (256 x 128
+# pairs) for the plain fp8 monolith step to run one head per wave
+SHAPES = {"small": (40, 32, 4, 12), "per_head": (300, 128, 8, 256)}
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_graph_replays_match_eager(shape):
+    num_slots, H, G, batch = SHAPES[shape]
+    spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype="fp8")
+    cache = synth.make_cache(spec, 7100 + H)
+    step = synth.make_step(spec, batch, 4, 7101 + H, 8, n_padding=2)
+    rng = np.random.default_rng(7102)
+    k = np.array([rng.integers(0, int(p) + 1) for p in step.pnat], np.int32)
+    k2 = np.minimum(step.pnat, 2).astype(np.int32)
+    st = sd.upload_step(step, gh.DEV)
+    kt = torch.from_numpy(k).to(gh.DEV)
+    k2t = torch.from_numpy(k2).to(gh.DEV)
+    print("case graph", shape, "batch", batch, "H", H, flush=True)
+
+    def make(t):
+        dc = gh.device_cache(spec, t)
+        outs = [gh.out_tensor(step, spec, "bf16") for _ in range(3)]
+        ws = torch.empty(max(ssu.workspace_size(dc, step.batch, step.T) // 4, 1), dtype=torch.float32,
+                         device=gh.DEV)
+        descs = [ssu.make_step_desc(step.batch, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"],
+                                    st["B"], st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, "bf16",
+                                    w, algo, num_fold=f)
+                 for out, w, algo, f in ((outs[0], None, "auto", kt), (outs[1], None, "monolith", None),
+                                         (outs[2], ws, "split", None))]
+        return dc, outs, descs
+
+    def calls(dc, descs):
+        for d in descs:
+            ssu.replay_step(dc, d)
+        ssu.flush(dc, st["slot_idx"], k2t, st["A"])
+
+    # every path once, eagerly, on a scratch copy (the library caches an
+    # occupancy query per kernel on first use)
+    dcw, _, descw = make(sd.upload_cache(cache, gh.DEV))
+    calls(dcw, descw)
+    torch.cuda.synchronize()
+    assert int(dcw.status.item()) == 0
+
+    ta, tb = sd.upload_cache(cache, gh.DEV), sd.upload_cache(cache, gh.DEV)
+    dca, outa, desca = make(ta)
+    dcb, outb, descb = make(tb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(dca, desca)
+    for rep in range(3):
+        graph.replay()
+        calls(dcb, descb)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outa, outb)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "replay %d, output %d" % (rep, i)
+        ga, gb = sd.download_cache(spec, ta), sd.download_cache(spec, tb)
+        for f in sd.CACHE_FIELDS + ("ring_start",):
+            assert np.array_equal(getattr(ga, f), getattr(gb, f)), "replay %d, %s" % (rep, f)
+        assert int(dca.status.item()) == 0 and int(dcb.status.item()) == 0
