@@ -209,6 +209,8 @@ struct EntryIn {
   int bos, eos, pnat, fold, ring_word;
 };
 
+// kUniform: b is the same in the whole wave (scalar loads); else one entry per lane.
+template <bool kUniform = true>
 __device__ __forceinline__ EntryIn load_entry_in(const KCache &c, const KStep &s, int b, int slot, bool slot_ok) {
   const bool varlen = s.cu != nullptr;
   const int32_t *cu0 = varlen ? s.cu + b : s.pnat + b;
@@ -219,7 +221,10 @@ __device__ __forceinline__ EntryIn load_entry_in(const KCache &c, const KStep &s
   // an empty statement that takes and gives back the five words: the loads
   // cannot be moved into the branches that use them, so they are issued
   // together and waited for once
-  asm volatile("" : "+s"(w0), "+s"(w1), "+s"(pn), "+s"(kf), "+s"(rw));
+  if constexpr (kUniform)
+    asm volatile("" : "+s"(w0), "+s"(w1), "+s"(pn), "+s"(kf), "+s"(rw));
+  else
+    asm volatile("" : "+v"(w0), "+v"(w1), "+v"(pn), "+v"(kf), "+v"(rw));
   EntryIn in;
   in.pnat = pn;
   in.fold = s.fold ? kf : 0;
@@ -1974,7 +1979,11 @@ template <int ST>
 __global__ void step_ring_advance_kernel(KCache c, KStep s) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= s.batch) return;
-  const Entry e = load_entry(c, s, b, false);
+  // the slot, then every other word at once: two memory round trips, not a
+  // chain of one per check
+  const int slot = s.slot_idx[b];
+  const bool slot_ok = slot > 0 && slot < c.num_slots;
+  const Entry e = make_entry(c, s, slot, load_entry_in<false>(c, s, b, slot, slot_ok), false);
   if (e.mode == 2 && e.k > 0) c.ring_start[e.slot] = e.r;
 }
 
