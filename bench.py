@@ -387,7 +387,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": (measured_traffic(dominant, args.workload + ("_fused" if fused else "")
                                          + ("_separate" if args.separate else ""))
-                        if batch == wl_batch else None),
+                        if batch == wl_batch and algo_used == "monolith" else None),  # as the summaries were taken
         },
         "kernels": kernels,
         "hbm_stream": dict(streams, frac_of_copy=achieved / streams["copy_GBps"]),
