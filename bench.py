@@ -1,32 +1,38 @@
 """Benchmark of the ReplaySSM hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload fp8|nvfp4|prod|mtp|large|tiny]
-                    [--algo auto|monolith|split] [--batch B] [--no-cpu-baseline]
-                    [--no-fuse] [--separate]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload large|fp8|nvfp4|prod|mtp|tiny] [--algo auto|monolith|split]
+                    [--batch B] [--no-cpu-baseline] [--no-extra] [--no-fuse] [--separate]
 
-One step = one pass of the whole hot path over one batch: the replay step
-(dt' softplus, decay prefix, C.B, checkpoint replay and readout, ring appends)
-and, for the fp8 workload, the flush (fold of the accepted tokens, fp8
-re-encode, ring_start advance).  The default workload is the quantised-
-checkpoint configuration: batch 256 of the cache's slots, 128 heads in 8
-groups, headdim 64, dstate 128, fp8 e4m3 checkpoint with fp32 row scales,
-T = 4 new tokens, k ~ U{1..4} accepted tokens flushed every step.  By
-default the flush is fused into the step: each call folds the k tokens the
-previous step accepted (pnat = num_fold = k) and then replays the 4 new ones,
-reading each checkpoint once; --no-fuse times the step with pnat = 0 followed
-by a separate ssu_flush of k tokens instead.  --separate (fp8 workload) adds
-the FP16 recurrence checkpoint: folds read and write it (stochastic rounding,
-a new seed every call) and write the fp8 read checkpoint the steps read.
+One step = one pass of the hot path over one batch of synthetic input: the
+replay step (dt' softplus, decay prefix, C.B, checkpoint replay and readout,
+ring appends) and, for the flushing workloads, the flush (fold of the
+accepted tokens, re-encode, ring_start advance).
+
+The headline workload is the largest single-GPU configuration: 1024 active
+entries of a 2048-slot cache (slot 0 padding, 256 B of padding between slot
+pages), 128 heads in 8 groups, headdim 64, dstate 128, bf16 checkpoint,
+varlen T_b ~ U{1..8} new tokens per entry, pnat ~ U{0..8} live ring tokens,
+ring length 16.  The same JSON line carries, under "extra", the quantised-
+checkpoint loop (fp8 e4m3 checkpoint with fp32 row scales, batch 256, T = 4,
+k ~ U{1..4} accepted tokens folded every step inside the step), the only
+configuration that runs every flush row.
 
 Inputs are synthetic, drawn on the GPU (synth package) and resident in HBM
 before timing.  To measure HBM rather than the 256 MB Infinity Cache the
-cache holds `--arenas` disjoint sets of `batch` slots (>= 2 GiB in total) and
-consecutive steps rotate through them.  The timed region replays a HIP graph
-of K steps between two stream synchronisations; per-kernel durations come
-from HIP events on the same stream.
+cache holds disjoint sets of `batch` slots (>= 2 GiB in total) and
+consecutive steps rotate through them.
 
-Prints one JSON line (metric, value = replayed tokens/s, roofline of the
-dominant kernel, CPU-oracle baseline).
+Timing protocol: W eager warmup steps; a HIP graph of K steps is captured;
+the graph is replayed for a settle phase of about --settle seconds (reported
+on its own: a GPU that has been idle runs its first milliseconds at lower
+clocks); then --trials replays of the K-step graph, each bracketed by HIP
+events on the launch stream between two synchronisations.  ms_per_step is
+the median trial / K (min and max reported).  The roofline of the dominant
+kernel comes from the same timed replays (its launches per step are stated),
+with the eager per-call event times beside it.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -47,11 +53,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "replayed SSU tokens/sec and achieved HBM GB/s (% of MI355X peak) at 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+HEADLINE = "large"
+EXTRA = "fp8"
 
 WORKLOADS = {
     "nvfp4": dict(nheads=128, ngroups=8, state_dtype="nvfp4", batch=256, T=4, pnat_max=0, out="bf16",
                   flush=(1, 4), varlen=False, slot_pad=0, separate=True,
-                  desc="NVFP4 read checkpoint (e2m1, e4m3 block scales, f32 head scale) + FP16 recurrence "
+                  desc="NVFP4 read checkpoint (e2m1, e4m3 block scales, f32 slot scale) + FP16 recurrence "
                        "checkpoint with stochastic rounding, batch 256, H128 G8, P64 N128, T=4, fold "
                        "k~U{1..4} every step, L=16"),
     "fp8": dict(nheads=128, ngroups=8, state_dtype="fp8", batch=256, T=4, pnat_max=0, out="bf16",
@@ -64,26 +72,30 @@ WORKLOADS = {
                       "L=16, ring_start~U{0..15}"),
     "mtp": dict(nheads=64, ngroups=8, state_dtype="bf16", batch=64, T=4, pnat_max=4, out="bf16",
                 flush=None, varlen=False, slot_pad=0,
-                desc="MTP decode, bf16 checkpoint, batch 64, H64 G8, P64 N128, T=4, pnat~U{0..4}, L=16"),
+                desc="MTP decode, bf16 checkpoint, batch 64 of 128 slots, H64 G8, P64 N128, T=4, "
+                     "pnat~U{0..4}, L=16"),
     "large": dict(nheads=128, ngroups=8, state_dtype="bf16", batch=1024, T=8, pnat_max=8, out="bf16",
                   flush=None, varlen=True, slot_pad=256,
-                  desc="large batch, bf16 checkpoint, 1024 active slots, H128 G8, P64 N128, varlen "
-                       "T_b~U{1..8}, pnat~U{0..8}, L=16, 256 B padding between slot pages"),
+                  desc="large batch, bf16 checkpoint, 1024 active of 2048 slots, H128 G8, P64 N128, "
+                       "varlen T_b~U{1..8}, pnat~U{0..8}, L=16, 256 B padding between slot pages"),
     "tiny": dict(nheads=8, ngroups=1, state_dtype="f32", batch=2, T=1, pnat_max=8, out="f32",
                  flush=None, varlen=False, slot_pad=0,
-                 desc="tiny reference, fp32 checkpoint, batch 2, H8 G1, T=1"),
+                 desc="tiny reference, fp32 checkpoint, batch 2 of 4 slots, H8 G1, T=1"),
 }
+
+# the arithmetic type of the readout products (MFMA inputs; every sum is fp32)
+COMPUTE_DTYPE = {"f32": "f32", "bf16": "bf16", "f16": "f16", "fp8": "bf16", "nvfp4": "bf16"}
 
 ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "nvfp4": 0.5}
 
 
 def scale_bytes(spec, H):
     """Scale bytes read or written with one slot's checkpoint: fp8 an f32 per
-    row, nvfp4 an e4m3 per 16 values and an f32 per head."""
+    row, nvfp4 an e4m3 per 16 values and the slot's f32 scale."""
     if spec.state_dtype == "fp8":
         return H * 64 * 4
     if spec.state_dtype == "nvfp4":
-        return H * (64 * 128 // 16 + 4)
+        return H * (64 * 128 // 16) + 4
     return 0
 
 
@@ -137,67 +149,68 @@ def flush_bytes(spec, H, G, k):
     return int(sum(2 * per_state + int(kk) * (H * P * 2 + G * N * 2 + H * 4) for kk in k if kk > 0))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="fp8", choices=sorted(WORKLOADS))
-    ap.add_argument("--algo", default="auto", choices=["auto", "monolith", "split"])
-    ap.add_argument("--batch", type=int, default=None)
-    ap.add_argument("--arenas", type=int, default=None, help="disjoint slot sets rotated per step")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    ap.add_argument("--seed", type=int, default=1234)
-    ap.add_argument("--fuse", action=argparse.BooleanOptionalAction, default=True,
-                    help="flush workloads: fold the accepted tokens inside the replay step (one "
-                         "ssu_replay_step with num_fold) instead of a separate ssu_flush call")
-    ap.add_argument("--separate", action="store_true",
-                    help="fp8 workload: separate FP16 recurrence checkpoint (stochastic rounding)")
-    args = ap.parse_args()
+# ---------------------------------------------------------------------------
+# GPU clocks (amdsmi, when it imports on the box)
+# ---------------------------------------------------------------------------
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the ReplaySSM step has no cross-GPU exchange "
-              "(slots and heads shard without communication); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
-        sys.exit(2)
+class Clocks:
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if hs:
+                self.amdsmi, self.h = amdsmi, hs[0]
+        except Exception:  # no amdsmi, or no permission: clocks are reported as null
+            self.h = None
 
+    def sample(self):
+        if self.h is None:
+            return None
+        out = {}
+        for name, kind in (("sclk_mhz", "GFX"), ("mclk_mhz", "MEM")):
+            try:
+                info = self.amdsmi.amdsmi_get_clock_info(self.h, getattr(self.amdsmi.AmdSmiClkType, kind))
+                out[name] = info.get("clk")
+                out[name.replace("_mhz", "_max_mhz")] = info.get("max_clk")
+            except Exception:
+                out[name] = None
+        return out
+
+
+# ---------------------------------------------------------------------------
+# one workload: cache, steps, graph, timed trials
+# ---------------------------------------------------------------------------
+
+def run_workload(args, name, clocks, dev, batch=None, cpu=False):
     import speculative_replay_state_amd as ssu
     import synth
     from synth import device as sd
 
-    wl = dict(WORKLOADS[args.workload])
+    wl = dict(WORKLOADS[name])
     wl_batch = wl["batch"]
+    separate = bool(wl.get("separate")) or (args.separate and name == args.workload)
     fused = bool(wl["flush"]) and args.fuse
-    if wl.get("separate"):
-        args.separate = True  # an nvfp4 read checkpoint always has the recurrence checkpoint
-    if args.separate and (not wl["flush"] or wl["state_dtype"] not in ("fp8", "nvfp4")):
-        print("--separate needs a workload with flushes and an fp8 checkpoint (fp8)", file=sys.stderr)
-        sys.exit(2)
-    if args.batch:
-        wl["batch"] = args.batch
+    if separate and (not wl["flush"] or wl["state_dtype"] not in ("fp8", "nvfp4")):
+        raise SystemExit("--separate needs a workload with flushes and an fp8 checkpoint (fp8)")
+    if batch:
+        wl["batch"] = batch
     batch, H, G, T = wl["batch"], wl["nheads"], wl["ngroups"], wl["T"]
-    dev = "cuda:0"
 
     # --- cache with rotating arenas (HBM, not the Infinity Cache) -----------
     probe = synth.CacheSpec(num_slots=2, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
-                            slot_pad=wl["slot_pad"], separate=args.separate)
-    st_ = probe.strides()
-    slot_bytes = sum(st_.values())
+                            slot_pad=wl["slot_pad"], separate=separate)
+    slot_bytes = sum(probe.strides().values())
     if args.arenas is None:
         arenas = max(1, math.ceil(2.2 * 2 ** 30 / (slot_bytes * batch)))
-        if args.workload == "large":
+        if name == "large" and batch == wl_batch:
             arenas = 2  # 2048 slots: 1024 active at a time, ~4.6 GB of checkpoints
     else:
         arenas = args.arenas
     num_slots = arenas * batch + 1
     spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype=wl["state_dtype"],
-                           slot_pad=wl["slot_pad"], separate=args.separate)
+                           slot_pad=wl["slot_pad"], separate=separate)
     tcache = sd.make_cache_device(spec, args.seed, dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     dc = ssu.DeviceCache(num_slots, H, G, spec.ring_len, spec.state_dtype, tcache["state"],
@@ -222,12 +235,13 @@ def main():
         t["out"] = torch.empty((stp.tokens, H, 64), dtype=out_dt, device=dev)
         tsteps.append(t)
     ws = None
-    algo_used = args.algo
     d0 = ssu.make_step_desc(batch, T, tsteps[0]["slot_idx"], tsteps[0]["pnat"], tsteps[0]["cu_seqlens"],
                             tsteps[0]["x"], tsteps[0]["B"], tsteps[0]["C"], tsteps[0]["dt"],
                             tsteps[0]["A"], tsteps[0]["D"], tsteps[0]["dt_bias"], tsteps[0]["out"],
                             wl["out"], None, args.algo, flush_k[0] if fused else None)
     resolved = ssu.ssu_resolve_algo(dc.desc(), d0)
+    if resolved < 0:
+        raise ssu.SsuError(resolved, ssu.ssu_last_error())
     algo_used = {ssu.SSU_ALGO_MONOLITH: "monolith", ssu.SSU_ALGO_SPLIT: "split"}[resolved]
     if algo_used == "split":
         ws = torch.empty(ssu.workspace_size(dc, batch, T) // 4 + 1, dtype=torch.float32, device=dev)
@@ -267,31 +281,58 @@ def main():
 
     K = args.steps
     graph = None
+    stream = torch.cuda.current_stream()
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(K):
                 one_step(args.warmup + i)
-        graph.replay()  # one untimed replay
         torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(K):
-            one_step(args.warmup + i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / K
 
-    # --- per-kernel durations (HIP events around each call, same stream) ----
+    def replay_once():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                one_step(args.warmup + i)
+
+    # --- settle: replay until the GPU has run for about --settle seconds ----
+    clk_before = clocks.sample()
+    torch.cuda.synchronize()
+    s0 = time.perf_counter()
+    settle_replays = 0
+    while True:
+        replay_once()
+        settle_replays += 1
+        if settle_replays % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - s0 >= args.settle:
+                break
+    torch.cuda.synchronize()
+    settle_s = time.perf_counter() - s0
+
+    # --- timed trials: each one replay of the K-step graph -------------------
+    clk_settled = clocks.sample()
+    trial_ms = []
+    wall_timed = 0.0
+    for _ in range(args.trials):
+        ta = torch.cuda.Event(enable_timing=True)
+        tb = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        ta.record(stream)
+        replay_once()
+        tb.record(stream)
+        torch.cuda.synchronize()
+        wall_timed += time.perf_counter() - w0
+        trial_ms.append(ta.elapsed_time(tb))
+    clk_after = clocks.sample()
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d after the timed replays" % int(status.item()))
+    ms_med = float(np.median(trial_ms))
+    ms_per_step = ms_med / K
+
+    # --- eager per-call durations (HIP events around each call, same stream) -
     nrep = min(K, 8 * arenas)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nrep)]
     torch.cuda.synchronize()
@@ -308,26 +349,128 @@ def main():
     tbs = [np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch for s in steps_in]
     if fused:
         sbytes = float(np.mean([fused_bytes(spec, H, G, k.cpu().numpy(), tb, ob)
-                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if args.separate else 0)
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if separate else 0)
                                 for k, tb in zip(flush_k, tbs)]))
         fbytes = 0.0
     else:
         sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat, tb, ob) for s, tb in zip(steps_in, tbs)]))
         fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy())
-                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if args.separate else 0)
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if separate else 0)
                                 for k in flush_k])) if flush_k else 0.0
+    # kernel launches per ssu_replay_step call (as dispatched for this workload)
+    launches = 1
+    if algo_used == "split":
+        launches = 2
+    elif fused:
+        launches = 2  # the fused kernel and its ring advance
     step_avg = float(np.mean(step_ms))
-    kernels = {"replay_step": {"algo": algo_used, "fused_flush": fused, "avg_us": 1e3 * step_avg,
-                               "bytes": sbytes, "GBps": sbytes / (step_avg * 1e6)}}
+    kernels = {"replay_step": {"algo": algo_used, "fused_flush": fused, "launches_per_call": launches,
+                               "eager_call_us": 1e3 * step_avg, "bytes": sbytes,
+                               "eager_GBps": sbytes / (step_avg * 1e6)}}
     dominant = "replay_step"
     if flush_ms:
         fl_avg = float(np.mean(flush_ms))
-        kernels["flush"] = {"avg_us": 1e3 * fl_avg, "bytes": fbytes, "GBps": fbytes / (fl_avg * 1e6)}
+        kernels["flush"] = {"eager_call_us": 1e3 * fl_avg, "bytes": fbytes, "eager_GBps": fbytes / (fl_avg * 1e6)}
         if fl_avg > step_avg:
             dominant = "flush"
-    dk = kernels[dominant]
-    achieved = dk["GBps"]
-    value = tokens_per_step * K / (ms_total * 1e-3)
+    # the roofline from the timed replays: a step that is one call (no separate
+    # flush) spends the whole step time in that call's launches
+    if not flush_ms:
+        call_us = 1e3 * ms_per_step
+        achieved = sbytes / (ms_per_step * 1e6)
+        timed_from = "timed graph replays (median trial / K steps)"
+    else:
+        call_us = kernels[dominant]["eager_call_us"]
+        achieved = kernels[dominant]["eager_GBps"]
+        timed_from = "eager per-call HIP events (a step holds a step and a flush call)"
+    value = tokens_per_step * K / (ms_med * 1e-3)
+
+    res = {
+        "name": name, "wl": wl, "spec": spec, "tcache": tcache, "steps_in": steps_in, "flush_k": flush_k,
+        "fused": fused, "separate": separate, "batch": batch, "H": H, "G": G, "T": T,
+        "value": value, "ms_per_step": ms_per_step, "trial_ms": trial_ms, "wall_timed": wall_timed,
+        "settle_s": settle_s, "settle_replays": settle_replays,
+        "clocks": {"before_settle": clk_before, "settled": clk_settled, "after_trials": clk_after},
+        "tokens_per_step": tokens_per_step, "positions_per_step": positions_per_step,
+        "sbytes": sbytes, "fbytes": fbytes, "algo": algo_used, "arenas": arenas, "num_slots": num_slots,
+        "graph": graph is not None, "kernels": kernels, "dominant": dominant, "call_us": call_us,
+        "achieved": achieved, "timed_from": timed_from, "launches": launches, "wl_batch": wl_batch,
+    }
+    if cpu and not args.no_cpu_baseline:
+        c = cpu_baseline(args, res)
+        c["effective_GBps"] = c["value"] * (sbytes + fbytes) / tokens_per_step / 1e9
+        res["cpu"] = c
+    return res
+
+
+def summary(res, K):
+    """The compact record of a workload run (the extra loop of the JSON line)."""
+    return {
+        "workload": res["name"] + ": " + res["wl"]["desc"],
+        "value": res["value"], "unit": "tokens/s", "ms_per_step": res["ms_per_step"],
+        "trials_ms_per_step": [t / K for t in res["trial_ms"]],
+        "algorithmic_bytes_per_step": res["sbytes"] + res["fbytes"],
+        "achieved_GBps_step": (res["sbytes"] + res["fbytes"]) / (res["ms_per_step"] * 1e6),
+        "frac_step": (res["sbytes"] + res["fbytes"]) / (res["ms_per_step"] * 1e6) / HBM_PEAK_GBS,
+        "kernels": res["kernels"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--trials", type=int, default=5, help="timed replays of the K-step graph (median)")
+    ap.add_argument("--settle", type=float, default=2.0, help="seconds of graph replays before the trials")
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--algo", default="auto", choices=["auto", "monolith", "split"])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--arenas", type=int, default=None, help="disjoint slot sets rotated per step")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the fp8 flush loop in the same line")
+    ap.add_argument("--no-streams", action="store_true", help="skip the plain HBM stream rates")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--fuse", action=argparse.BooleanOptionalAction, default=True,
+                    help="flush workloads: fold the accepted tokens inside the replay step (one "
+                         "ssu_replay_step with num_fold) instead of a separate ssu_flush call")
+    ap.add_argument("--separate", action="store_true",
+                    help="fp8 workload: separate FP16 recurrence checkpoint (stochastic rounding)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ReplaySSM step has no cross-GPU exchange "
+              "(slots and heads shard without communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.trials < 1:
+        print("--steps and --trials must be >= 1", file=sys.stderr)
+        sys.exit(2)
+
+    dev = "cuda:0"
+    clocks = Clocks()
+    K = args.steps
+    res = run_workload(args, args.workload, clocks, dev, batch=args.batch, cpu=True)
+    cpu = res.pop("cpu", None)
+    extra = None
+    if not args.no_extra and args.workload == HEADLINE and not args.batch:
+        # the headline's cache is freed first (the extra loop draws its own)
+        head_keep = {k: v for k, v in res.items() if k not in ("tcache",)}
+        del res
+        torch.cuda.empty_cache()
+        ex = run_workload(args, EXTRA, clocks, dev)
+        extra = {EXTRA + "_fused_flush": summary(ex, K)}
+        del ex
+        torch.cuda.empty_cache()
+        res = head_keep
+    else:
+        res.pop("tcache", None)
 
     # --- counter calibration copy (1 GiB), only when asked ------------------
     if args.calib_copy:
@@ -339,71 +482,93 @@ def main():
         del src, dst
 
     # --- what plain streams reach on this GPU (context for the roofline) ----
-    streams = hbm_streams(dev)
+    streams = None if args.no_streams else hbm_streams(dev)
 
-    # --- CPU oracle on a bounded sample of the same workload ----------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused)
-        # the oracle's effective rate in the same algorithmic bytes per token as the GPU line
-        cpu["effective_GBps"] = cpu["value"] * (sbytes + fbytes) / tokens_per_step / 1e9
-
+    wl, spec = res["wl"], res["spec"]
+    batch, H, G, T = res["batch"], res["H"], res["G"], res["T"]
+    name = res["name"]
+    achieved = res["achieved"]
+    fused, separate = res["fused"], res["separate"]
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": COMPUTE_DTYPE[wl["state_dtype"]],
         "data": "synthetic (seeded, drawn on the GPU; no dataset)",
         "config": {
-            "workload": args.workload + ": " + wl["desc"],
+            "workload": name + ": " + wl["desc"],
             "batch": batch, "nheads": H, "ngroups": G, "headdim": 64, "dstate": 128, "ring_len": 16,
-            "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "algo": algo_used,
-            "separate_checkpoints": (None if not args.separate else
+            "T": T, "state_dtype": wl["state_dtype"], "out_dtype": wl["out"], "accumulate": "f32",
+            "algo": res["algo"],
+            "separate_checkpoints": (None if not separate else
                                      "FP16 recurrence checkpoint, stochastic rounding, %s read checkpoint"
                                      % wl["state_dtype"]),
             "flush": (None if not wl["flush"] else
                       "fused into the replay step (ssu_replay_step with num_fold = pnat = k)" if fused
                       else "separate ssu_flush after the step"),
-            "arenas": arenas, "cache_slots": num_slots, "graph": graph is not None,
-            "tokens_per_step": tokens_per_step,
-            "replayed_positions_per_s": positions_per_step * K / (ms_total * 1e-3),
-            "algorithmic_bytes_per_step": sbytes + fbytes,
-            "achieved_GBps_step": (sbytes + fbytes) / (ms_per_step * 1e6),
-            "wall_s_timed": wall1 - wall0,
+            "arenas": res["arenas"], "cache_slots": res["num_slots"], "graph": res["graph"],
+            "tokens_per_step": res["tokens_per_step"],
+            "replayed_positions_per_s": res["positions_per_step"] * K / (res["ms_per_step"] * K * 1e-3),
+            "algorithmic_bytes_per_step": res["sbytes"] + res["fbytes"],
+            "achieved_GBps_step": (res["sbytes"] + res["fbytes"]) / (res["ms_per_step"] * 1e6),
+        },
+        "timing": {
+            "trials": len(res["trial_ms"]),
+            "steps_per_trial": K,
+            "ms_per_step_median": res["ms_per_step"],
+            "ms_per_step_min": min(res["trial_ms"]) / K,
+            "ms_per_step_max": max(res["trial_ms"]) / K,
+            "settle_s": res["settle_s"],
+            "settle_replays": res["settle_replays"],
+            "wall_s_timed": res["wall_timed"],
+            "clocks": res["clocks"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": dominant,
+            "kernel": res["dominant"],
+            "launches_per_call": res["launches"],
+            "call_us": res["call_us"],
+            "timed_from": res["timed_from"],
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": (measured_traffic(dominant, args.workload + ("_fused" if fused else "")
-                                         + ("_separate" if args.separate else ""))
-                        if batch == wl_batch and algo_used == "monolith" else None),  # as the summaries were taken
+            "traffic": (measured_traffic(res["dominant"], name + ("_fused" if fused else "")
+                                         + ("_separate" if separate else ""))
+                        if batch == res["wl_batch"] and res["algo"] == "monolith" else None),
         },
-        "kernels": kernels,
-        "hbm_stream": dict(streams, frac_of_copy=achieved / streams["copy_GBps"]),
+        "kernels": res["kernels"],
+        "hbm_stream": (None if streams is None else
+                       dict(streams, frac_of_copy=achieved / streams["copy_GBps"],
+                            frac_of_rmw=achieved / streams["rmw_GBps"])),
+        "extra": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def hbm_streams(dev, nbytes=2 ** 30, reps=5):
-    """GB/s of plain PyTorch streams over 1 GiB buffers on this GPU: a device
-    copy (half reads, half writes, like a read-modify-write of the
-    checkpoint) and a fill (writes).  Best of `reps`."""
+def hbm_streams(dev, nbytes=2 ** 31, reps=5):
+    """GB/s of plain PyTorch streams over 2 GiB buffers on this GPU: a device
+    copy (half reads, half writes), an in-place read-modify-write of one
+    buffer (x.mul_(1.0): every byte read and written back, as a checkpoint
+    fold does), a fill (writes only) and a sum (reads only).  Best of `reps`."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    ops = {"copy_GBps": (lambda: dst.copy_(src), 2 * nbytes), "write_GBps": (lambda: dst.fill_(2.0), nbytes)}
-    out = {}
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    ops = {
+        "copy_GBps": (lambda: dst.copy_(src), 2 * nbytes),
+        "rmw_GBps": (lambda: src.mul_(1.0), 2 * nbytes),
+        "write_GBps": (lambda: dst.fill_(2.0), nbytes),
+        "read_GBps": (lambda: torch.sum(src, dim=0, out=acc), nbytes),
+    }
+    out = {"bytes_per_buffer": nbytes}
     for name, (fn, moved) in ops.items():
         fn()
         best = float("inf")
@@ -415,18 +580,20 @@ def hbm_streams(dev, nbytes=2 ** 30, reps=5):
             torch.cuda.synchronize()
             best = min(best, a.elapsed_time(b))
         out[name] = moved / (best * 1e6)
-    del src, dst
+    del src, dst, acc
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused):
+def cpu_baseline(args, res):
     """The CPU oracle (as it stands) on a bounded sample: the first 64 entries
     of the first arena, step (+ flush), repeated until --cpu-seconds of work,
     once with every OpenMP thread the host offers and once with one thread."""
     from oracle import ssu_oracle as O
     from synth import device as sd
 
+    spec, tcache, steps_in, flush_k, fused = (res["spec"], res["tcache"], res["steps_in"], res["flush_k"],
+                                              res["fused"])
     step = steps_in[0]
     n = min(64, step.batch)
     entries = list(range(n))
@@ -458,9 +625,9 @@ def cpu_baseline(args, wl, spec, tcache, steps_in, flush_k, fused):
     v_one, reps1, el1 = timed(args.cpu_seconds / 2)
     O.set_threads(threads)
     return {"value": v_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d entries of the first batch, step%s, repeated %d times (%.1f s)" % (
-                n, step.batch, (" with fused flush" if fused else " + flush") if k is not None else "",
-                reps, el),
+            "sample": "%d of %d entries of the first batch (%d new tokens), step%s, repeated %d times (%.1f s)" % (
+                n, step.batch, sub.tokens,
+                (" with fused flush" if fused else " + flush") if k is not None else "", reps, el),
             "single_thread": {"value": v_one, "cores": 1, "repeats": reps1, "seconds": el1},
             "host": {"os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}}
 
