@@ -57,17 +57,22 @@
  *    read as stochastic rounding with 7 random bits per value (or_sr_f16),
  *    the bits coming from Philox4x32-10 keyed by a per-call 64-bit seed.
  *  - NVFP4 read checkpoint (same PR, Claims: FP8/NVFP4 read checkpoints with
- *    nearest encoding; the API page's init computes a maximum over a group's
- *    heads and a second-level scale max / (6 * 448)): e2m1 elements, an e4m3
- *    scale per block of 16 along dstate, and an fp32 second-level scale; the
- *    second-level scale is taken per (slot, head) here (encode_head_nvfp4),
- *    the unit one fold rewrites, so every flush re-derives it exactly.
+ *    nearest encoding; vLLM API page, initialize_replayssm_state, NVFP4
+ *    branch: the largest |value| of each group of heads, then their maximum
+ *    over the groups divided by 6 * 448, one second-level scale per slot,
+ *    1 where that is not positive): e2m1 elements, an e4m3 scale per block of
+ *    16 along dstate, one fp32 second-level scale g per slot.  The page shows
+ *    the encode only at init; a fold is read here as re-encoding the whole
+ *    slot the same way from its folded fp32 state (encode_slot_nvfp4), so the
+ *    read checkpoint is always the init encoding of the current state.
  *  - A padding entry (slot <= 0 or slot >= num_slots) writes zero output rows
  *    and touches no cache.  An entry with pnat < 0 or pnat + T_b > L is
  *    treated the same way and raises status bit 1; a flush entry with k < 0
  *    or k > L is skipped and raises status bit 2; a varlen entry whose token
  *    count is negative or above max_seqlen is skipped (no output written) and
- *    raises status bit 4.
+ *    raises status bit 4; a slot whose ring_start lies outside [0, L) is
+ *    skipped by the step (zero output rows) and by the flush, and raises
+ *    status bit 8.
  *
  * Layouts (all byte strides between slots are arguments; inside a slot the
  * layout is packed):
@@ -323,7 +328,8 @@ typedef struct {
    * state, element type fp16) or NULL when the state is the only checkpoint. */
   uint8_t *recur;
   int64_t recur_stride;
-  /* NVFP4 state only: the per-(slot, head) second-level scale, f32. */
+  /* NVFP4 state only, f32 [slot][1 + H]: word 0 the slot's second-level
+   * scale g, word 1 + h the largest |value| of head h when it was encoded. */
   uint8_t *gscale;
   int64_t gscale_stride;
 } or_cache;
@@ -348,8 +354,8 @@ static int64_t head_bytes(const or_cache *c) {
 /*
  * NVFP4 checkpoint (a reading of the pages' NVFP4 read checkpoint; the
  * layout is this library's): element (p, n) is an e2m1 code, blocks of 16
- * consecutive n of a row share an e4m3 block scale, and each (slot, head) has
- * an fp32 second-level scale g; the value is e2m1 * e4m3(block) * g.
+ * consecutive n of a row share an e4m3 block scale, and each slot has one
+ * fp32 second-level scale g; the value is e2m1 * e4m3(block) * g.
  * Codes, row-major: element p N + n in byte (p N + n) / 2, the even element
  * in the low nibble.  Tiled (P = 64, N = 128): the 32 values of quarter q of
  * row p (lane l = 16 q + m, rb = p / 16, m = p % 16, t = n % 32) fill the
@@ -375,10 +381,15 @@ static int64_t nvfp4_scale_byte(const or_cache *c, int p, int n) {
   return (int64_t)l * 8 + rb * 2 + t / 16;
 }
 
-static float nvfp4_gscale(const or_cache *c, int slot, int head) {
+/* Word w of a slot's NVFP4 scale words (0: g; 1 + h: head h's maximum). */
+static float nvfp4_word(const or_cache *c, int slot, int w) {
   float g;
-  memcpy(&g, c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)head * 4, 4);
+  memcpy(&g, c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)w * 4, 4);
   return g;
+}
+
+static void nvfp4_set_word(const or_cache *c, int slot, int w, float v) {
+  memcpy(c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)w * 4, &v, 4);
 }
 
 /* Byte offset of element (p, n) inside one head's checkpoint.
@@ -402,7 +413,7 @@ static void decode_state(const or_cache *c, int slot, int head, double *h) {
   const uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * head_bytes(c);
   if (c->state_dtype == OR_NVFP4) {
     const uint8_t *sf = c->scale + (int64_t)slot * c->scale_stride + (int64_t)head * (P * N / 16);
-    const double g = nvfp4_gscale(c, slot, head);
+    const double g = nvfp4_word(c, slot, 0);
     for (int p = 0; p < P; ++p)
       for (int n = 0; n < N; ++n) {
         int hi;
@@ -489,24 +500,16 @@ static void encode_row(const or_cache *c, int slot, int head, int p,
 }
 
 /*
- * Encode one head of an fp32 state into the NVFP4 checkpoint, nearest
- * encoding at both levels: g = fp32(max |v| / 2688) (2688 = 6 * 448: the
- * head's largest value maps to the largest e2m1 value times the largest
- * e4m3 value; 1 if not positive), and per block of 16 with a = max |v|:
+ * Encode one head of an fp32 state into the NVFP4 checkpoint with the slot's
+ * second-level scale g, nearest encoding: per block of 16 with a = max |v|,
  * block scale = e4m3_sat(fp32(a / fp32(6 g))), element scale
  * es = fp32(e4m3 value * g), code = e2m1_sat(fp32(v / es)) (a zero block
  * scale stores signed zeros).  IEEE single precision throughout.
  */
-static void encode_head_nvfp4(const or_cache *c, int slot, int head, const float *hv) {
+static void encode_head_nvfp4(const or_cache *c, int slot, int head, const float *hv, float g) {
   const int P = c->headdim, N = c->dstate;
   uint8_t *base = c->state + (int64_t)slot * c->state_stride + (int64_t)head * head_bytes(c);
   uint8_t *sf = c->scale + (int64_t)slot * c->scale_stride + (int64_t)head * (P * N / 16);
-  float m = 0.0f;
-  for (int i = 0; i < P * N; ++i)
-    if (fabsf(hv[i]) > m) m = fabsf(hv[i]);
-  float g = m / 2688.0f;
-  if (!(g > 0.0f)) g = 1.0f;
-  memcpy(c->gscale + (int64_t)slot * c->gscale_stride + (int64_t)head * 4, &g, 4);
   const float ds = 6.0f * g;
   for (int p = 0; p < P; ++p)
     for (int n0 = 0; n0 < N; n0 += 16) {
@@ -526,6 +529,30 @@ static void encode_head_nvfp4(const or_cache *c, int slot, int head, const float
         *byte = hi ? (uint8_t)((*byte & 0x0F) | (e << 4)) : (uint8_t)((*byte & 0xF0) | e);
       }
     }
+}
+
+/*
+ * Encode a whole slot of fp32 values hv[H][P][N] into the NVFP4 checkpoint,
+ * as initialize_replayssm_state's NVFP4 branch does (vLLM API page): the
+ * second-level scale is the largest |value| over every head of the slot
+ * divided by 6 * 448 = 2688 (the largest e2m1 value times the largest e4m3
+ * value), in IEEE single precision, and 1 where that is not positive.  Word
+ * 1 + h of the slot's scale words records head h's largest |value|.
+ */
+static void encode_slot_nvfp4(const or_cache *c, int slot, const float *hv) {
+  const int H = c->nheads, PN = c->headdim * c->dstate;
+  float m = 0.0f;
+  for (int h = 0; h < H; ++h) {
+    float mh = 0.0f;
+    for (int i = 0; i < PN; ++i)
+      if (fabsf(hv[(int64_t)h * PN + i]) > mh) mh = fabsf(hv[(int64_t)h * PN + i]);
+    nvfp4_set_word(c, slot, 1 + h, mh);
+    if (mh > m) m = mh;
+  }
+  float g = m / 2688.0f;
+  if (!(g > 0.0f)) g = 1.0f;
+  nvfp4_set_word(c, slot, 0, g);
+  for (int h = 0; h < H; ++h) encode_head_nvfp4(c, slot, h, hv + (int64_t)h * PN, g);
 }
 
 /* fp64 state mode (test only, row-major): store without rounding. */
@@ -588,6 +615,7 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
     if (Tb < 0 || Tb > T) { status |= 4; ok[b] = 0; continue; }
     if (slot <= 0 || slot >= c->num_slots) { ok[b] = 1; /* padding */ }
     else if (pnat[b] < 0 || pnat[b] + Tb > L) { status |= 1; ok[b] = 1; }
+    else if (c->ring_start[slot] < 0 || c->ring_start[slot] >= L) { status |= 8; ok[b] = 1; }
     else ok[b] = 2;
     if (ok[b] == 1)
       for (int i = 0; i < Tb; ++i)
@@ -670,71 +698,101 @@ int or_replay_step(const or_cache *c, int batch, int T, const int32_t *cu_seqlen
 /* ---------------------------------------------------------------------- */
 
 /*
+ * The fold of the first k live ring tokens of (slot, head) into h[P*N] in
+ * fp64, starting from the checkpoint's value (the FP16 recurrence checkpoint
+ * when there is one): the same recurrence as the step, over ring tokens
+ * (ring_start + s) mod L, s < k, with their stored dt'.
+ */
+static void fold_head(const or_cache *c, int slot, int hh, int k, float a, double *h) {
+  const int G = c->ngroups, P = c->headdim, N = c->dstate, L = c->ring_len, g = hh / (c->nheads / G);
+  const int r = c->ring_start[slot];
+  double *xv = (double *)malloc(sizeof(double) * P);
+  double *Bv = (double *)malloc(sizeof(double) * N);
+  if (c->recur)
+    decode_recur(c, slot, hh, h);
+  else
+    decode_state(c, slot, hh, h);
+  const uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
+  const uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
+  const uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
+  for (int s = 0; s < k; ++s) {
+    int pos = (r + s) % L;
+    double d = rd_f32(ds + ((int64_t)hh * L + pos) * 4);
+    for (int p = 0; p < P; ++p)
+      xv[p] = or_bf16_value(rd_u16(xs + (((int64_t)hh * L + pos) * P + p) * 2));
+    for (int q = 0; q < N; ++q)
+      Bv[q] = or_bf16_value(rd_u16(Bs + (((int64_t)g * L + pos) * N + q) * 2));
+    ssu_token(h, P, N, a, d, xv, Bv);
+  }
+  free(xv); free(Bv);
+}
+
+/*
  * For each entry j with k = num_fold[j] > 0: fold the first k live ring
  * tokens into the checkpoint (fp64 recurrence, result rounded to fp32 as the
  * flush's FP32 state), re-encode it, and advance ring_start by k (mod L).
+ * An NVFP4 checkpoint is re-encoded slot by slot (encode_slot_nvfp4).
  */
 int or_flush(const or_cache *c, int n, const int32_t *slot_idx,
              const int32_t *num_fold, const float *A, uint64_t seed) {
-  const int H = c->nheads, G = c->ngroups, P = c->headdim, N = c->dstate,
-            L = c->ring_len, HPG = H / G;
+  const int H = c->nheads, P = c->headdim, N = c->dstate, L = c->ring_len;
   int status = 0;
   build_tables(); /* before any parallel region */
+  /* which entries fold: a valid slot, k in [1, L] and a valid ring_start */
+  int *go = (int *)calloc(n > 0 ? n : 1, sizeof(int));
   for (int j = 0; j < n; ++j) {
     int slot = slot_idx[j], k = num_fold[j];
     if (slot <= 0 || slot >= c->num_slots) continue;
     if (k < 0 || k > L) { status |= 2; continue; }
+    if (k == 0) continue;
+    if (c->ring_start[slot] < 0 || c->ring_start[slot] >= L) { status |= 8; continue; }
+    go[j] = 1;
   }
-#pragma omp parallel for collapse(2) schedule(dynamic)
-  for (int j = 0; j < n; ++j) {
-    for (int hh = 0; hh < H; ++hh) {
-      const int slot = slot_idx[j], k = num_fold[j];
-      if (slot <= 0 || slot >= c->num_slots || k <= 0 || k > L) continue;
-      const int r = c->ring_start[slot], g = hh / HPG;
-      double *h = (double *)malloc(sizeof(double) * P * N);
-      double *xv = (double *)malloc(sizeof(double) * P);
-      double *Bv = (double *)malloc(sizeof(double) * N);
-      float *row = (float *)malloc(sizeof(float) * N);
+  if (c->state_dtype == OR_NVFP4) {
+    /* the slot's scale needs every head's folded values: fold all heads of an
+     * entry, then encode the slot */
+    float *hvs = (float *)malloc(sizeof(float) * (size_t)H * P * N);
+    for (int j = 0; j < n; ++j) {
+      if (!go[j]) continue;
+#pragma omp parallel for schedule(dynamic)
+      for (int hh = 0; hh < H; ++hh) {
+        double *h = (double *)malloc(sizeof(double) * P * N);
+        fold_head(c, slot_idx[j], hh, num_fold[j], A[hh], h);
+        for (int e = 0; e < P * N; ++e) hvs[(int64_t)hh * P * N + e] = (float)h[e];
+        free(h);
+      }
+      encode_slot_nvfp4(c, slot_idx[j], hvs);
       if (c->recur)
-        decode_recur(c, slot, hh, h); /* separate checkpoints: fold the FP16 recurrence one */
-      else
-        decode_state(c, slot, hh, h);
-      const uint8_t *xs = c->x_cache + (int64_t)slot * c->x_stride;
-      const uint8_t *Bs = c->B_cache + (int64_t)slot * c->B_stride;
-      const uint8_t *ds = c->dt_cache + (int64_t)slot * c->dt_stride;
-      for (int s = 0; s < k; ++s) {
-        int pos = (r + s) % L;
-        double d = rd_f32(ds + ((int64_t)hh * L + pos) * 4);
-        for (int p = 0; p < P; ++p)
-          xv[p] = or_bf16_value(rd_u16(xs + (((int64_t)hh * L + pos) * P + p) * 2));
-        for (int q = 0; q < N; ++q)
-          Bv[q] = or_bf16_value(rd_u16(Bs + (((int64_t)g * L + pos) * N + q) * 2));
-        ssu_token(h, P, N, A[hh], d, xv, Bv);
-      }
-      if (c->state_dtype == OR_F64) {
-        store_state_f64(c, slot, hh, h);
-      } else if (c->state_dtype == OR_NVFP4) {
-        float *hv = (float *)malloc(sizeof(float) * P * N);
-        for (int e = 0; e < P * N; ++e) hv[e] = (float)h[e];
-        encode_head_nvfp4(c, slot, hh, hv);
-        if (c->recur)
-          for (int p = 0; p < P; ++p) encode_recur_row(c, slot, hh, p, hv + (int64_t)p * N, seed);
-        free(hv);
-      } else {
-        for (int p = 0; p < P; ++p) {
-          for (int q = 0; q < N; ++q) row[q] = (float)h[p * N + q];
-          encode_row(c, slot, hh, p, row);
-          if (c->recur) encode_recur_row(c, slot, hh, p, row, seed);
+        for (int hh = 0; hh < H; ++hh)
+          for (int p = 0; p < P; ++p)
+            encode_recur_row(c, slot_idx[j], hh, p, hvs + ((int64_t)hh * P + p) * N, seed);
+    }
+    free(hvs);
+  } else {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int j = 0; j < n; ++j) {
+      for (int hh = 0; hh < H; ++hh) {
+        if (!go[j]) continue;
+        const int slot = slot_idx[j];
+        double *h = (double *)malloc(sizeof(double) * P * N);
+        float *row = (float *)malloc(sizeof(float) * N);
+        fold_head(c, slot, hh, num_fold[j], A[hh], h);
+        if (c->state_dtype == OR_F64) {
+          store_state_f64(c, slot, hh, h);
+        } else {
+          for (int p = 0; p < P; ++p) {
+            for (int q = 0; q < N; ++q) row[q] = (float)h[p * N + q];
+            encode_row(c, slot, hh, p, row);
+            if (c->recur) encode_recur_row(c, slot, hh, p, row, seed);
+          }
         }
+        free(h); free(row);
       }
-      free(h); free(xv); free(Bv); free(row);
     }
   }
-  for (int j = 0; j < n; ++j) {
-    int slot = slot_idx[j], k = num_fold[j];
-    if (slot <= 0 || slot >= c->num_slots || k <= 0 || k > L) continue;
-    c->ring_start[slot] = (c->ring_start[slot] + k) % L;
-  }
+  for (int j = 0; j < n; ++j)
+    if (go[j]) c->ring_start[slot_idx[j]] = (c->ring_start[slot_idx[j]] + num_fold[j]) % L;
+  free(go);
   return status;
 }
 
@@ -763,7 +821,7 @@ void or_init_state(const or_cache *c, const float *states, int64_t states_stride
         store_state_f64(c, slot, hh, h);
         free(h);
       } else if (c->state_dtype == OR_NVFP4) {
-        encode_head_nvfp4(c, slot, hh, src + (int64_t)hh * P * N);
+        if (hh == 0) encode_slot_nvfp4(c, slot, src); /* one scale over every head */
         if (c->recur)
           for (int p = 0; p < P; ++p) encode_recur_row(c, slot, hh, p, src + ((int64_t)hh * P + p) * N, seed);
       } else {
@@ -807,10 +865,10 @@ void or_enc_e2m1_array(const double *v, uint8_t *out, int64_t n) {
 }
 /* Decode one (slot, head) checkpoint into out[P*N] (any state dtype). */
 void or_decode_head(const or_cache *c, int slot, int head, double *out) { decode_state(c, slot, head, out); }
-/* Encode one head of fp32 values into an NVFP4 checkpoint. */
-void or_encode_head_nvfp4(const or_cache *c, int slot, int head, const float *hv) {
+/* Encode a slot of fp32 values [H][P][N] into an NVFP4 checkpoint. */
+void or_encode_slot_nvfp4(const or_cache *c, int slot, const float *hv) {
   build_tables();
-  encode_head_nvfp4(c, slot, head, hv);
+  encode_slot_nvfp4(c, slot, hv);
 }
 void or_e4m3_value_array(const uint8_t *b, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = or_e4m3_value(b[i]);

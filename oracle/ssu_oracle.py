@@ -80,8 +80,8 @@ def lib():
             L.or_sr_bits_array.argtypes = [ctypes.c_uint64, I, I, P, I64]
             L.or_decode_head.restype = None
             L.or_decode_head.argtypes = [ctypes.POINTER(_OrCache), I, I, P]
-            L.or_encode_head_nvfp4.restype = None
-            L.or_encode_head_nvfp4.argtypes = [ctypes.POINTER(_OrCache), I, I, P]
+            L.or_encode_slot_nvfp4.restype = None
+            L.or_encode_slot_nvfp4.argtypes = [ctypes.POINTER(_OrCache), I, P]
             for name in ("or_enc_bf16_array", "or_enc_f16_array", "or_enc_e4m3_array",
                          "or_bf16_value_array", "or_f16_value_array", "or_e4m3_value_array",
                          "or_e2m1_value_array", "or_enc_e2m1_array", "or_softplus_array"):
@@ -278,11 +278,14 @@ def sr_bits(seed, slot, head, n):
     return out
 
 
-def encode_head_nvfp4(cache, slot, head, values):
-    """Encode fp32 [P, N] values into head `head` of an NVFP4 checkpoint."""
+def encode_slot_nvfp4(cache, slot, values):
+    """Encode fp32 [H, P, N] values into one slot of an NVFP4 checkpoint (one
+    second-level scale over every head of the slot)."""
+    s = cache.spec
     v = np.ascontiguousarray(values, np.float32)
+    assert v.shape == (s.nheads, s.headdim, s.dstate)
     oc = _as_orcache(cache)
-    lib().or_encode_head_nvfp4(ctypes.byref(oc), int(slot), int(head), v.ctypes.data)
+    lib().or_encode_slot_nvfp4(ctypes.byref(oc), int(slot), v.ctypes.data)
 
 
 def e2m1_value(b):

@@ -78,8 +78,9 @@ def make_cache_device(spec: CacheSpec, seed: int, device, h0_std: float = 0.1,
             e = torch.randint(5, 9, (n, H * P * N // 16), generator=g, device=device, dtype=torch.int32)
             m = torch.randint(0, 8, (n, H * P * N // 16), generator=g, device=device, dtype=torch.int32)
             t["scale"][sl, : spec.scale_bytes()] = (e * 8 + m).to(torch.uint8)
-            gs = (h0_std / 3.0) * (0.5 + torch.rand(n, H, generator=g, device=device))
-            t["gscale"][sl, : spec.gscale_bytes()] = gs.view(torch.uint8).reshape(n, -1)
+            gs = (h0_std / 3.0) * (0.5 + torch.rand(n, 1, generator=g, device=device))
+            words = torch.cat([gs, (gs * 2688.0).expand(n, H)], dim=1).contiguous()
+            t["gscale"][sl, : spec.gscale_bytes()] = words.view(torch.uint8).reshape(n, -1)
         elif dt == "fp8":
             codes = (torch.randn(n, H, P, N, generator=g, device=device) * 32.0).clamp(-448, 448)
             t["state"][sl, : spec.state_bytes()] = codes.to(torch.float8_e4m3fn).view(

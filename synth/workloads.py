@@ -83,8 +83,9 @@ class CacheSpec:
         return self.nheads * self.headdim * 4
 
     def gscale_bytes(self):
-        """nvfp4: the f32 second-level scale of each head."""
-        return self.nheads * 4
+        """nvfp4: f32 words [1 + H]: the slot's second-level scale, then the
+        largest |value| of each head at its last encode."""
+        return (1 + self.nheads) * 4
 
     def x_bytes(self):
         return self.nheads * self.ring_len * self.headdim * 2
@@ -260,15 +261,16 @@ def _fill_slots(arr: np.ndarray, packed: np.ndarray):
 def random_nvfp4(n: int, H: int, P: int, N: int, g: torch.Generator, h0_std: float = 0.1):
     """Random nvfp4 checkpoints: every code byte uniform (all 16 e2m1 codes in
     both nibbles), block-scale codes with exponent field 5..8 and a random
-    mantissa (e4m3 values 0.25 .. 3.75), second-level scales
-    h0_std / 3 * U(0.5, 1.5): codes, block scales and second-level scales as
-    byte arrays [n, ...]."""
+    mantissa (e4m3 values 0.25 .. 3.75), one second-level scale per slot
+    h0_std / 3 * U(0.5, 1.5), head maxima words 2688 times it: codes, block
+    scales and scale words as byte arrays [n, ...]."""
     codes = torch.randint(0, 256, (n, H * P * N // 2), generator=g, dtype=torch.int32).to(torch.uint8)
     e = torch.randint(5, 9, (n, H * P * N // 16), generator=g, dtype=torch.int32)
     m = torch.randint(0, 8, (n, H * P * N // 16), generator=g, dtype=torch.int32)
     sf = (e * 8 + m).to(torch.uint8)
-    gs = (h0_std / 3.0) * (0.5 + torch.rand(n, H, generator=g))
-    return codes.numpy(), sf.numpy(), gs.to(torch.float32).numpy().view(np.uint8).reshape(n, -1)
+    gs = (h0_std / 3.0) * (0.5 + torch.rand(n, 1, generator=g))
+    words = torch.cat([gs, (gs * 2688.0).expand(n, H)], dim=1)
+    return codes.numpy(), sf.numpy(), words.to(torch.float32).numpy().view(np.uint8).reshape(n, -1)
 
 
 def random_state_bytes(spec: CacheSpec, n: int, g: torch.Generator, h0_std: float = 0.1):

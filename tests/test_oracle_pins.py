@@ -427,6 +427,41 @@ def test_padding_and_invalid_entries(oracle):
     assert st == 2
 
 
+@pytest.mark.parametrize("bad", [-1, 16, 40])
+def test_bad_ring_start_is_skipped(oracle, bad):
+    """A slot whose ring_start lies outside [0, L) has no live or append
+    position under the ring contract (FlashInfer PR, Description item 2):
+    the step writes zero output rows for its entry, touches none of its
+    cache and raises status bit 8; the flush leaves it alone and raises the
+    same bit; the other entries are computed as if it were absent."""
+    spec, cache, step = _small_case("f32", seed=103, T=2, pnat_max=3, batch=3, num_slots=6)
+    slot = int(step.slot_idx[1])
+    cache.ring_start[slot] = bad
+    before = cache.copy()
+    out, st = oracle.replay_step(cache, step)
+    assert st == 8
+    assert np.all(out[2:4] == 0.0)
+    for f in ("x_cache", "B_cache", "dt_cache", "state"):
+        assert np.array_equal(getattr(cache, f)[slot], getattr(before, f)[slot]), f
+    # the other entries: as in a call without the bad one
+    keep = [0, 2]
+    sub = synth.StepInputs(2, step.T, step.slot_idx[keep], step.pnat[keep], None,
+                           np.concatenate([step.x[0:2], step.x[4:6]]), np.concatenate([step.B[0:2], step.B[4:6]]),
+                           np.concatenate([step.C[0:2], step.C[4:6]]), np.concatenate([step.dt[0:2], step.dt[4:6]]),
+                           step.A, step.D, step.dt_bias)
+    o2, st2 = oracle.replay_step(before.copy(), sub)
+    assert st2 == 0
+    assert np.array_equal(np.concatenate([out[0:2], out[4:6]]), o2)
+    k = np.array([1, 2, 1], np.int32)
+    c2 = before.copy()
+    assert oracle.flush(c2, step.slot_idx, k, step.A) == 8
+    assert c2.ring_start[slot] == bad
+    assert np.array_equal(c2.state[slot], before.state[slot])
+    for b in (0, 2):
+        sl = int(step.slot_idx[b])
+        assert c2.ring_start[sl] == (before.ring_start[sl] + k[b]) % spec.ring_len
+
+
 # --------------------------------------------------------------------------
 # ring contract fixture (positions fixed by the page's formula)
 # --------------------------------------------------------------------------
