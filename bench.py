@@ -134,11 +134,21 @@ def recur_bytes(H):
     return H * 64 * 128 * 2
 
 
-def separate_extra_bytes(spec, H, k):
+def separate_extra_bytes(spec, H, k, G=8):
     """What separate checkpoints add to a fold of each entry with k > 0: the
     recurrence checkpoint is read and written, the read checkpoint (+ scales)
-    only written."""
-    return int(sum(2 * recur_bytes(H) - state_bytes(spec, H) for kk in k if kk > 0))
+    only written.  An NVFP4 read checkpoint has one scale per slot over every
+    head, so its fold first makes a pass that reads the recurrence checkpoint
+    and the k ring tokens for the head maxima (4 B written per head), and the
+    encode reads the slot's H maxima back."""
+    extra = 0
+    for kk in k:
+        if kk <= 0:
+            continue
+        extra += 2 * recur_bytes(H) - state_bytes(spec, H)
+        if spec.state_dtype == "nvfp4":
+            extra += recur_bytes(H) + int(kk) * (H * 64 * 2 + G * 128 * 2 + H * 4) + 2 * H * 4
+    return int(extra)
 
 
 def flush_bytes(spec, H, G, k):
@@ -349,13 +359,13 @@ def run_workload(args, name, clocks, dev, batch=None, cpu=False):
     tbs = [np.diff(s.cu_seqlens) if s.cu_seqlens is not None else [T] * batch for s in steps_in]
     if fused:
         sbytes = float(np.mean([fused_bytes(spec, H, G, k.cpu().numpy(), tb, ob)
-                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if separate else 0)
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy(), G) if separate else 0)
                                 for k, tb in zip(flush_k, tbs)]))
         fbytes = 0.0
     else:
         sbytes = float(np.mean([step_bytes(spec, H, G, s.pnat, tb, ob) for s, tb in zip(steps_in, tbs)]))
         fbytes = float(np.mean([flush_bytes(spec, H, G, k.cpu().numpy())
-                                + (separate_extra_bytes(spec, H, k.cpu().numpy()) if separate else 0)
+                                + (separate_extra_bytes(spec, H, k.cpu().numpy(), G) if separate else 0)
                                 for k in flush_k])) if flush_k else 0.0
     # kernel launches per ssu_replay_step call (as dispatched for this workload)
     launches = 1

@@ -63,7 +63,7 @@ typedef enum ssu_dtype {
   SSU_BF16 = 1,
   SSU_F16 = 2,
   SSU_FP8_E4M3 = 3, /* OCP e4m3fn codes (max 448) with an fp32 scale per state row */
-  SSU_NVFP4 = 4     /* e2m1 codes, an e4m3 scale per 16 values, an fp32 scale per head */
+  SSU_NVFP4 = 4     /* e2m1 codes, an e4m3 scale per 16 values, one fp32 scale per slot */
 } ssu_dtype;
 
 typedef enum ssu_algo {
@@ -96,7 +96,10 @@ enum {
  *   state_scale [slot][nheads][headdim]          f32, fp8 state only: the row's
  *                                                value is code * scale
  *               [slot][nheads][512]              u8, nvfp4 state: e4m3 block scales
- *   state_head_scale [slot][nheads]              f32, nvfp4 state only
+ *   state_gscale [slot][1 + nheads]              f32, nvfp4 state only: word 0
+ *                                                the slot's second-level scale,
+ *                                                word 1 + h head h's largest
+ *                                                |value| at its last encode
  *   x_cache     [slot][nheads][ring_len][headdim] io_dtype
  *   B_cache     [slot][ngroups][ring_len][dstate] io_dtype
  *   dt_cache    [slot][nheads][ring_len]          f32, holds dt' = softplus(dt + dt_bias)
@@ -125,13 +128,17 @@ enum {
  * 64-bit sr_seed (e = p * 128 + n); a caller passes a different seed on
  * every call.  recur_state requires state_dtype SSU_FP8_E4M3 or SSU_NVFP4
  * (else SSU_ERR_UNSUPPORTED).
- * NVFP4 read checkpoint [VP Claims; VD init] (requires recur_state): value =
- * e2m1(code) * e4m3(block scale) * g, blocks of 16 consecutive n of a row, g
- * per (slot, head).  Written with nearest encoding from the fp32 fold:
- * g = fp32(max |v| / 2688) (1 if not positive), block scale =
- * e4m3(fp32(a / fp32(6 g))) for a block's max |v| (saturating), code =
- * e2m1(v * fp32(1 / fp32(e4m3 * g))) (nearest even, saturating at 6; a zero
- * block scale gives signed zeros).  Layout of one head: row block rb, lane
+ * NVFP4 read checkpoint [VP Claims; VD initialize_replayssm_state, NVFP4
+ * branch] (requires recur_state): value = e2m1(code) * e4m3(block scale) * g,
+ * blocks of 16 consecutive n of a row, ONE g per slot: g = fp32(M / 2688)
+ * (1 if not positive) with M the largest |value| over every head of the slot
+ * (2688 = 6 * 448), as the page's init computes it.  Init and every fold write
+ * the whole slot that way, with nearest encoding of the fp32 values: block
+ * scale = e4m3(fp32(a / fp32(6 g))) for a block's max |v| (saturating), code
+ * = e2m1(v * fp32(1 / fp32(e4m3 * g))) (nearest even, saturating at 6; a zero
+ * block scale gives signed zeros).  Because g needs every head's folded
+ * values, an NVFP4 fold is two launches: a pass that records each head's
+ * maximum in state_gscale, then the encode.  Layout of one head: row block rb, lane
  * l = 16 q + m (row 16 rb + m, values n = 32 q + t): codes of t = 0..31 in
  * the 16 bytes at rb * 1024 + l * 16 (value t in byte t / 2, even t in the
  * low nibble); block scales (t < 16, t >= 16) in state_scale bytes
@@ -158,8 +165,8 @@ typedef struct ssu_cache {
   int32_t *status;
   void *recur_state;
   int64_t recur_slot_stride;
-  float *state_head_scale; /* nvfp4 only, else NULL */
-  int64_t head_scale_slot_stride;
+  float *state_gscale; /* nvfp4 only, else NULL */
+  int64_t gscale_slot_stride;
 } ssu_cache;
 
 /*

@@ -54,7 +54,7 @@ class SsuCache(ctypes.Structure):
         ("dt_cache", _P), ("dt_slot_stride", _I64),
         ("ring_start", _P), ("status", _P),
         ("recur_state", _P), ("recur_slot_stride", _I64),
-        ("state_head_scale", _P), ("head_scale_slot_stride", _I64),
+        ("state_gscale", _P), ("gscale_slot_stride", _I64),
     ]
 
 
@@ -181,7 +181,7 @@ class DeviceCache:
     headdim: int = 64
     dstate: int = 128
     recur: object = None  # FP16 recurrence checkpoint (separate checkpoints) or None
-    gscale: object = None  # nvfp4: uint8 [num_slots, stride] holding the f32 head scales
+    gscale: object = None  # nvfp4: uint8 [num_slots, stride]: f32 slot scale, then the head maxima
 
     def desc(self) -> SsuCache:
         scaled = self.state_dtype in ("fp8", "nvfp4")

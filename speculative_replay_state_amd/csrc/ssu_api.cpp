@@ -83,14 +83,14 @@ int check_cache(const ssu_cache *c) {
   const bool nvfp4 = c->state_dtype == SSU_NVFP4;
   if ((c->state_dtype == SSU_FP8_E4M3 || nvfp4) && !c->state_scale)
     return fail(SSU_ERR_INVALID, "fp8 and nvfp4 states require state_scale");
-  if (nvfp4 && !c->state_head_scale)
-    return fail(SSU_ERR_INVALID, "nvfp4 state requires state_head_scale");
+  if (nvfp4 && !c->state_gscale)
+    return fail(SSU_ERR_INVALID, "nvfp4 state requires state_gscale");
   if (nvfp4 && !c->recur_state)
     return fail(SSU_ERR_UNSUPPORTED, "an nvfp4 read checkpoint requires recur_state (separate checkpoints)");
   if (c->recur_state && c->state_dtype != SSU_FP8_E4M3 && !nvfp4)
     return fail(SSU_ERR_UNSUPPORTED, "recur_state (separate checkpoints) requires an fp8 or nvfp4 state");
-  if (c->state_head_scale && !aligned16(c->state_head_scale))
-    return fail(SSU_ERR_INVALID, "state_head_scale must be 16-byte aligned");
+  if (c->state_gscale && !aligned16(c->state_gscale))
+    return fail(SSU_ERR_INVALID, "state_gscale must be 16-byte aligned");
   if (c->recur_state && !aligned16(c->recur_state))
     return fail(SSU_ERR_INVALID, "recur_state must be 16-byte aligned");
   if (!aligned16(c->state) || !aligned16(c->x_cache) || !aligned16(c->B_cache) || !aligned16(c->dt_cache) ||
@@ -107,7 +107,7 @@ int check_cache(const ssu_cache *c) {
       {"state", c->state_slot_stride, need_state, true},
       {"state_scale", c->scale_slot_stride, nvfp4 ? H * ssu::kHeadDim * ssu::kDState / 16 : H * ssu::kHeadDim * 4,
        c->state_dtype == SSU_FP8_E4M3 || nvfp4},
-      {"state_head_scale", c->head_scale_slot_stride, H * 4, nvfp4},
+      {"state_gscale", c->gscale_slot_stride, (1 + H) * 4, nvfp4},
       {"x_cache", c->x_slot_stride, H * L * ssu::kHeadDim * 2, true},
       {"B_cache", c->B_slot_stride, G * L * ssu::kDState * 2, true},
       {"dt_cache", c->dt_slot_stride, H * L * 4, true},
@@ -148,8 +148,8 @@ ssu::KCache kcache(const ssu_cache *c, uint64_t seed) {
   k.recur_stride = c->recur_slot_stride;
   k.seed_lo = (uint32_t)seed;
   k.seed_hi = (uint32_t)(seed >> 32);
-  k.hscale = reinterpret_cast<uint8_t *>(c->state_head_scale);
-  k.hscale_stride = c->head_scale_slot_stride;
+  k.gw = reinterpret_cast<uint8_t *>(c->state_gscale);
+  k.gw_stride = c->gscale_slot_stride;
   return k;
 }
 

@@ -39,8 +39,8 @@ struct KCache {
   uint8_t *recur;        // NULL, or the FP16 recurrence checkpoint (separate checkpoints)
   int64_t recur_stride;
   uint32_t seed_lo, seed_hi;  // this call's stochastic-rounding seed
-  uint8_t *hscale;       // nvfp4: the f32 second-level scale of each head
-  int64_t hscale_stride;
+  uint8_t *gw;           // nvfp4: f32 words per slot: the slot's second-level scale, then the head maxima
+  int64_t gw_stride;
 };
 
 // One replay step.

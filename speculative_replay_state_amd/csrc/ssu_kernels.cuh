@@ -986,7 +986,13 @@ __device__ __forceinline__ void fold_setup(float Ah, int k, const FoldHeadLoads<
 
 // The rank-k update of row block rb into the lane's quarter row:
 // acc[nb] += sum_s B_s[n] (coef_s x_s[p]) for p = 16 rb + m, with coef_s x_s[p]
-// split into bf16 hi + lo (+ lo2 for fp32 state).
+// split into bf16 hi + lo (+ lo2 for fp32 and fp8 states).  Two parts keep 16
+// bits of each term (relative error 2^-17); an fp8 row's subnormal codes are
+// rowmax * 2^-9 / 448 apart, which a value that cancels to near zero can
+// straddle with that error, so fp8 folds take the third part (24 bits, the
+// precision of the fp32 flush itself) as fp32 states do.
+constexpr bool fold_lo2(int ST) { return ST == kF32 || ST == kFP8; }
+
 template <int ST, int KW, bool LEAN>
 __device__ __forceinline__ void fold_update(const FoldOps<ST, KW, LEAN> &fo, const uint16_t *xT, int rb, int lane,
                                             f32x4 *acc) {
@@ -1003,14 +1009,14 @@ __device__ __forceinline__ void fold_update(const FoldOps<ST, KW, LEAN> &fo, con
     const __bf16 lo = (__bf16)r1;
     bhi[e] = hi;
     blo[e] = lo;
-    if constexpr (ST == kF32) blo2[e] = (__bf16)(r1 - (float)lo);
+    if constexpr (fold_lo2(ST)) blo2[e] = (__bf16)(r1 - (float)lo);
   }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
     const V a = LEAN ? fo.abl[nb * 64 + (lane & 63)] : fo.ab[LEAN ? 0 : nb];
     acc[nb] = mfma_win<KW>(a, bhi, acc[nb]);
     acc[nb] = mfma_win<KW>(a, blo, acc[nb]);
-    if constexpr (ST == kF32) acc[nb] = mfma_win<KW>(a, blo2, acc[nb]);
+    if constexpr (fold_lo2(ST)) acc[nb] = mfma_win<KW>(a, blo2, acc[nb]);
   }
 }
 
@@ -1087,18 +1093,21 @@ __device__ __forceinline__ f32x2 block_max2(const f32x4 *acc) {
   return f32x2{a, b};
 }
 
-// The NVFP4 scales from the lane's eight block maxima bm (row blocks 0..3,
-// two each): the head maximum over the wave gives g = fp32(m / 2688) (1 if
-// not positive); block i gets the e4m3 code of fp32(bm[i] / fp32(6 g))
-// (nearest, saturating at 448) in byte i of sfw, and y[i] = fp32(1 / (e4m3
-// value * g)), 0 for a zero block scale (its values encode as signed zeros).
+// NVFP4 scales.  A slot has one second-level scale g = fp32(M / 2688) (1 if
+// not positive), M the largest |value| over every head of the slot, as the
+// vLLM API page's initialize_replayssm_state computes it (2688 = 6 * 448: the
+// largest e2m1 value times the largest e4m3 value); word 0 of the slot's
+// scale words holds g and word 1 + h head h's largest |value|.  Block i of a
+// lane gets the e4m3 code of fp32(bm[i] / fp32(6 g)) (nearest, saturating at
+// 448) in byte i of sfw, and y[i] = fp32(1 / (e4m3 value * g)), 0 for a zero
+// block scale (its values encode as signed zeros).
 __device__ __forceinline__ float wave_max(float v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) v = fmaxf(v, lane_xor(v, lane, d));
   return v;
 }
-__device__ __forceinline__ float nvfp4_gscale(float head_max) {
-  const float g = head_max / 2688.0f;
+__device__ __forceinline__ float nvfp4_gscale(float slot_max) {
+  const float g = slot_max / 2688.0f;
   return g > 0.0f ? g : 1.0f;
 }
 __device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float &y) {
@@ -1108,26 +1117,65 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float &y
   y = es > 0.0f ? 1.0f / es : 0.0f;
   return code;
 }
-__device__ __forceinline__ void nvfp4_scales(const float *bm, int lane, float &g, u32x2 &sfw, float *y) {
-  float mx = bm[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, bm[i]);
-  g = nvfp4_gscale(wave_max(mx, lane));
+__device__ __forceinline__ void nvfp4_block_scales(const float *bm, float g, u32x2 &sfw, float *y) {
   uint32_t sb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sb[i] = nvfp4_block_scale(bm[i], g, y[i]);
   sfw = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24), sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
 }
 
+__device__ __forceinline__ float *nvfp4_words(const KCache &c, int slot) {
+  return reinterpret_cast<float *>(c.gw + (int64_t)slot * c.gw_stride);
+}
+
+// The slot's head maxima (words 1 .. H), read in two parts so that the loads
+// can go out early: head_max_load takes words lane and lane + 64 (clamped to
+// the last head: every address is valid and a repeated word changes no
+// maximum), slot_scale finishes with any heads past 128 and reduces over the
+// wave.
+struct HeadMaxLoads {
+  float a, b;
+};
+__device__ __forceinline__ HeadMaxLoads head_max_load(const KCache &c, int slot, int lane) {
+  const float *w = nvfp4_words(c, slot) + 1;
+  const int last = c.H - 1;
+  return HeadMaxLoads{w[lane < last ? lane : last], w[lane + 64 < last ? lane + 64 : last]};
+}
+__device__ __forceinline__ float slot_scale(const KCache &c, int slot, int lane, const HeadMaxLoads &hm) {
+  float m = fmaxf(hm.a, hm.b);
+  const float *w = nvfp4_words(c, slot) + 1;
+  for (int i = lane + 128; i < c.H; i += 64) m = fmaxf(m, w[i]);
+  return nvfp4_gscale(wave_max(m, lane));
+}
+
+// The fold of an FP16 recurrence tile rch for an NVFP4 read checkpoint, first
+// pass: the largest |value| of the folded head.  The same instructions on the
+// same operands as fold_head_nvfp4's passes, hence the same values.
+template <int KW, bool LEAN>
+__device__ __forceinline__ float fold_head_max(const FoldOps<kNVFP4, KW, LEAN> &fo, const uint16_t *xT, int lane,
+                                               const u32x4 (*rch)[4]) {
+  float mx = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc[8];
+    decode_quarter<kF16>(rch[rb], fo.D0, acc);
+    fold_update<kNVFP4, KW>(fo, xT, rb, lane, acc);
+    const f32x2 b2 = block_max2(acc);
+    mx = fmaxf(mx, fmaxf(b2[0], b2[1]));
+  }
+  return wave_max(mx, lane);
+}
+
 // Separate checkpoints with an NVFP4 read checkpoint: fold the FP16
-// recurrence tile rch.  The scales need the whole head's maximum, so the fold
-// runs twice: pass 1 keeps the block maxima, pass 2 (the same instructions on
-// the same operands, hence the same values) writes the new recurrence chunks
-// over rch (stochastic rounding) and the e2m1 codes into codes.
+// recurrence tile rch with the slot's second-level scale g.  The block scales
+// need each block's maximum, so the fold runs twice: pass 1 keeps the block
+// maxima, pass 2 (the same instructions on the same operands, hence the same
+// values) writes the new recurrence chunks over rch (stochastic rounding) and
+// the e2m1 codes into codes.
 template <int KW, bool LEAN>
 __device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW, LEAN> &fo, const uint16_t *xT, int lane,
-                                                const KCache &c, int slot, int head, u32x4 (*rch)[4],
-                                                u32x4 (*codes)[1], u32x2 &sfw, float &g) {
+                                                const KCache &c, int slot, int head, float g, u32x4 (*rch)[4],
+                                                u32x4 (*codes)[1], u32x2 &sfw) {
   const int m = lane & 15, q = lane >> 4;
   float bm[8];
 #pragma unroll
@@ -1140,7 +1188,7 @@ __device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW, LEAN> 
     bm[2 * rb + 1] = b2[1];
   }
   float y[8];
-  nvfp4_scales(bm, lane, g, sfw, y);
+  nvfp4_block_scales(bm, g, sfw, y);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     f32x4 acc[8];
@@ -1151,14 +1199,15 @@ __device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW, LEAN> 
   }
 }
 
-// Stores an NVFP4 tile with its block and head scales.
+// Stores an NVFP4 tile with its block scales; the wave of head 0 also writes
+// the slot's second-level scale (word 0: no wave of a folding slot reads it).
 __device__ __forceinline__ void store_nvfp4(const KCache &c, int slot, int h, int lane, const u32x4 (*codes)[1],
                                             u32x2 sfw, float g) {
   uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(kNVFP4);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) store_chunks<kNVFP4>(hp, rb, lane, codes[rb]);
   st8(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) + lane * 8, sfw);
-  if (lane == 0) *reinterpret_cast<float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4) = g;
+  if (h == 0 && lane == 0) nvfp4_words(c, slot)[0] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -1179,7 +1228,7 @@ struct HeadLoads {
   u32x4 xw[Win<KW>::kRounds];                // x window chunks
   f32x4 rscale[4];                           // fp8 row scales of rows 16 rb + 4 q + j
   u32x2 sfw;                                 // nvfp4: the lane's 8 block scales (rb 0..3, 2 each)
-  float gs;                                  // nvfp4: the head's second-level scale
+  float gs;                                  // nvfp4: the slot's second-level scale
   float dtv;                                 // lane s: stored dt' (s < pnat) or raw dt (new)
   float dtb, Ah, Dh;                         // dt_bias[h], A[h], D[h]
   u32x4 zw[2];                               // output gate chunks (gated variant only)
@@ -1205,7 +1254,7 @@ __device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int
     for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_off(rb, u, lane, T::kNLD));
   if constexpr (ST == kNVFP4) {  // the block scales and the head scale belong to the tile
     ld.sfw = ld8(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) + lane * 8);
-    ld.gs = *reinterpret_cast<const float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4);
+    ld.gs = nvfp4_words(c, slot)[0];
   }
 }
 
@@ -1621,17 +1670,19 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   FoldBLoads<KW> fb;
   load_fold_head<ST, KW>(c, slot, h, r, k, lane, fl);
   load_fold_B<KW>(c, slot, h / c.hpg, r, k, lane, fb);
+  HeadMaxLoads hm{};
+  if constexpr (ST == kNVFP4) hm = head_max_load(c, slot, lane);  // written by fold_max_kernel
 
   // 2. coefficients, xT, A operands
   FoldOps<ST, KW> fo;
   fold_setup<ST, KW>(A[h], k, fl, fb, xT, nullptr, lane, fo);
   wave_sync();  // xT written by this wave -> read below
 
-  if constexpr (ST == kNVFP4) {  // the whole head at once: its scales need the head's maximum
+  if constexpr (ST == kNVFP4) {  // the whole head at once: its block scales need the slot's scale
     u32x4 codes[4][1];
     u32x2 sfw;
-    float g;
-    fold_head_nvfp4<KW>(fo, xT, lane, c, slot, h, rraw, codes, sfw, g);
+    const float g = slot_scale(c, slot, lane, hm);
+    fold_head_nvfp4<KW>(fo, xT, lane, c, slot, h, g, rraw, codes, sfw);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) store_chunks<kF16>(rp, rb, lane, rraw[rb]);
     store_nvfp4(c, slot, h, lane, codes, sfw, g);
@@ -1660,6 +1711,61 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
   if constexpr (ST == kFP8)
     (reinterpret_cast<float *>(c.scale + (int64_t)slot * c.scale_stride) + h * kHeadDim)[lane] = pick4(scs[0], scs[1], scs[2], scs[3], q);
   }
+}
+
+// NVFP4 folds, first pass: the largest |value| of every folded head, stored
+// as word 1 + h of the slot's scale words; the fold's encode pass (flush or
+// fused step, launched next on the same stream) reduces them to the slot's
+// second-level scale.  A slot's scale depends on every head of the slot, so
+// no head can be encoded before all of them are folded: this pass reads the
+// FP16 recurrence tiles once more.  One wave per (entry, head), the same
+// loads and fold instructions as the encode pass.  STEP: the entries of a
+// fused step (its validity rules; k = num_fold from the ring start at call
+// time); else those of a flush (slot_idx, num_fold, A).
+template <int KW, bool STEP>
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fold_max_kernel(KCache c, KStep s, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
+                     int htiles, int64_t ntiles) {
+  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= ntiles) return;
+  const int j = (int)(tile / htiles);
+  const int h = (int)(tile - (int64_t)j * htiles) * kHeadWaves + wave;
+  if (h >= c.H) return;
+  int slot, k, r;
+  float Ah;
+  if constexpr (STEP) {
+    const Entry e = load_entry(c, s, j, false);
+    if (e.mode != 2 || e.k <= 0) return;
+    slot = e.slot;
+    k = e.k;
+    r = e.r0;
+    Ah = s.A[h];
+  } else {
+    slot = slot_idx[j];
+    k = num_fold[j];
+    if (slot <= 0 || slot >= c.num_slots || k <= 0 || k > c.L) return;
+    r = c.ring_start[slot];
+    if (r < 0 || r >= c.L) return;
+    Ah = A[h];
+  }
+  uint16_t *xT = xT_all[wave];
+  u32x4 rraw[4][4];
+  const uint8_t *rp = c.recur + (int64_t)slot * c.recur_stride + (int64_t)h * (kHeadElems * 2);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rraw[rb][u] = ld16_nt(rp + tile_chunk(rb, u, lane, 2));
+  FoldHeadLoads<kNVFP4, KW> fl;
+  FoldBLoads<KW> fb;
+  load_fold_head<kNVFP4, KW>(c, slot, h, r, k, lane, fl);
+  load_fold_B<KW>(c, slot, h / c.hpg, r, k, lane, fb);
+  FoldOps<kNVFP4, KW> fo;
+  fold_setup<kNVFP4, KW>(Ah, k, fl, fb, xT, nullptr, lane, fo);
+  wave_sync();  // xT written by this wave -> read below
+  const float mx = fold_head_max<KW>(fo, xT, lane, rraw);
+  if (lane == 0) nvfp4_words(c, slot)[1 + h] = mx;
 }
 
 // ---------------------------------------------------------------------------
@@ -1754,13 +1860,16 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
   if (e.k > 0) {
     FoldBLoads<KW> fb;
     load_fold_B<KW>(c, e.slot, g, e.r0, e.k, lane, fb);
+    HeadMaxLoads hm{};
+    if constexpr (ST == kNVFP4) hm = head_max_load(c, e.slot, lane);  // written by fold_max_kernel
     FoldOps<ST, KW, kAbLds> fo;
     fold_setup<ST, KW>(Ah, e.k, fl, fb, xT,
                        kAbLds ? reinterpret_cast<typename Win<KW>::V *>(lds_all[wave] + kXTWords) : nullptr, lane,
                        fo);
     wave_sync();  // xT written by this wave -> read below
     if constexpr (ST == kNVFP4) {
-      fold_head_nvfp4<KW>(fo, xT, lane, c, e.slot, h, rraw, ld.raw, ld.sfw, ld.gs);
+      ld.gs = slot_scale(c, e.slot, lane, hm);
+      fold_head_nvfp4<KW>(fo, xT, lane, c, e.slot, h, ld.gs, rraw, ld.raw, ld.sfw);
     } else {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -1850,6 +1959,34 @@ __global__ void ring_advance_kernel(KCache c, const int32_t *slot_idx, const int
 // clear the slot's rings.
 // ---------------------------------------------------------------------------
 
+// NVFP4 init, first pass: the largest |value| of every head of the prefill
+// states (word 1 + h of the slot's scale words), from which init_rows_kernel
+// takes the slot's second-level scale.  Same geometry as init_rows_kernel.
+template <int ST>
+__global__ __launch_bounds__(kWaves * 64) void init_max_kernel(KCache c, const float *states,
+                                                               int64_t states_stride, const int32_t *slot_idx) {
+  static_assert(ST == kNVFP4, "only an nvfp4 checkpoint has a slot scale");
+  const int j = blockIdx.x / c.H, h = blockIdx.x - j * c.H;
+  const int slot = slot_idx[j];
+  if (slot <= 0 || slot >= c.num_slots) return;
+  const int rb = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const float *src = states + (int64_t)j * states_stride + (int64_t)h * kHeadElems +
+                     (16 * rb + m) * kDState + 32 * q;
+  f32x4 acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 4 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) QV(acc, 4 * u + e) = a[e];
+  }
+  __shared__ float wmax[kWaves];
+  const f32x2 b2 = block_max2(acc);
+  const float mx = wave_max(fmaxf(b2[0], b2[1]), lane);
+  if (lane == 0) wmax[rb] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) nvfp4_words(c, slot)[1 + h] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
 template <int ST>
 __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const float *states,
                                                                 int64_t states_stride,
@@ -1870,20 +2007,16 @@ __global__ __launch_bounds__(kWaves * 64) void init_rows_kernel(KCache c, const 
     for (int e = 0; e < 4; ++e) QV(acc, 4 * u + e) = a[e];
   }
   if constexpr (ST == kNVFP4) {
-    // the head's maximum over the four waves (one row block each)
-    __shared__ float wmax[kWaves];
+    // the slot's scale from every head's maximum (init_max_kernel ran first)
+    const float g = slot_scale(c, slot, lane, head_max_load(c, slot, lane));
     const f32x2 b2 = block_max2(acc);
-    const float mx = wave_max(fmaxf(b2[0], b2[1]), lane);
-    if (lane == 0) wmax[rb] = mx;
-    __syncthreads();
-    const float g = nvfp4_gscale(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
     float y0, y1;
     const uint32_t s0 = nvfp4_block_scale(b2[0], g, y0), s1 = nvfp4_block_scale(b2[1], g, y1);
     u32x4 ch[1] = {nvfp4_encode_quarter(acc, y0, y1)};
     store_chunks<ST>(hp, rb, lane, ch);
     *reinterpret_cast<uint16_t *>(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) +
                                   lane * 8 + rb * 2) = (uint16_t)(s0 | (s1 << 8));
-    if (threadIdx.x == 0) *reinterpret_cast<float *>(c.hscale + (int64_t)slot * c.hscale_stride + (int64_t)h * 4) = g;
+    if (h == 0 && threadIdx.x == 0) nvfp4_words(c, slot)[0] = g;
   } else {
     float sc = 1.f, y = 1.f;
     bool fast = true;
@@ -1992,6 +2125,16 @@ hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
   const int64_t ntiles = (int64_t)s.batch * htiles;
   const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
+  if constexpr (ST == kNVFP4) {  // a step that folds: the maxima pass first (the encode needs the slot's scale)
+    if (s.fold) {
+      if (c.L <= 16)
+        fold_max_kernel<16, true><<<grid, block, 0, st>>>(c, s, nullptr, nullptr, nullptr, htiles, ntiles);
+      else
+        fold_max_kernel<32, true><<<grid, block, 0, st>>>(c, s, nullptr, nullptr, nullptr, htiles, ntiles);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+  }
   if (c.L <= 16)
     fused_kernel<ST, OT, 16, HAS_Z, SEP><<<grid, block, 0, st>>>(c, s, htiles, ntiles);
   else
@@ -2053,6 +2196,15 @@ hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_
   const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
   bool sep = ST == kNVFP4;
   if constexpr (ST == kFP8) sep = c.recur != nullptr;
+  if constexpr (ST == kNVFP4) {  // the maxima pass first: the encode needs the slot's scale
+    const KStep none{};
+    if (c.L <= 16)
+      fold_max_kernel<16, false><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
+    else
+      fold_max_kernel<32, false><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (sep) {
     if constexpr (ST == kFP8 || ST == kNVFP4) {
       if (c.L <= 16)
@@ -2077,6 +2229,11 @@ hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_
 template <int ST>
 hipError_t init_t(const KCache &c, const float *states, int64_t stride, const int32_t *slot_idx, int n,
                   hipStream_t st) {
+  if constexpr (ST == kNVFP4) {
+    init_max_kernel<ST><<<dim3((unsigned)((int64_t)n * c.H)), dim3(kWaves * 64), 0, st>>>(c, states, stride, slot_idx);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   init_rows_kernel<ST><<<dim3((unsigned)((int64_t)n * c.H)), dim3(kWaves * 64), 0, st>>>(c, states, stride,
                                                                                          slot_idx);
   hipError_t err = hipGetLastError();

@@ -2,9 +2,12 @@
 
 The oracle defines the fused call as a flush of the first k live tokens
 followed by the step with pnat - k.  Checked here on the GPU through the C
-ABI: outputs and cache against that oracle composition (bounds as for the
-step and the flush), the GPU's own flush-then-step bit for bit, k = 0 against
-the plain monolith step bit for bit, and invalid k reported and skipped.
+ABI: outputs against the oracle's plain step on the GPU's own post-fold
+checkpoint at the plain bound, and against the oracle's composition (plus the
+propagation of the accepted state differences); cache against the oracle's
+flush (bounds as for the flush); the GPU's own flush-then-step bit for bit,
+k = 0 against the plain monolith step bit for bit, and invalid k reported and
+skipped.
 """
 import numpy as np
 import pytest
@@ -60,10 +63,7 @@ def test_fused_step_parity(case):
     ref_cache = cache.copy()
     ref, st = O.replay_step(ref_cache, step, num_fold=k)
     assert st == 0
-    got = gh.to_f64(out)
-    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
-    excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, out_dtype) * (1.0 + np.abs(ref)) - extra
-    assert np.all(excess <= 1e-12), "max excess %g (plain rel err %g)" % (np.max(excess), gh.rel_err(got, ref))
+    gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, out_dtype)
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)
@@ -131,8 +131,7 @@ def test_fused_invalid_fold_is_skipped_and_reported():
     assert st == ssu.SSU_STATUS_BAD_FOLD
     got = gh.to_f64(out)
     assert np.all(got[3:9] == 0.0)
-    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
-    assert np.all(np.abs(got - ref) <= 2e-2 * (1.0 + np.abs(ref)) + extra + 1e-12)
+    gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, "bf16")
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     for b in (1, 2):
         s = int(step.slot_idx[b])
@@ -186,10 +185,7 @@ def test_fp8_fold_extreme_rows(kind):
         assert status == 0
         ref, st_ = O.replay_step(ref_cache, step, num_fold=k)
         assert st_ == 0
-        got = gh.to_f64(out)
-        extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
-        excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, "bf16") * (1.0 + np.abs(ref)) - extra
-        assert np.all(excess <= 1e-12 * (1.0 + np.abs(ref))), "max excess %g" % np.max(excess)
+        gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, "bf16")
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     sc = [gpu.scale_view(s).astype(np.float64) for s in (2, 3, 4)]
     assert np.min(sc[1]) > 2.0 ** 70 and np.median(sc[2]) > 2.0 ** 100, (np.min(sc[1]), np.median(sc[2]))
@@ -229,10 +225,7 @@ def test_fused_empty_windows(state_dtype):
     ref_cache = cache.copy()
     ref, st = O.replay_step(ref_cache, step, num_fold=k)
     assert st == 0
-    got = gh.to_f64(out)
-    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
-    excess = np.abs(got - ref) - gh.tol_for(spec.state_dtype, "bf16") * (1.0 + np.abs(ref)) - extra
-    assert np.all(excess <= 1e-12), "max excess %g" % np.max(excess)
+    gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, "bf16")
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)

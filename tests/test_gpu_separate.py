@@ -169,10 +169,7 @@ def test_separate_fused_step_parity(name, with_z):
     ref_cache = cache.copy()
     ref, st = O.replay_step(ref_cache, step, num_fold=k, seed=seed)
     assert st == 0
-    got = gh.to_f64(out)
-    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache)
-    excess = np.abs(got - ref) - 2e-2 * (1.0 + np.abs(ref)) - extra
-    assert np.all(excess <= 1e-12), "max excess %g" % np.max(excess)
+    gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, "bf16")
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     assert np.array_equal(gpu.x_cache, ref_cache.x_cache)
     assert np.array_equal(gpu.B_cache, ref_cache.B_cache)

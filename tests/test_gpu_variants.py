@@ -98,12 +98,7 @@ def test_variants_with_fused_flush(case):
     ref_cache = cache.copy()
     ref, st = O.replay_step(ref_cache, step, num_fold=k)
     assert st == 0
-    got = gh.to_f64(out)
-    # the gate scales the propagated state difference by |silu(z)|
-    zv = gh.bf16_bits_to_f64(step.z)
-    gate = np.abs(zv / (1.0 + np.exp(-zv)))
-    extra = gh.state_propagation_bound(spec, step, k, gpu, ref_cache) * gate
-    assert np.all(np.abs(got - ref) <= gh.tol_for(spec.state_dtype, out_dtype) * (1 + np.abs(ref)) + extra + 1e-12)
+    gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, out_dtype)
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
