@@ -264,6 +264,30 @@ int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_b
 int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t stream);
 
 /*
+ * ssu_replay_step for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step, bit for bit, except that the SPLIT algorithm's scratch (the fp32 C.B
+ * table of every (entry, group), ssu_workspace_size bytes) is a device array
+ * the library holds, SSU_NOALLOC_SCRATCH_BYTES bytes on every GPU it runs on
+ * until the process ends, instead of step->workspace, which is ignored.
+ *  - A step whose SPLIT scratch would exceed SSU_NOALLOC_SCRATCH_BYTES
+ *    (ssu_workspace_size(cache, batch, max_seqlen) > it: at 128 bytes per
+ *    (entry, group, token), e.g. batch 2048 with 8 groups and 8 tokens fits,
+ *    batch 2049 does not) returns SSU_ERR_WORKSPACE before any launch.
+ *  - Allocates and frees nothing.  Its first call on a device looks up the
+ *    array's device address there (hipGetSymbolAddress; SSU_ERR_HIP if that
+ *    fails); devices 0..63.
+ *  - Every call on one GPU shares that GPU's array and it keeps the last
+ *    call's contents (a call reads only what it wrote itself): calls that may
+ *    overlap on one GPU (streams not ordered with each other) race, and the
+ *    caller must order them.
+ * A step that AUTO resolves to MONOLITH uses no scratch and runs exactly as
+ * ssu_replay_step.
+ */
+#define SSU_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int ssu_replay_step_noalloc(const ssu_cache *cache, const ssu_step *step, hipStream_t stream);
+
+/*
  * Flush [FI item 2 (host owns the ring); VP (FP32 flush, nearest-encoded FP8
  * with FP32 row scales)].  For each j with slot = slot_idx[j] valid and
  * k = num_fold[j] in [1, ring_len]: fold the first k live ring tokens into

@@ -76,6 +76,8 @@ _lib.ssu_init_state.restype = ctypes.c_int
 _lib.ssu_init_state.argtypes = [ctypes.POINTER(SsuCache), _P, _I64, _P, _I32, ctypes.c_uint64, _P]
 _lib.ssu_replay_step.restype = ctypes.c_int
 _lib.ssu_replay_step.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep), _P]
+_lib.ssu_replay_step_noalloc.restype = ctypes.c_int
+_lib.ssu_replay_step_noalloc.argtypes = [ctypes.POINTER(SsuCache), ctypes.POINTER(SsuStep), _P]
 _lib.ssu_flush.restype = ctypes.c_int
 _lib.ssu_flush.argtypes = [ctypes.POINTER(SsuCache), _P, _P, _P, _I32, ctypes.c_uint64, _P]
 _lib.ssu_resolve_algo.restype = ctypes.c_int
@@ -87,9 +89,10 @@ _lib.ssu_set_split_threshold.argtypes = [_I64]
 _lib.ssu_last_error.restype = ctypes.c_char_p
 _lib.ssu_last_error.argtypes = []
 
-EXPORTED = ("ssu_workspace_size", "ssu_init_state", "ssu_replay_step", "ssu_flush",
+EXPORTED = ("ssu_workspace_size", "ssu_init_state", "ssu_replay_step", "ssu_replay_step_noalloc", "ssu_flush",
             "ssu_resolve_algo", "ssu_get_split_threshold", "ssu_set_split_threshold",
             "ssu_last_error")
+SSU_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class SsuError(RuntimeError):
@@ -124,6 +127,10 @@ def ssu_init_state(cache: SsuCache, states: int, states_batch_stride: int, slot_
 
 def ssu_replay_step(cache: SsuCache, step: SsuStep, stream: int = 0) -> int:
     return _lib.ssu_replay_step(ctypes.byref(cache), ctypes.byref(step), stream)
+
+
+def ssu_replay_step_noalloc(cache: SsuCache, step: SsuStep, stream: int = 0) -> int:
+    return _lib.ssu_replay_step_noalloc(ctypes.byref(cache), ctypes.byref(step), stream)
 
 
 def ssu_flush(cache: SsuCache, slot_idx: int, num_fold: int, A: int, n: int, sr_seed: int = 0,

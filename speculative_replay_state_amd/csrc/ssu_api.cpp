@@ -5,6 +5,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
 
 #include "../../include/ssu.h"
 #include "ssu_internal.h"
@@ -185,6 +188,39 @@ int check_step(const ssu_cache *c, const ssu_step *s) {
   return SSU_OK;
 }
 
+// The scratch of ssu_replay_step_noalloc: a file-scope device array (one
+// copy per GPU, held until the process ends).  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up per
+// device with hipGetSymbolAddress, and only that address is passed on.
+constexpr size_t kNoAllocBytes = SSU_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(SSU_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSU_ERR_UNSUPPORTED, "device %d: the no-allocation scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(SSU_ERR_HIP, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                  hipGetErrorString(err));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SSU_OK;
+}
+
 int resolve(const ssu_cache *c, const ssu_step *s) {
   if (s->algo == SSU_ALGO_MONOLITH || s->algo == SSU_ALGO_SPLIT) return s->algo;
   if (s->num_fold) return SSU_ALGO_MONOLITH;
@@ -215,13 +251,14 @@ int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step) {
   return resolve(cache, step);
 }
 
-int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t stream) {
-  int rc = check_cache(cache);
-  if (rc != SSU_OK) return rc;
-  rc = check_step(cache, step);
-  if (rc != SSU_OK) return rc;
-  if (step->batch == 0) return ok();
-  const int algo = resolve(cache, step);
+}  // extern "C"
+
+namespace {
+
+// ssu_replay_step after validation, with the SPLIT scratch `ws` of ws_bytes
+// bytes (the caller's workspace or the no-allocation array).
+int replay_step_checked(const ssu_cache *cache, const ssu_step *step, int algo, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
   ssu::KStep k;
   k.batch = step->batch;
   k.T = step->max_seqlen;
@@ -245,17 +282,50 @@ int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t st
   hipError_t err;
   if (algo == SSU_ALGO_SPLIT) {
     const size_t need = split_bytes(cache, step->batch, step->max_seqlen);
-    if (!step->workspace || step->workspace_bytes < need)
-      return fail(SSU_ERR_WORKSPACE, "SPLIT needs a workspace of %zu bytes (got %zu%s)", need,
-                  step->workspace_bytes, step->workspace ? "" : ", NULL");
-    if (!aligned16(step->workspace)) return fail(SSU_ERR_INVALID, "workspace must be 16-byte aligned");
-    k.cb = static_cast<float *>(step->workspace);
+    if (!ws || ws_bytes < need)
+      return fail(SSU_ERR_WORKSPACE, "SPLIT needs a workspace of %zu bytes (got %zu%s)", need, ws_bytes,
+                  ws ? "" : ", NULL");
+    if (!aligned16(ws)) return fail(SSU_ERR_INVALID, "workspace must be 16-byte aligned");
+    k.cb = static_cast<float *>(ws);
     err = ssu::launch_replay_split(kcache(cache, step->sr_seed), k, st, ot, stream);
   } else {
     err = ssu::launch_replay_monolith(kcache(cache, step->sr_seed), k, st, ot, stream);
   }
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssu_replay_step(const ssu_cache *cache, const ssu_step *step, hipStream_t stream) {
+  int rc = check_cache(cache);
+  if (rc != SSU_OK) return rc;
+  rc = check_step(cache, step);
+  if (rc != SSU_OK) return rc;
+  if (step->batch == 0) return ok();
+  return replay_step_checked(cache, step, resolve(cache, step), step->workspace, step->workspace_bytes, stream);
+}
+
+int ssu_replay_step_noalloc(const ssu_cache *cache, const ssu_step *step, hipStream_t stream) {
+  int rc = check_cache(cache);
+  if (rc != SSU_OK) return rc;
+  rc = check_step(cache, step);
+  if (rc != SSU_OK) return rc;
+  if (step->batch == 0) return ok();
+  const int algo = resolve(cache, step);
+  if (algo != SSU_ALGO_SPLIT) return replay_step_checked(cache, step, algo, nullptr, 0, stream);
+  const size_t need = split_bytes(cache, step->batch, step->max_seqlen);
+  if (need > kNoAllocBytes)
+    return fail(SSU_ERR_WORKSPACE,
+                "ssu_replay_step_noalloc: SPLIT needs %zu bytes of scratch for batch %d, max_seqlen %d, %d groups; "
+                "the library's array holds %zu (SSU_NOALLOC_SCRATCH_BYTES)",
+                need, step->batch, step->max_seqlen, cache->ngroups, kNoAllocBytes);
+  void *ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != SSU_OK) return rc;
+  return replay_step_checked(cache, step, algo, ws, kNoAllocBytes, stream);
 }
 
 int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
