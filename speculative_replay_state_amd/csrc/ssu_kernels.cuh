@@ -1941,6 +1941,128 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
                                   (ST == kFP8 && kAbLds) ? fl.osc : nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// PAIR: plain steps of 16-bit checkpoints, two heads of one group per wave.
+// A wave issues every load of both heads (checkpoint tiles, windows) and of
+// their group (C, the B rows of the window) at once, then reads out head A,
+// stores it, and reads out head B.  A one-head wave spends much of its life
+// on the latency of its loads and, at its end, on the acknowledgements of its
+// stores (a wave's memory operations must complete before it ends), with no
+// loads in flight meanwhile; two heads per wave pay each of those waits once
+// per two heads, keep 32 KiB of checkpoint in flight per wave, and share C
+// and C.B.  Workgroup: 4 waves, heads h0 .. h0 + 7 of one entry, wave w runs
+// h0 + w and h0 + 4 + w (both in one group: the group size is a multiple of
+// 8).  Same arithmetic as the other paths, so the outputs are bit-identical.
+// ---------------------------------------------------------------------------
+
+#ifndef SSU_PAIR_MIN_UNITS
+#define SSU_PAIR_MIN_UNITS 32768  // (entry, head) pairs from which plain 16-bit steps run two heads per wave
+#endif
+constexpr int kPairHeads = 2 * kHeadWaves;  // heads per workgroup
+
+// C of the group's new tokens in the readout's k order, without branches: the
+// rows of tokens past T_b (>= 1) load token T_b - 1 again; their readout
+// column, C.B row and coefficients are never used.
+template <int ST, int KW>
+__device__ __forceinline__ void load_item_c_flat(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
+                                                 ItemLoads<ST, KW> &il) {
+  static_assert(ST == kBF16 || ST == kF16, "16-bit checkpoints");
+  const int m = lane & 15, q = lane >> 4;
+  const int mm = m < e.Tb ? m : e.Tb - 1;
+  const uint16_t *Crow = s.C + ((int64_t)(e.bos + mm) * c.G + g) * kDState + 32 * q;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u32x4 v = ld16(Crow + 8 * u);
+    il.craw[u] = ST == kF16 ? __builtin_bit_cast(u32x4, bf16x8_to_f16x8(v)) : v;
+  }
+}
+
+// The operands of the group's C.B (load_cb with its own C, u order), without
+// branches: window positions past S (>= 1) load position S - 1 again and
+// tokens past T_b token T_b - 1; those columns and rows are never used.
+template <int KW>
+__device__ __forceinline__ void load_cb_flat(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
+                                             CbLoads<KW> &cl) {
+  const int m = lane & 15, q = lane >> 4, L = c.L, S = e.pnat + e.Tb;
+  const int mm = m < e.Tb ? m : e.Tb - 1;
+  const uint16_t *Crow = s.C + ((int64_t)(e.bos + mm) * c.G + g) * kDState;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cl.ca[u] = __builtin_bit_cast(bf16x8, ld16(Crow + cb_k(false, u, q)));
+  const uint16_t *Bring = reinterpret_cast<const uint16_t *>(c.Bc + (int64_t)e.slot * c.B_stride) +
+                          (int64_t)g * L * kDState;
+#pragma unroll
+  for (int nb = 0; nb < KW / 16; ++nb) {
+    const int sig = nb * 16 + m, sg = sig < S ? sig : S - 1;
+    const uint16_t *rp = sg < e.pnat ? Bring + ring_pos(e.r, sg, L) * kDState
+                                     : s.B + ((int64_t)(e.bos + sg - e.pnat) * c.G + g) * kDState;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cl.bw[nb][u] = ld16(rp + cb_k(false, u, q));
+  }
+}
+
+template <int ST, int OT, int KW, bool HAS_Z>
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void pair_kernel(KCache c, KStep s, int ptiles, int64_t ntiles) {
+  static_assert(ST == kBF16 || ST == kF16, "two 16-bit tiles per wave");
+  constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
+  constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
+  __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  if (tile >= ntiles) return;
+  const int b = (int)(tile / ptiles);
+  const int h0 = (int)(tile - (int64_t)b * ptiles) * kPairHeads;
+  const int hA = h0 + wave, hB = hA + kHeadWaves, g = h0 / c.hpg, m = lane & 15, q = lane >> 4;
+  uint16_t *xT = reinterpret_cast<uint16_t *>(lds_all[wave]);
+  float *cbw = reinterpret_cast<float *>(lds_all[wave] + kXTWords);
+
+  // 1. both tiles as soon as the slot is known (an out-of-range slot loads
+  //    slot 0's page, in bounds and never used), then the entry's words as
+  //    scalar loads, then both windows and the group's C and B rows: every
+  //    load of the wave is issued before its first store
+  const int slot0 = s.slot_idx[b];
+  const bool slot_ok = slot0 > 0 && slot0 < c.num_slots;
+  HeadLoads<ST, KW> la, lb;
+  load_state<ST, KW>(c, slot_ok ? slot0 : 0, hA, lane, la);
+  load_state<ST, KW>(c, slot_ok ? slot0 : 0, hB, lane, lb);
+  __builtin_amdgcn_sched_barrier(0);
+  const Entry e = make_entry(c, s, slot0, load_entry_in(c, s, b, slot0, slot_ok), h0 == 0 && wave == 0);
+  if (e.mode == 0) return;
+  if (e.mode == 1) {
+    zero_out_head<OT>(s, c.H, e, hA, lane);
+    zero_out_head<OT>(s, c.H, e, hB, lane);
+    return;
+  }
+  if (e.Tb == 0) return;  // no new token: nothing to read out or append
+  load_window<ST, OT, KW, HAS_Z, true>(c, s, e, hA, lane, la);
+  load_window<ST, OT, KW, HAS_Z, true>(c, s, e, hB, lane, lb);
+  ItemLoads<ST, KW> il;
+  load_item_c_flat<ST, KW>(c, s, e, g, lane, il);
+  CbLoads<KW> cl;
+  load_cb_flat<KW>(c, s, e, g, lane, cl);
+
+  // 2. C.B of the group (the wave of its first head appends the B rows)
+  {
+    f32x4 cb[KW / 16];
+    cb_tiles<KW>(cl, cb, nullptr);
+    if (hA % c.hpg == 0) append_B_rows<KW>(c, e, g, lane, cl, false);
+#pragma unroll
+    for (int nb = 0; nb < KW / 16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cbw[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
+  }
+  wave_sync();  // C.B rows written by this wave -> read below
+  load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
+  wave_sync();  // C.B rows read before the LDS words are reused
+
+  // 3. the two heads, one after the other.  (A wave that loaded a third head
+  //    after storing the first, reusing the first head's registers, measured
+  //    slower: one counter tracks a wave's loads and stores in issue order,
+  //    so using those loads waits for the stores before them.)
+  head_compute<ST, OT, KW, HAS_Z>(c, s, e, hA, la, il, xT, lds_all[wave], lane);
+  head_compute<ST, OT, KW, HAS_Z>(c, s, e, hB, lb, il, xT, lds_all[wave], lane);
+}
+
 // Ring bookkeeping after a flush: ring_start <- (ring_start + k) mod L.
 template <int ST>
 __global__ void ring_advance_kernel(KCache c, const int32_t *slot_idx, const int32_t *num_fold, int n) {
@@ -2159,6 +2281,18 @@ hipError_t fused_z(const KCache &c, const KStep &s, hipStream_t st) {
   }
 }
 
+template <int ST, int OT, bool HAS_Z>
+hipError_t pair_z(const KCache &c, const KStep &s, hipStream_t st) {
+  if constexpr (ST == kBF16 || ST == kF16) {
+    const int ptiles = c.H / kPairHeads;
+    const int64_t ntiles = (int64_t)s.batch * ptiles;
+    pair_kernel<ST, OT, 16, HAS_Z><<<dim3(xcd_grid(ntiles)), dim3(kHeadWaves * 64), 0, st>>>(c, s, ptiles, ntiles);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int ST, int OT, bool SPLIT, bool HAS_Z>
 hipError_t replay_z(const KCache &c, const KStep &s, hipStream_t st) {
   return c.L <= 16 ? replay_kw<ST, OT, 16, SPLIT, HAS_Z>(c, s, st) : replay_kw<ST, OT, 32, SPLIT, HAS_Z>(c, s, st);
@@ -2175,6 +2309,11 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   // 1-3 % faster (batch 256-1024 of 128 heads, varlen or not), fp8 10 %
   // faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint 20 % and
   // nvfp4 57 % slower (those forms of it hold more registers).
+  if constexpr (ST == kBF16 || ST == kF16) {
+    // (rings of up to 16 entries: with a 32-deep window the two register sets spill)
+    if ((int64_t)s.batch * c.H >= SSU_PAIR_MIN_UNITS && c.hpg % kPairHeads == 0 && c.L <= 16)
+      return s.z ? pair_z<ST, OT, true>(c, s, st) : pair_z<ST, OT, false>(c, s, st);
+  }
   if constexpr (ST == kBF16 || ST == kFP8) {
     if ((ST == kBF16 || !c.recur) && (int64_t)s.batch * c.H >= kPerHeadPlainUnits)
       return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);

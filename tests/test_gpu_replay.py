@@ -54,6 +54,11 @@ CASES = {
                           pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "fp8_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="fp8"), batch=256, T=4,
                          pnat_max=12, out="bf16", n_padding=2),
+    # 32768 pairs of a 16-bit checkpoint: the monolith runs two heads per wave (groups of 16 and of 8)
+    "f16_pair": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="f16"), batch=256, T=8,
+                     pnat_max=8, out="bf16", varlen=True, n_padding=3),
+    "bf16_pair_hpg8": dict(spec=dict(num_slots=600, nheads=64, ngroups=8, state_dtype="bf16"), batch=512, T=4,
+                           pnat_max=4, out="bf16", n_padding=2),
 }
 
 
@@ -230,3 +235,35 @@ def test_status_bits_and_padding():
     for b in (3, 4, 5):
         s = int(step.slot_idx[b])
         assert np.array_equal(after.state[s], before.state[s])
+
+
+@pytest.mark.parametrize("state_dtype", ["bf16", "f16"])
+def test_pair_path_empty_entries(state_dtype):
+    """Two heads per wave (plain 16-bit steps from 32768 pairs) with varlen
+    entries that have no new token, padding entries and the last entry empty:
+    bit for bit against the split, and against the oracle."""
+    from tests.test_gpu_fused import _with_empty_entries
+    spec = synth.CacheSpec(num_slots=300, nheads=128, ngroups=8, state_dtype=state_dtype, slot_pad=256)
+    cache = synth.make_cache(spec, 4100)
+    step = synth.make_step(spec, 256, 8, 4101, 8, varlen=True, n_padding=4)
+    step = _with_empty_entries(step, [0, 17, 100, 255])
+    print("pair path empty entries", state_dtype, "Tb", np.diff(step.cu_seqlens)[:20], flush=True)
+    outs, caches = [], []
+    for algo in ("monolith", "split"):
+        t = sd.upload_cache(cache, gh.DEV)
+        st = sd.upload_step(step, gh.DEV)
+        dc = gh.device_cache(spec, t)
+        out = gh.out_tensor(step, spec, "bf16")
+        gh.run_step(dc, st, step, out, "bf16", algo)
+        torch.cuda.synchronize()
+        assert int(dc.status.item()) == 0
+        outs.append(out)
+        caches.append(sd.download_cache(spec, t))
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    for f in sd.CACHE_FIELDS + ("ring_start",):
+        assert np.array_equal(getattr(caches[0], f), getattr(caches[1], f)), f
+    ref_cache = cache.copy()
+    ref, status = O.replay_step(ref_cache, step)
+    assert status == 0
+    assert gh.rel_err(gh.to_f64(outs[0]), ref) <= gh.tol_for(state_dtype, "bf16")
+    gh.check_cache_after_step(spec, cache, caches[0], ref_cache)
