@@ -220,9 +220,10 @@ typedef struct ssu_step {
   uint64_t sr_seed; /* stochastic-rounding seed of a fused fold (separate checkpoints) */
 } ssu_step;
 
-/* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen):
- * the fp32 C.B products of every (entry, group).  Returns 0 for an invalid
- * cache description. */
+/* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen): the
+ * fp32 C.B products of every (entry, group) [FI Description item 1: the
+ * precompute writes C.B to caller-provided, graph-safe scratch, allocated by
+ * the caller like the output].  Returns 0 for an invalid cache description. */
 size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen);
 
 /*

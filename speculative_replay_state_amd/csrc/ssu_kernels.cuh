@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/ssu.h"
 #include "ssu_internal.h"
 
@@ -74,9 +76,10 @@ __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<c
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 // Streaming (non-temporal) forms for data touched once per call whose every
 // wave instruction covers whole cache lines (the tiled checkpoint, whose
-// chunk u of a row block is 1 KiB contiguous over the wave, and the x
-// windows).  On MI355X they lift a line-contiguous read stream from ~5.7 to
-// ~6.1 TB/s and a read + write stream from ~5.4 to ~6.2 TB/s.
+// chunk u of a row block is 1 KiB contiguous over the wave, the x windows and
+// the staged output rows).  Measured on the large-batch step (bf16, batch
+// 1024 of 128 heads, one head per wave): its output rows written with plain
+// stores took 469 us per step against 450 us with streaming stores.
 __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
@@ -2207,10 +2210,29 @@ int chunks_per_group(int64_t batch, int G, int hpg, int64_t resident_waves) {
   return hpg;
 }
 
+// Blocks of a kernel resident on the current device, from the occupancy
+// query, remembered per device (devices 0..63; others query every call).  A
+// host-side query: no stream operation, so a first call inside a HIP graph
+// capture is fine.
+template <typename K>
+int resident_on_device(K kernel, std::atomic<int> *cache) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < 64) {
+    int r = cache[dev].load(std::memory_order_relaxed);
+    if (r == 0) {
+      r = resident_blocks(kernel, 0);
+      cache[dev].store(r, std::memory_order_relaxed);
+    }
+    return r;
+  }
+  return resident_blocks(kernel, 0);
+}
+
 template <int ST, int OT, int KW, bool SPLIT, bool HAS_Z>
 hipError_t replay_kw(const KCache &c, const KStep &s, hipStream_t st) {
-  static int resident = 0;  // blocks resident on the device (per template instance)
-  if (resident == 0) resident = resident_blocks(replay_kernel<ST, OT, KW, SPLIT, HAS_Z>, 0);
+  static std::atomic<int> cache[64];  // per template instance, per device
+  const int resident = resident_on_device(replay_kernel<ST, OT, KW, SPLIT, HAS_Z>, cache);
   if (SPLIT) {
     const int64_t pre_items = (int64_t)s.batch * c.G;
     precompute_kernel<KW, cb_qorder(ST)><<<dim3((unsigned)((pre_items + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, st>>>(c, s);
