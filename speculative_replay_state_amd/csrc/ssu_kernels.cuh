@@ -580,27 +580,30 @@ __device__ __forceinline__ void load_gate(const KStep &s, int H, const Entry &e,
   }
 }
 
-template <int OT, bool HAS_Z>
+// NRB < 4: acc holds row blocks rb0 .. rb0 + NRB - 1 (values 16 rb0 ..
+// 16 (rb0 + NRB) - 1 of each output row), which are all this call writes.
+template <int OT, bool HAS_Z, int NRB = 4>
 __device__ __forceinline__ void store_out_staged(const KStep &s, int H, const Entry &e, int h, int lane,
-                                                 const f32x4 acc[4], const u32x4 zw[2], uint32_t *ot) {
+                                                 const f32x4 *acc, const u32x4 zw[2], uint32_t *ot, int rb0 = 0) {
+  static_assert(NRB == 4 || !HAS_Z, "the gate chunks cover whole rows");
   const int m = lane & 15, q = lane >> 4;
   if constexpr (OT == kOutF32 || HAS_Z) {  // fp32 rows (the gate is applied before rounding)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
       *reinterpret_cast<u32x4 *>(ot + m * kOutRowWords + rb * 16 + 4 * q) = __builtin_bit_cast(u32x4, acc[rb]);
   } else {
     // bf16 rows of 64 values = 32 words, same row pitch
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
       *reinterpret_cast<u32x2 *>(ot + m * kOutRowWords + rb * 8 + 2 * q) =
           u32x2{pack_bf16(acc[rb][0], acc[rb][1]), pack_bf16(acc[rb][2], acc[rb][3])};
   }
   wave_sync();
-  constexpr int kChunks = OT == kOutF32 ? 16 : 8;  // 16-byte output chunks per token row
-  constexpr int kRowsPer = 64 / kChunks;           // token rows per instruction
+  constexpr int kChunks = (OT == kOutF32 ? 16 : 8) * NRB / 4;  // 16-byte output chunks per token row
+  constexpr int kRowsPer = 64 / kChunks;                       // token rows per instruction
   const int c = lane % kChunks, i0 = lane / kChunks;
 #pragma unroll
-  for (int r = 0; r < kMaxTokens / kRowsPer; ++r) {
+  for (int r = 0; r < (kMaxTokens + kRowsPer - 1) / kRowsPer; ++r) {
     const int i = i0 + kRowsPer * r;
     if (i < e.Tb) {
       u32x4 v;
@@ -622,7 +625,7 @@ __device__ __forceinline__ void store_out_staged(const KStep &s, int H, const En
                   pack_bf16(y1[0] * g[4], y1[1] * g[5]), pack_bf16(y1[2] * g[6], y1[3] * g[7])};
       }
       uint8_t *dst = static_cast<uint8_t *>(s.out) +
-                     (((int64_t)(e.bos + i) * H + h) * kHeadDim) * (OT == kOutF32 ? 4 : 2) + 16 * c;
+                     (((int64_t)(e.bos + i) * H + h) * kHeadDim + 16 * rb0) * (OT == kOutF32 ? 4 : 2) + 16 * c;
       st16_nt(dst, v);
     }
   }
@@ -1246,15 +1249,18 @@ struct ItemLoads {
 };
 
 // The checkpoint tile of (slot, h): 16-byte chunks, 1 KiB contiguous per wave
-// instruction, streamed (non-temporal).
-template <int ST, int KW>
-__device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int lane, HeadLoads<ST, KW> &ld) {
+// instruction, streamed (non-temporal).  NRB < 4: row blocks rb0 ..
+// rb0 + NRB - 1 only, into raw[0 .. NRB - 1].
+template <int ST, int KW, int NRB = 4>
+__device__ __forceinline__ void load_state(const KCache &c, int slot, int h, int lane, HeadLoads<ST, KW> &ld,
+                                           int rb0 = 0) {
   using T = HeadLoads<ST, KW>;
+  static_assert(NRB == 4 || ST == kF32 || ST == kBF16 || ST == kF16, "part tiles: 16- and 32-bit checkpoints");
   const uint8_t *hp = c.state + (int64_t)slot * c.state_stride + (int64_t)h * st_head_bytes(ST);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_off(rb, u, lane, T::kNLD));
+    for (int u = 0; u < T::kNLD; ++u) ld.raw[rb][u] = ld16_nt(hp + tile_off(rb0 + rb, u, lane, T::kNLD));
   if constexpr (ST == kNVFP4) {  // the block scales and the head scale belong to the tile
     ld.sfw = ld8(c.scale + (int64_t)slot * c.scale_stride + (int64_t)h * (kHeadElems / 16) + lane * 8);
     ld.gs = nvfp4_words(c, slot)[0];
@@ -1386,10 +1392,15 @@ __device__ __forceinline__ void load_cb_row(const Entry &e, const float *cb, int
                          : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-template <int ST, int OT, int KW, bool HAS_Z>
+// NRB < 4 (part tiles): ld.raw holds row blocks rb0 .. rb0 + NRB - 1 and only
+// those output values are read out and written; append = false leaves the
+// dt and x rings to another part's wave.
+template <int ST, int OT, int KW, bool HAS_Z, int NRB = 4>
 __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, const Entry &e, int h,
                                              const HeadLoads<ST, KW> &ld, const ItemLoads<ST, KW> &il,
-                                             uint16_t *xT, uint32_t *ot, int lane, const float *osc = nullptr) {
+                                             uint16_t *xT, uint32_t *ot, int lane, const float *osc = nullptr,
+                                             int rb0 = 0, bool append = true) {
+  static_assert(NRB == 4 || ST == kF32 || ST == kBF16 || ST == kF16, "part tiles: 16- and 32-bit checkpoints");
   using WC = Win<KW>;
   using V = typename WC::V;
   const int m = lane & 15, q = lane >> 4;
@@ -1403,7 +1414,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
     dtp = ld.dtv + ld.dtb;
     if (s.dt_softplus) dtp = softplus_f(dtp);
     float *dtring = reinterpret_cast<float *>(c.dtc + (int64_t)e.slot * c.dt_stride) + h * L;
-    dtring[ring_pos(e.r, lane, L)] = dtp;
+    if (append) dtring[ring_pos(e.r, lane, L)] = dtp;
   }
   const float cum = scan_win<KW>(ld.Ah * dtp, lane);
 
@@ -1415,7 +1426,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   for (int jj = 0; jj < WC::kRounds; ++jj) {
     const int sig = xw_pos(lane, jj), pc = xw_chunk(lane);
     const u32x4 v = ld.xw[jj];
-    if (sig >= e.pnat && sig < S) st16(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8, v);
+    if (append && sig >= e.pnat && sig < S) st16(xring + ring_pos(e.r, sig, L) * kHeadDim + pc * 8, v);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
       xT[(pc * 8 + tt) * WC::kXS + sig] = (uint16_t)((tt & 1) ? (v[tt >> 1] >> 16) : (v[tt >> 1] & 0xFFFFu));
@@ -1447,10 +1458,10 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   }
   wave_sync();  // xT written by this wave -> read below
 
-  // 4. checkpoint readout: acc[rb][j] = sum_n h0[16 rb + 4 q + j][n] C_i[n]
-  f32x4 acc[4];
+  // 4. checkpoint readout: acc[rb][j] = sum_n h0[16 (rb0 + rb) + 4 q + j][n] C_i[n]
+  f32x4 acc[NRB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     if constexpr (ST == kBF16) {
 #pragma unroll
@@ -1488,7 +1499,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   // 5. epilogue: decay to the token (and fp8 row scale), then add the ring /
   //    new-token replay terms through the x MFMA.
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (ST == kFP8)  // row 16 rb + 4 q + j: loaded, or held by lane 4 q + j in osc[rb]
@@ -1498,7 +1509,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
       else
         acc[rb][j] = acc[rb][j] * beta;
     }
-    const V xa = *reinterpret_cast<const V *>(xT + (rb * 16 + m) * WC::kXS + WC::kE * q);
+    const V xa = *reinterpret_cast<const V *>(xT + ((rb0 + rb) * 16 + m) * WC::kXS + WC::kE * q);
     acc[rb] = mfma_win<KW>(xa, whi, acc[rb]);
     acc[rb] = mfma_win<KW>(xa, wlo, acc[rb]);
     if constexpr (ST == kF32) acc[rb] = mfma_win<KW>(xa, wlo2, acc[rb]);
@@ -1506,7 +1517,7 @@ __device__ __forceinline__ void head_compute(const KCache &c, const KStep &s, co
   wave_sync();  // xT reads done before the tile is reused
 
   // 6. output rows of the new tokens
-  store_out_staged<OT, HAS_Z>(s, H, e, h, lane, acc, ld.zw, ot);
+  store_out_staged<OT, HAS_Z, NRB>(s, H, e, h, lane, acc, ld.zw, ot, rb0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1959,7 +1970,11 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
 // ---------------------------------------------------------------------------
 
 #ifndef SSU_PAIR_MIN_UNITS
-#define SSU_PAIR_MIN_UNITS 32768  // (entry, head) pairs from which plain 16-bit steps run two heads per wave
+// (entry, head) pairs from which plain 16-bit steps run two heads per wave.
+// Measured against the persistent kernel (fp16 prod, graph-replayed steps):
+// batch 16 (2048 pairs) 12.47 against 12.78 us, 32: 18.95 / 19.18, 64: 33.16 /
+// 32.84, 128: 61.00 / 64.71, 192: 89.82 / 96.44; bf16 mtp (4096) 18.35 / 18.31.
+#define SSU_PAIR_MIN_UNITS 2048
 #endif
 constexpr int kPairHeads = 2 * kHeadWaves;  // heads per workgroup
 
@@ -2064,6 +2079,75 @@ void pair_kernel(KCache c, KStep s, int ptiles, int64_t ntiles) {
   //    so using those loads waits for the stores before them.)
   head_compute<ST, OT, KW, HAS_Z>(c, s, e, hA, la, il, xT, lds_all[wave], lane);
   head_compute<ST, OT, KW, HAS_Z>(c, s, e, hB, lb, il, xT, lds_all[wave], lane);
+}
+
+// ---------------------------------------------------------------------------
+// D-SPLIT: plain steps of few (entry, head) pairs (small batches).  The
+// head's 64 state rows are cut into DS parts of 64 / DS rows and each part is
+// read out by a wave of its own, one wave per (entry, head, part), so a small
+// batch still spreads over the chip and each wave's serial work (its share of
+// the tile loads, the readout MFMAs and the output stores) shrinks DS-fold.
+// Every part forms the group's C.B and the head's decay prefix itself (a few
+// hundred flops) and loads the whole x window (the other parts' rows come
+// from L2); part 0 appends the new tokens' x and dt' to the rings, part 0 of
+// the group's first head its B rows.  Each output value is the same
+// arithmetic as on the other paths: the outputs are bit-identical.
+// ---------------------------------------------------------------------------
+
+template <int ST, int OT, int KW, int DS>
+__global__ __launch_bounds__(kHeadWaves * 64) void dsplit_kernel(KCache c, KStep s, int64_t nwaves) {
+  static_assert(ST == kF32 || ST == kBF16 || ST == kF16, "part tiles: 16- and 32-bit checkpoints");
+  static_assert(DS == 2 || DS == 4, "parts of 2 or 1 row blocks");
+  constexpr int NRB = 4 / DS;
+  constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
+  constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
+  __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t gw = xcd_tile(blockIdx.x, gridDim.x) * kHeadWaves + wave;
+  if (gw >= nwaves) return;
+  const int part = (int)(gw % DS);
+  const int64_t unit = gw / DS;
+  const int b = (int)(unit / c.H), h = (int)(unit - (int64_t)b * c.H);
+  const int g = h / c.hpg, m = lane & 15, q = lane >> 4, rb0 = part * NRB;
+  uint16_t *xT = reinterpret_cast<uint16_t *>(lds_all[wave]);
+  float *cbw = reinterpret_cast<float *>(lds_all[wave] + kXTWords);
+
+  // the part's rows of the tile as soon as the slot is known (an out-of-range
+  // slot loads slot 0's page, in bounds and never used), then the entry's
+  // words, then the window and the group's C and B rows
+  const int slot0 = s.slot_idx[b];
+  const bool slot_ok = slot0 > 0 && slot0 < c.num_slots;
+  HeadLoads<ST, KW> ld;
+  load_state<ST, KW, NRB>(c, slot_ok ? slot0 : 0, h, lane, ld, rb0);
+  __builtin_amdgcn_sched_barrier(0);
+  const Entry e = make_entry(c, s, slot0, load_entry_in(c, s, b, slot0, slot_ok), h == 0 && part == 0);
+  if (e.mode == 0) return;
+  if (e.mode == 1) {
+    if (part == 0) zero_out_head<OT>(s, c.H, e, h, lane);
+    return;
+  }
+  if (e.Tb == 0) return;  // no new token: nothing to read out or append
+  load_window<ST, OT, KW, false, true>(c, s, e, h, lane, ld);
+  ItemLoads<ST, KW> il;
+  if constexpr (ST == kF32)
+    load_item_c<ST, KW>(c, s, e, g, lane, il);
+  else
+    load_item_c_flat<ST, KW>(c, s, e, g, lane, il);
+  CbLoads<KW> cl;
+  load_cb_flat<KW>(c, s, e, g, lane, cl);
+  {
+    f32x4 cb[KW / 16];
+    cb_tiles<KW>(cl, cb, nullptr);
+    if (h % c.hpg == 0 && part == 0) append_B_rows<KW>(c, e, g, lane, cl, false);
+#pragma unroll
+    for (int nb = 0; nb < KW / 16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cbw[(4 * q + j) * kCbLds + nb * 16 + m] = cb[nb][j];
+  }
+  wave_sync();  // C.B rows written by this wave -> read below
+  load_cb_row<ST, KW>(e, cbw, kCbLds, lane, il);
+  wave_sync();  // C.B rows read before the LDS words are reused
+  head_compute<ST, OT, KW, false, NRB>(c, s, e, h, ld, il, xT, lds_all[wave], lane, nullptr, rb0, part == 0);
 }
 
 // Ring bookkeeping after a flush: ring_start <- (ring_start + k) mod L.
@@ -2315,6 +2399,42 @@ hipError_t pair_z(const KCache &c, const KStep &s, hipStream_t st) {
   }
 }
 
+// (entry, head) pairs up to which plain steps of 16- and 32-bit checkpoints
+// split each head's rows over 2 waves, and over 4.  Measured (graph-replayed
+// steps, one MI355X): fp16 prod, batch 1 (128 pairs): 7.25 us per step on the
+// persistent kernel, 5.65 in 2 parts, 5.49 in 4; batch 4 (512): 7.90, 6.17,
+// 7.55; batch 16 (2048): 12.85, 13.79, 17.64; fp32 tiny (16 pairs): 9.71,
+// 6.58, 5.71; bf16 mtp (4096 pairs): 18.24, 19.58, 24.12; batch 8 (1024
+// pairs) in 2 parts 9.96 against about 9.3.
+#ifndef SSU_DSPLIT_MAX_UNITS
+#define SSU_DSPLIT_MAX_UNITS 512
+#endif
+#ifndef SSU_DSPLIT4_MAX_UNITS
+#define SSU_DSPLIT4_MAX_UNITS 256
+#endif
+
+template <int ST, int OT>
+hipError_t dsplit_t(const KCache &c, const KStep &s, int ds, hipStream_t st) {
+  if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {
+    const int64_t nwaves = (int64_t)s.batch * c.H * ds;
+    const dim3 grid(xcd_grid((nwaves + kHeadWaves - 1) / kHeadWaves)), block(kHeadWaves * 64);
+    if (ds == 4) {
+      if (c.L <= 16)
+        dsplit_kernel<ST, OT, 16, 4><<<grid, block, 0, st>>>(c, s, nwaves);
+      else
+        dsplit_kernel<ST, OT, 32, 4><<<grid, block, 0, st>>>(c, s, nwaves);
+    } else {
+      if (c.L <= 16)
+        dsplit_kernel<ST, OT, 16, 2><<<grid, block, 0, st>>>(c, s, nwaves);
+      else
+        dsplit_kernel<ST, OT, 32, 2><<<grid, block, 0, st>>>(c, s, nwaves);
+    }
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int ST, int OT, bool SPLIT, bool HAS_Z>
 hipError_t replay_z(const KCache &c, const KStep &s, hipStream_t st) {
   return c.L <= 16 ? replay_kw<ST, OT, 16, SPLIT, HAS_Z>(c, s, st) : replay_kw<ST, OT, 32, SPLIT, HAS_Z>(c, s, st);
@@ -2339,6 +2459,10 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if constexpr (ST == kBF16 || ST == kFP8) {
     if ((ST == kBF16 || !c.recur) && (int64_t)s.batch * c.H >= kPerHeadPlainUnits)
       return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
+  }
+  if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {
+    const int64_t units = (int64_t)s.batch * c.H;
+    if (!s.z && units <= SSU_DSPLIT_MAX_UNITS) return dsplit_t<ST, OT>(c, s, units <= SSU_DSPLIT4_MAX_UNITS ? 4 : 2, st);
   }
   return s.z ? replay_z<ST, OT, false, true>(c, s, st) : replay_z<ST, OT, false, false>(c, s, st);
 }

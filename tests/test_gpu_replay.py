@@ -49,16 +49,31 @@ CASES = {
                         batch=5, T=16, pnat_max=16, out="f32"),
     "f16_hpg1": dict(spec=dict(num_slots=12, nheads=6, ngroups=6, state_dtype="f16", ring_len=12),
                      batch=7, T=5, pnat_max=7, out="bf16"),
-    # 256 x 128 = 32768 (entry, head) pairs: a plain bf16 or fp8 monolith step runs one head per wave
-    "bf16_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="bf16"), batch=256, T=4,
+    # 342 x 96 = 32832 (entry, head) pairs, groups of 12 heads: a plain bf16 monolith step runs one head per
+    # wave; 33 x 128 fp8 pairs run in the persistent kernel, 256 x 128 in the one-head kernel
+    "bf16_per_head": dict(spec=dict(num_slots=400, nheads=96, ngroups=8, state_dtype="bf16"), batch=342, T=4,
                           pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "fp8_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="fp8"), batch=256, T=4,
                          pnat_max=12, out="bf16", n_padding=2),
-    # 32768 pairs of a 16-bit checkpoint: the monolith runs two heads per wave (groups of 16 and of 8)
+    # 16-bit checkpoints from 2048 pairs (groups of a multiple of 8 heads, rings up to 16): two heads per
+    # wave (groups of 16 and of 8); prod_f16, mtp_bf16 and large_bf16_varlen above run there too
     "f16_pair": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="f16"), batch=256, T=8,
                      pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "bf16_pair_hpg8": dict(spec=dict(num_slots=600, nheads=64, ngroups=8, state_dtype="bf16"), batch=512, T=4,
                            pnat_max=4, out="bf16", n_padding=2),
+    # 513 to 2047 pairs of a 16- or 32-bit checkpoint: the persistent kernel
+    "f16_persistent": dict(spec=dict(num_slots=20, nheads=128, ngroups=8, state_dtype="f16"), batch=12, T=8,
+                           pnat_max=8, out="bf16", varlen=True, n_padding=1),
+    "f32_persistent": dict(spec=dict(num_slots=120, nheads=8, ngroups=2, state_dtype="f32"), batch=100, T=3,
+                           pnat_max=10, out="f32", n_padding=4),
+    # up to 512 pairs: each head's rows split over waves, 2 parts from 257 pairs, 4 parts up to 256
+    # (tiny_f32, bf16_f32out, f32_T16_L32 and f16_hpg1 above run in 4 parts)
+    "bf16_dsplit2": dict(spec=dict(num_slots=8, nheads=128, ngroups=8, state_dtype="bf16"), batch=4, T=6,
+                         pnat_max=8, out="bf16", varlen=True, n_padding=1),
+    "f32_dsplit2_L32": dict(spec=dict(num_slots=48, nheads=8, ngroups=2, state_dtype="f32", ring_len=32),
+                            batch=40, T=12, pnat_max=20, out="f32", n_padding=2),
+    "f16_dsplit4_L24": dict(spec=dict(num_slots=16, nheads=16, ngroups=4, state_dtype="f16", ring_len=24),
+                            batch=10, T=5, pnat_max=19, out="bf16", varlen=True, n_padding=1),
 }
 
 
@@ -239,7 +254,7 @@ def test_status_bits_and_padding():
 
 @pytest.mark.parametrize("state_dtype", ["bf16", "f16"])
 def test_pair_path_empty_entries(state_dtype):
-    """Two heads per wave (plain 16-bit steps from 32768 pairs) with varlen
+    """Two heads per wave (plain 16-bit steps from 2048 pairs) with varlen
     entries that have no new token, padding entries and the last entry empty:
     bit for bit against the split, and against the oracle."""
     from tests.test_gpu_fused import _with_empty_entries
