@@ -54,9 +54,14 @@ constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
 // Waves per SIMD the fused kernel is compiled for.  The kernel is latency
 // bound (each wave streams its tile only between compute phases), so it runs
 // as many waves as fit: the fp8 step with bf16 output folds in 96 registers
-// (5 waves, no spills); the other forms need more and get 3, 2 or 1.
+// (5 waves, no spills); the other forms need more and get 3, 2 or 1.  The
+// NVFP4 step (not gated, rings up to 16) runs 3 waves although 12 registers
+// spill: 344.5 us per step against 351.2 at 2 waves (182 registers, none
+// spilled), batch 256 of 128 heads.
 #define SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP) \
-  (ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
+  (ST == kF32 ? 1                                                                 \
+   : ((KW == 32 || (SEP && !(ST == kNVFP4 && !HAS_Z))) ? 2                        \
+      : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
 #endif
 constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
 // (entry, head) pairs from which a plain bf16 or fp8 step runs one head per wave
@@ -1123,12 +1128,6 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float &y
   y = es > 0.0f ? 1.0f / es : 0.0f;
   return code;
 }
-__device__ __forceinline__ void nvfp4_block_scales(const float *bm, float g, u32x2 &sfw, float *y) {
-  uint32_t sb[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sb[i] = nvfp4_block_scale(bm[i], g, y[i]);
-  sfw = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24), sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
-}
 
 __device__ __forceinline__ float *nvfp4_words(const KCache &c, int slot) {
   return reinterpret_cast<float *>(c.gw + (int64_t)slot * c.gw_stride);
@@ -1156,7 +1155,7 @@ __device__ __forceinline__ float slot_scale(const KCache &c, int slot, int lane,
 
 // The fold of an FP16 recurrence tile rch for an NVFP4 read checkpoint, first
 // pass: the largest |value| of the folded head.  The same instructions on the
-// same operands as fold_head_nvfp4's passes, hence the same values.
+// same operands as fold_head_nvfp4, hence the same values.
 template <int KW, bool LEAN>
 __device__ __forceinline__ float fold_head_max(const FoldOps<kNVFP4, KW, LEAN> &fo, const uint16_t *xT, int lane,
                                                const u32x4 (*rch)[4]) {
@@ -1173,36 +1172,30 @@ __device__ __forceinline__ float fold_head_max(const FoldOps<kNVFP4, KW, LEAN> &
 }
 
 // Separate checkpoints with an NVFP4 read checkpoint: fold the FP16
-// recurrence tile rch with the slot's second-level scale g.  The block scales
-// need each block's maximum, so the fold runs twice: pass 1 keeps the block
-// maxima, pass 2 (the same instructions on the same operands, hence the same
-// values) writes the new recurrence chunks over rch (stochastic rounding) and
-// the e2m1 codes into codes.
+// recurrence tile rch with the slot's second-level scale g, one row block at
+// a time (a block of 16 values lies inside one lane's quarter row, so its
+// scale needs only that row block's values): the new recurrence chunks
+// (stochastic rounding) over rch, the e2m1 codes into codes, the block
+// scales into sfw.
 template <int KW, bool LEAN>
 __device__ __forceinline__ void fold_head_nvfp4(const FoldOps<kNVFP4, KW, LEAN> &fo, const uint16_t *xT, int lane,
                                                 const KCache &c, int slot, int head, float g, u32x4 (*rch)[4],
                                                 u32x4 (*codes)[1], u32x2 &sfw) {
   const int m = lane & 15, q = lane >> 4;
-  float bm[8];
+  uint32_t sb[8];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     f32x4 acc[8];
     decode_quarter<kF16>(rch[rb], fo.D0, acc);
     fold_update<kNVFP4, KW>(fo, xT, rb, lane, acc);
     const f32x2 b2 = block_max2(acc);
-    bm[2 * rb] = b2[0];
-    bm[2 * rb + 1] = b2[1];
-  }
-  float y[8];
-  nvfp4_block_scales(bm, g, sfw, y);
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    f32x4 acc[8];
-    decode_quarter<kF16>(rch[rb], fo.D0, acc);
-    fold_update<kNVFP4, KW>(fo, xT, rb, lane, acc);
+    float y0, y1;
+    sb[2 * rb] = nvfp4_block_scale(b2[0], g, y0);
+    sb[2 * rb + 1] = nvfp4_block_scale(b2[1], g, y1);
     encode_quarter_sr(acc, c, slot, head, 16 * rb + m, q, rch[rb]);
-    codes[rb][0] = nvfp4_encode_quarter(acc, y[2 * rb], y[2 * rb + 1]);
+    codes[rb][0] = nvfp4_encode_quarter(acc, y0, y1);
   }
+  sfw = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24), sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
 }
 
 // Stores an NVFP4 tile with its block scales; the wave of head 0 also writes
@@ -1737,7 +1730,7 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // fused step (its validity rules; k = num_fold from the ring start at call
 // time); else those of a flush (slot_idx, num_fold, A).
 template <int KW, bool STEP>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void fold_max_kernel(KCache c, KStep s, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                      int htiles, int64_t ntiles) {
   __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
