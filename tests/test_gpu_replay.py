@@ -282,3 +282,66 @@ def test_pair_path_empty_entries(state_dtype):
     assert status == 0
     assert gh.rel_err(gh.to_f64(outs[0]), ref) <= gh.tol_for(state_dtype, "bf16")
     gh.check_cache_after_step(spec, cache, caches[0], ref_cache)
+
+
+# every replay path: (case, algo, fold) -> the kernel the step runs in
+BAD_RING_PATHS = [
+    ("tiny_f32", "monolith", False),        # head rows in 4 parts
+    ("bf16_dsplit2", "monolith", False),    # head rows in 2 parts
+    ("f16_persistent", "monolith", False),  # persistent kernel
+    ("f16_pair", "monolith", False),        # two heads per wave
+    ("f16_pair", "split", False),           # C.B precompute + persistent kernel
+    ("fp8_per_head", "monolith", False),    # one head per wave, nothing folded
+    ("fp8", "monolith", False),             # persistent kernel, fp8 tile
+    ("fp8_per_head", "auto", True),         # fused flush-in-step
+]
+
+
+@pytest.mark.parametrize("case,algo,fold", BAD_RING_PATHS)
+def test_bad_ring_start_each_path(case, algo, fold):
+    """An entry whose slot's ring_start lies outside [0, L) (one past the
+    end, one negative) is skipped on every path: its output rows are zero,
+    its rings, checkpoint and ring_start stay as they were, and the status
+    word says SSU_STATUS_BAD_RING; every other entry matches the oracle,
+    which skips such entries the same way."""
+    spec, cache, step, out_dtype = _setup(case, 4200 + len(case))
+    live = [b for b in range(step.batch) if 0 < step.slot_idx[b] < spec.num_slots]
+    bad = [live[0], live[len(live) // 2]]
+    cache.ring_start[int(step.slot_idx[bad[0]])] = spec.ring_len + 3
+    cache.ring_start[int(step.slot_idx[bad[1]])] = -1
+    print("case", case, algo, "fold" if fold else "", "bad entries", bad, flush=True)
+    k = None
+    if fold:
+        k = np.minimum(step.pnat, 1).astype(np.int32)
+    t = sd.upload_cache(cache, gh.DEV)
+    st = sd.upload_step(step, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    out = gh.out_tensor(step, spec, out_dtype)
+    if fold:
+        kt = torch.from_numpy(k).to(gh.DEV)
+        desc = ssu.make_step_desc(step.batch, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"],
+                                  st["B"], st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, out_dtype,
+                                  None, algo, num_fold=kt)
+        ssu.replay_step(dc, desc)
+    else:
+        gh.run_step(dc, st, step, out, out_dtype, algo)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == ssu.SSU_STATUS_BAD_RING
+    gpu = sd.download_cache(spec, t)
+    ref_cache = cache.copy()
+    ref, status = O.replay_step(ref_cache, step, num_fold=k) if fold else O.replay_step(ref_cache, step)
+    assert status == ssu.SSU_STATUS_BAD_RING
+    got = gh.to_f64(out)
+    cu = step.cu_seqlens if step.cu_seqlens is not None else np.arange(step.batch + 1) * step.T
+    for b in bad:
+        assert np.all(got[cu[b]:cu[b + 1]] == 0.0)
+        s = int(step.slot_idx[b])
+        for f in sd.CACHE_FIELDS:
+            assert np.array_equal(getattr(gpu, f)[s], getattr(cache, f)[s]), f
+        assert gpu.ring_start[s] == cache.ring_start[s]
+    if fold:
+        gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, out_dtype)
+    else:
+        assert gh.rel_err(got, ref) <= gh.tol_for(spec.state_dtype, out_dtype)
+        gh.check_cache_after_step(spec, cache, gpu, ref_cache)
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
