@@ -68,7 +68,7 @@ typedef enum ssu_dtype {
 
 typedef enum ssu_algo {
   SSU_ALGO_AUTO = 0,     /* monolith below the work-unit threshold, split above [FI item 1] */
-  SSU_ALGO_MONOLITH = 1, /* one kernel per step (a fused step adds a small ring-advance launch) */
+  SSU_ALGO_MONOLITH = 1, /* one kernel per step (a fused step adds a small ring-advance launch, an NVFP4 fold a maxima pass) */
   SSU_ALGO_SPLIT = 2     /* precompute (C.B per group) + persistent replay kernel */
 } ssu_algo;
 

@@ -17,11 +17,12 @@ namespace {
 thread_local char g_err[512] = "";
 
 // Default AUTO crossover in work units (batch * nheads).  On MI355X the
-// monolith is at least as fast as the split at every measured size (128 to
-// 65536 work units: the split trails by 26 % at one entry and by 1 % from
-// 32768 up), because forming C.B on MFMA inside each replay wave costs less
-// than the split's extra launch and scratch round trip.  AUTO therefore never
-// picks the split unless a caller lowers the threshold.
+// monolith is faster than the split at every measured size (128 to 65536
+// work units of fp16 with 128 heads: the split reaches 0.58-0.60 of the
+// monolith's throughput up to 512 units, 0.73-0.92 from 1024 to 8192, and
+// 0.89-0.90 from 16384 up), because forming C.B on MFMA inside each replay
+// wave costs less than the split's extra launch and scratch round trip.  AUTO
+// therefore never picks the split unless a caller lowers the threshold.
 std::atomic<int64_t> g_split_threshold{INT64_MAX};
 
 int fail(int code, const char *fmt, ...) {

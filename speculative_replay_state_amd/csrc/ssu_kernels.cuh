@@ -15,7 +15,8 @@
 // of the group.  The state stream dominates the bytes, so every kernel here
 // is built around reading each checkpoint exactly once with 16-byte loads.
 //
-// MI355X mapping (one wave64 per head):
+// MI355X mapping (a wave64 reads out one head, two heads, or a part of a
+// head's rows):
 //  * readout h0 . C_t is a [64 x 128] x [128 x T] product: 16 MFMA
 //    v_mfma_f32_16x16x32 (bf16 / f16 state; fp8 codes decoded to bf16
 //    exactly; fp32 state uses v_mfma_f32_16x16x4f32), the state tile feeding
@@ -25,10 +26,14 @@
 //    16 (24) mantissa bits while x (bf16) is exact;
 //  * the 32-long decay prefix is a wave scan; the dstate row maxima of the
 //    fp8 encoder are DPP reductions inside 16-lane rows.
-// The monolith computes C . B in LDS per workgroup; the split writes it to a
-// caller-provided fp32 scratch from a precompute kernel and a persistent
-// grid-stride kernel replays every (entry, head).  Both run the same device
-// functions in the same order, so their outputs are bit-identical.
+// The monolith forms C . B inside each replay wave, in the kernel its size
+// picks: each head's rows in parts (small batches), the persistent kernel,
+// two heads per wave (16-bit checkpoints from 2048 pairs) or one head per
+// wave (the fused flush-in-step, and some large plain steps); the split
+// writes C . B to a caller-provided fp32 scratch from a precompute kernel and
+// the persistent kernel replays every (entry, head).  All of them run the
+// same device functions on the same operands, so their outputs are
+// bit-identical.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -2437,13 +2442,19 @@ template <int ST, int OT>
 hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   if (s.batch <= 0) return hipSuccess;
   if (s.fold) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
-  // A plain step with enough (entry, head) pairs and a bf16 checkpoint, or an
-  // fp8 one without the recurrence checkpoint, runs in the one-head-per-wave
-  // kernel with nothing to fold (its readout is the same arithmetic, bit for
-  // bit).  Measured against the persistent kernel from 32768 pairs up: bf16
-  // 1-3 % faster (batch 256-1024 of 128 heads, varlen or not), fp8 10 %
-  // faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint 20 % and
-  // nvfp4 57 % slower (those forms of it hold more registers).
+  // Plain steps, by checkpoint type and size (every path is the same
+  // arithmetic per output value, bit for bit):
+  //  - 16-bit, from SSU_PAIR_MIN_UNITS (entry, head) pairs, groups of a
+  //    multiple of 8 heads, rings up to 16: two heads per wave;
+  //  - bf16 (other group sizes or rings) and fp8 without the recurrence
+  //    checkpoint, from kPerHeadPlainUnits pairs: the one-head-per-wave kernel
+  //    with nothing to fold.  Measured against the persistent kernel from
+  //    32768 pairs up: bf16 1-3 % faster (batch 256-1024 of 128 heads), fp8
+  //    10 % faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint
+  //    20 % and nvfp4 57 % slower (those forms of it hold more registers);
+  //  - 16- and 32-bit, not gated, up to SSU_DSPLIT_MAX_UNITS pairs: each
+  //    head's rows in parts;
+  //  - the rest: the persistent kernel.
   if constexpr (ST == kBF16 || ST == kF16) {
     // (rings of up to 16 entries: with a 32-deep window the two register sets spill)
     if ((int64_t)s.batch * c.H >= SSU_PAIR_MIN_UNITS && c.hpg % kPairHeads == 0 && c.L <= 16)
