@@ -60,8 +60,9 @@ constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
 // bound (each wave streams its tile only between compute phases), so it runs
 // as many waves as fit: the fp8 step with bf16 output folds in 96 registers
 // (5 waves, no spills); the other forms need more and get 3, 2 or 1.  The
-// NVFP4 step (not gated, rings up to 16) runs 3 waves although 12 registers
-// spill: 344.5 us per step against 351.2 at 2 waves (182 registers, none
+// NVFP4 step (not gated, rings up to 16) runs 3 waves although registers
+// spill (12 before its C.B shared the readout's C, 2 since): 344.5 us per
+// step with 12 spilled against 351.2 at 2 waves (182 registers, none
 // spilled), batch 256 of 128 heads.
 #define SSU_FUSED_WPE(ST, OT, KW, HAS_Z, SEP) \
   (ST == kF32 ? 1                                                                 \
@@ -442,7 +443,7 @@ __device__ __forceinline__ float scan_win(float v, int lane) {
 // n = 32 q + 8 u + e, so that a caller holding those can pass them as the A
 // operand instead of loading C again (own_c = false).  The k order changes the
 // MFMA's summation grouping, so every path of one state type uses the same
-// order (cb_qorder): the fp8 paths q order, the others u order.
+// order (cb_qorder): the fp8 and nvfp4 paths q order, the others u order.
 template <int KW>
 struct CbLoads {
   bf16x8 ca[4];
@@ -452,8 +453,10 @@ struct CbLoads {
 // Element offset, in a row of 128, of k step u's chunk for lane quarter q.
 __device__ __forceinline__ int cb_k(bool qorder, int u, int q) { return qorder ? 32 * q + 8 * u : 32 * u + 8 * q; }
 
-// The C.B k order of a state type (the fp8 fused step shares the readout's C).
-constexpr bool cb_qorder(int ST) { return ST == kFP8; }
+// The C.B k order of a state type (the fp8 and nvfp4 fused steps share the
+// readout's C: for nvfp4 that takes the fused kernel's spill from 12 registers
+// to 2 at 3 waves per SIMD).
+constexpr bool cb_qorder(int ST) { return ST == kFP8 || ST == kNVFP4; }
 
 template <int KW>
 __device__ __forceinline__ void load_cb(const KCache &c, const KStep &s, const Entry &e, int g, int lane,
