@@ -37,6 +37,11 @@ def _need_gpu():
 FULL = {
     "tiny_b2": dict(nheads=8, ngroups=1, state="f32", batch=2, slots=4, T=1, pnat_max=8, out="f32"),
     "mtp_b64": dict(nheads=64, ngroups=8, state="bf16", batch=64, slots=128, T=4, pnat_max=4, out="bf16"),
+    # production sizes at the small end: 4 (rows of each head in parts), 8 (persistent kernel), 32 (two heads
+    # per wave)
+    "prod_b4": dict(nheads=128, ngroups=8, state="f16", batch=4, slots=9, T=8, pnat_max=8, out="bf16"),
+    "prod_b8": dict(nheads=128, ngroups=8, state="f16", batch=8, slots=17, T=8, pnat_max=8, out="bf16"),
+    "prod_b32": dict(nheads=128, ngroups=8, state="f16", batch=32, slots=65, T=8, pnat_max=8, out="bf16"),
     "prod_b256": dict(nheads=128, ngroups=8, state="f16", batch=256, slots=513, T=8, pnat_max=8, out="bf16"),
     "prod_b512": dict(nheads=128, ngroups=8, state="f16", batch=512, slots=1025, T=8, pnat_max=8, out="bf16"),
     "fp8_b256": dict(nheads=128, ngroups=8, state="fp8", batch=256, slots=513, T=4, pnat_max=0, out="bf16",
@@ -49,7 +54,8 @@ FULL = {
     "large_b1024": dict(nheads=128, ngroups=8, state="bf16", batch=1024, slots=2048, T=8, pnat_max=8,
                         out="bf16", varlen=True, pad=256),
 }
-RUNS = [("tiny_b2", "monolith"), ("mtp_b64", "monolith"), ("mtp_b64", "split"), ("prod_b256", "monolith"),
+RUNS = [("tiny_b2", "monolith"), ("mtp_b64", "monolith"), ("mtp_b64", "split"), ("prod_b4", "monolith"),
+        ("prod_b4", "split"), ("prod_b8", "monolith"), ("prod_b32", "monolith"), ("prod_b256", "monolith"),
         ("prod_b256", "split"), ("prod_b512", "monolith"), ("fp8_b256", "fused"), ("fp8_b256", "separate"),
         ("fp8sep_b256", "fused"), ("nvfp4_b256", "fused"), ("nvfp4_b256", "separate"),
         ("large_b1024", "monolith")]
