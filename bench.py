@@ -568,15 +568,19 @@ def hbm_streams(dev, nbytes=2 ** 31, reps=5):
     """GB/s of plain PyTorch streams over 2 GiB buffers on this GPU: a device
     copy (half reads, half writes), an in-place read-modify-write of one
     buffer (x.mul_(1.0): every byte read and written back, as a checkpoint
-    fold does), a fill (writes only) and a sum (reads only).  Best of `reps`."""
+    fold does), a fill (writes only) and row sums over rows of 2048 values
+    (reads, with 1/2048 as many bytes written; a sum of the whole buffer to
+    one value runs as a multi-pass reduction and reads far slower).  Best of
+    `reps`."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    acc = torch.empty((), dtype=torch.float32, device=dev)
+    rows = src.view(-1, 2048)
+    acc = torch.empty(rows.shape[0], dtype=torch.float32, device=dev)
     ops = {
         "copy_GBps": (lambda: dst.copy_(src), 2 * nbytes),
         "rmw_GBps": (lambda: src.mul_(1.0), 2 * nbytes),
         "write_GBps": (lambda: dst.fill_(2.0), nbytes),
-        "read_GBps": (lambda: torch.sum(src, dim=0, out=acc), nbytes),
+        "read_GBps": (lambda: torch.sum(rows, dim=1, out=acc), nbytes + 4 * rows.shape[0]),
     }
     out = {"bytes_per_buffer": nbytes}
     for name, (fn, moved) in ops.items():
@@ -590,7 +594,7 @@ def hbm_streams(dev, nbytes=2 ** 31, reps=5):
             torch.cuda.synchronize()
             best = min(best, a.elapsed_time(b))
         out[name] = moved / (best * 1e6)
-    del src, dst, acc
+    del src, dst, rows, acc
     torch.cuda.empty_cache()
     return out
 
