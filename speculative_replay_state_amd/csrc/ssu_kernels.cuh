@@ -2455,8 +2455,10 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   //    32768 pairs up: bf16 1-3 % faster (batch 256-1024 of 128 heads), fp8
   //    10 % faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint
   //    20 % and nvfp4 57 % slower (those forms of it hold more registers);
-  //  - 16- and 32-bit, not gated, up to SSU_DSPLIT_MAX_UNITS pairs: each
-  //    head's rows in parts;
+  //  - not gated: 16-bit up to SSU_DSPLIT_MAX_UNITS pairs and 32-bit at
+  //    any size, each head's rows in parts (fp32 tiny at batch 128 / 256 /
+  //    512 of 8 heads: 12.31 / 19.39 / 35.11 us per step against 16.06 /
+  //    26.02 / 40.57 on the persistent kernel);
   //  - the rest: the persistent kernel.
   if constexpr (ST == kBF16 || ST == kF16) {
     // (rings of up to 16 entries: with a 32-deep window the two register sets spill)
@@ -2469,7 +2471,8 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   }
   if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {
     const int64_t units = (int64_t)s.batch * c.H;
-    if (!s.z && units <= SSU_DSPLIT_MAX_UNITS) return dsplit_t<ST, OT>(c, s, units <= SSU_DSPLIT4_MAX_UNITS ? 4 : 2, st);
+    if (!s.z && (ST == kF32 || units <= SSU_DSPLIT_MAX_UNITS))
+      return dsplit_t<ST, OT>(c, s, units <= SSU_DSPLIT4_MAX_UNITS ? 4 : 2, st);
   }
   return s.z ? replay_z<ST, OT, false, true>(c, s, st) : replay_z<ST, OT, false, false>(c, s, st);
 }

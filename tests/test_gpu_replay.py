@@ -61,12 +61,14 @@ CASES = {
                      pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "bf16_pair_hpg8": dict(spec=dict(num_slots=600, nheads=64, ngroups=8, state_dtype="bf16"), batch=512, T=4,
                            pnat_max=4, out="bf16", n_padding=2),
-    # 513 to 2047 pairs of a 16- or 32-bit checkpoint: the persistent kernel
+    # 513 to 2047 pairs of a 16-bit checkpoint: the persistent kernel
     "f16_persistent": dict(spec=dict(num_slots=20, nheads=128, ngroups=8, state_dtype="f16"), batch=12, T=8,
                            pnat_max=8, out="bf16", varlen=True, n_padding=1),
-    "f32_persistent": dict(spec=dict(num_slots=120, nheads=8, ngroups=2, state_dtype="f32"), batch=100, T=3,
-                           pnat_max=10, out="f32", n_padding=4),
-    # up to 512 pairs: each head's rows split over waves, 2 parts from 257 pairs, 4 parts up to 256
+    # 800 pairs of fp32: each head's rows in 2 parts (fp32 plain steps split at any size; the split
+    # algorithm runs the persistent kernel)
+    "f32_mid": dict(spec=dict(num_slots=120, nheads=8, ngroups=2, state_dtype="f32"), batch=100, T=3,
+                    pnat_max=10, out="f32", n_padding=4),
+    # 16-bit up to 512 pairs: each head's rows split over waves, 2 parts from 257 pairs, 4 parts up to 256
     # (tiny_f32, bf16_f32out, f32_T16_L32 and f16_hpg1 above run in 4 parts)
     "bf16_dsplit2": dict(spec=dict(num_slots=8, nheads=128, ngroups=8, state_dtype="bf16"), batch=4, T=6,
                          pnat_max=8, out="bf16", varlen=True, n_padding=1),
