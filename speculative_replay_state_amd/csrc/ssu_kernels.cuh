@@ -2083,11 +2083,13 @@ void pair_kernel(KCache c, KStep s, int ptiles, int64_t ntiles) {
 }
 
 // ---------------------------------------------------------------------------
-// D-SPLIT: plain steps of few (entry, head) pairs (small batches).  The
-// head's 64 state rows are cut into DS parts of 64 / DS rows and each part is
-// read out by a wave of its own, one wave per (entry, head, part), so a small
-// batch still spreads over the chip and each wave's serial work (its share of
-// the tile loads, the readout MFMAs and the output stores) shrinks DS-fold.
+// D-SPLIT: plain steps of few (entry, head) pairs (small batches), and fp32
+// plain steps of any size (a 32 KiB tile is too much for one wave's register
+// budget).  The head's 64 state rows are cut into DS parts of 64 / DS rows
+// and each part is read out by a wave of its own, one wave per (entry, head,
+// part), so a small batch still spreads over the chip and each wave's serial
+// work (its share of the tile loads, the readout MFMAs and the output stores)
+// shrinks DS-fold.
 // Every part forms the group's C.B and the head's decay prefix itself (a few
 // hundred flops) and loads the whole x window (the other parts' rows come
 // from L2); part 0 appends the new tokens' x and dt' to the rings, part 0 of
@@ -2400,8 +2402,9 @@ hipError_t pair_z(const KCache &c, const KStep &s, hipStream_t st) {
   }
 }
 
-// (entry, head) pairs up to which plain steps of 16- and 32-bit checkpoints
-// split each head's rows over 2 waves, and over 4.  Measured (graph-replayed
+// (entry, head) pairs up to which plain 16-bit steps split each head's rows
+// over 2 waves, and over 4 (fp32 plain steps split at every size, in 4 parts
+// up to SSU_DSPLIT4_MAX_UNITS pairs, else in 2).  Measured (graph-replayed
 // steps, one MI355X): fp16 prod, batch 1 (128 pairs): 7.25 us per step on the
 // persistent kernel, 5.65 in 2 parts, 5.49 in 4; batch 4 (512): 7.90, 6.17,
 // 7.55; batch 16 (2048): 12.85, 13.79, 17.64; fp32 tiny (16 pairs): 9.71,
