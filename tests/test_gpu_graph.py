@@ -34,15 +34,18 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-# (num_slots, nheads, ngroups, batch): the second is large enough (256 x 128
-# pairs) for the plain fp8 monolith step to run one head per wave
-SHAPES = {"small": (40, 32, 4, 12), "per_head": (300, 128, 8, 256)}
+# (state dtype, num_slots, nheads, ngroups, batch), by the kernel the plain
+# monolith step runs in: fp8 persistent (12 x 32 pairs) and one head per wave
+# (256 x 128); fp16 two heads per wave (256 x 128); bf16 head rows in 4 parts
+# (9 x 16)
+SHAPES = {"small": ("fp8", 40, 32, 4, 12), "per_head": ("fp8", 300, 128, 8, 256),
+          "f16_pair": ("f16", 300, 128, 8, 256), "bf16_parts": ("bf16", 24, 16, 2, 9)}
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
 def test_graph_replays_match_eager(shape):
-    num_slots, H, G, batch = SHAPES[shape]
-    spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype="fp8")
+    state_dtype, num_slots, H, G, batch = SHAPES[shape]
+    spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype=state_dtype)
     cache = synth.make_cache(spec, 7100 + H)
     step = synth.make_step(spec, batch, 4, 7101 + H, 8, n_padding=2)
     rng = np.random.default_rng(7102)
@@ -101,11 +104,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def first_calls_in_capture():
     """Run in a fresh process: capture the library's first calls (a plain
-    monolith step on the persistent kernel, a split step, a flush), replay the
-    graph three times and compare with the same calls run eagerly on a copy."""
+    monolith step on the persistent kernel (20 x 32 = 640 pairs), a split
+    step, a flush), replay the graph three times and compare with the same
+    calls run eagerly on a copy."""
     spec = synth.CacheSpec(num_slots=40, nheads=32, ngroups=4, state_dtype="f16")
     cache = synth.make_cache(spec, 7300)
-    step = synth.make_step(spec, 12, 4, 7301, 8, n_padding=2)
+    step = synth.make_step(spec, 20, 4, 7301, 8, n_padding=2)
     k2 = np.minimum(step.pnat, 2).astype(np.int32)
     st = sd.upload_step(step, gh.DEV)
     k2t = torch.from_numpy(k2).to(gh.DEV)
