@@ -232,9 +232,12 @@ size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seq
  * each [nheads][64][128] packed; states_batch_stride == 0 broadcasts entry 0
  * to every slot.  For each slot_idx[j] in [1, num_slots): encode the state
  * (fp32 stored, bf16/fp16 round to nearest even, fp8 per row:
- * scale = max|h| / 448 (1 if zero), code = nearest e4m3fn of h / scale),
- * zero its x/B/dt rings and set ring_start to 0.  Other ids are ignored.
- * slot ids must be unique.  n == 0 is a no-op.
+ * scale = max|h| / 448 (1 if zero), code = nearest e4m3fn of h / scale;
+ * nvfp4 as described at ssu_cache, g from the slot's largest |value|),
+ * write recur_state when present (fp16 with the stochastic rounding above,
+ * keyed by sr_seed; sr_seed is unused otherwise), zero its x/B/dt rings and
+ * set ring_start to 0.  Other ids are ignored.  slot ids must be unique.
+ * n == 0 is a no-op.
  */
 int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
                    const int32_t *slot_idx, int32_t n, uint64_t sr_seed, hipStream_t stream);
