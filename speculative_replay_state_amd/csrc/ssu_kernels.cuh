@@ -2097,16 +2097,20 @@ void pair_kernel(KCache c, KStep s, int ptiles, int64_t ntiles) {
 // arithmetic as on the other paths: the outputs are bit-identical.
 // ---------------------------------------------------------------------------
 
-template <int ST, int OT, int KW, int DS>
-__global__ __launch_bounds__(kHeadWaves * 64) void dsplit_kernel(KCache c, KStep s, int64_t nwaves) {
+// WPG waves per workgroup: 1 for the smallest grids, so that their few waves
+// spread over every CU (fp32 tiny, 64 waves: 4.82 us per step against 5.72
+// with 4 waves per workgroup; fp16 batch 1, 512 waves: 5.11 against 5.54),
+// else kHeadWaves (fp16 batch 4, 1024 waves: 6.15 against 6.25 with 1).
+template <int ST, int OT, int KW, int DS, int WPG>
+__global__ __launch_bounds__(WPG * 64) void dsplit_kernel(KCache c, KStep s, int64_t nwaves) {
   static_assert(ST == kF32 || ST == kBF16 || ST == kF16, "part tiles: 16- and 32-bit checkpoints");
   static_assert(DS == 2 || DS == 4, "parts of 2 or 1 row blocks");
   constexpr int NRB = 4 / DS;
   constexpr int kXTWords = kHeadDim * Win<KW>::kXS / 2, kCbWords = kMaxTokens * kCbLds;
   constexpr int kWords = kXTWords + kCbWords > kOutTile ? kXTWords + kCbWords : kOutTile;
-  __shared__ __align__(16) uint32_t lds_all[kHeadWaves][kWords];
+  __shared__ __align__(16) uint32_t lds_all[WPG][kWords];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t gw = xcd_tile(blockIdx.x, gridDim.x) * kHeadWaves + wave;
+  const int64_t gw = xcd_tile(blockIdx.x, gridDim.x) * WPG + wave;
   if (gw >= nwaves) return;
   const int part = (int)(gw % DS);
   const int64_t unit = gw / DS;
@@ -2417,21 +2421,31 @@ hipError_t pair_z(const KCache &c, const KStep &s, hipStream_t st) {
 #define SSU_DSPLIT4_MAX_UNITS 256
 #endif
 
+constexpr int64_t kDsplitOneWaveMax = 512;  // waves up to which the split runs one wave per workgroup
+
+template <int ST, int OT, int KW, int DS>
+void dsplit_launch(const KCache &c, const KStep &s, int64_t nwaves, hipStream_t st) {
+  if (nwaves <= kDsplitOneWaveMax)
+    dsplit_kernel<ST, OT, KW, DS, 1><<<dim3(xcd_grid(nwaves)), dim3(64), 0, st>>>(c, s, nwaves);
+  else
+    dsplit_kernel<ST, OT, KW, DS, kHeadWaves><<<dim3(xcd_grid((nwaves + kHeadWaves - 1) / kHeadWaves)),
+                                                dim3(kHeadWaves * 64), 0, st>>>(c, s, nwaves);
+}
+
 template <int ST, int OT>
 hipError_t dsplit_t(const KCache &c, const KStep &s, int ds, hipStream_t st) {
   if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {
     const int64_t nwaves = (int64_t)s.batch * c.H * ds;
-    const dim3 grid(xcd_grid((nwaves + kHeadWaves - 1) / kHeadWaves)), block(kHeadWaves * 64);
     if (ds == 4) {
       if (c.L <= 16)
-        dsplit_kernel<ST, OT, 16, 4><<<grid, block, 0, st>>>(c, s, nwaves);
+        dsplit_launch<ST, OT, 16, 4>(c, s, nwaves, st);
       else
-        dsplit_kernel<ST, OT, 32, 4><<<grid, block, 0, st>>>(c, s, nwaves);
+        dsplit_launch<ST, OT, 32, 4>(c, s, nwaves, st);
     } else {
       if (c.L <= 16)
-        dsplit_kernel<ST, OT, 16, 2><<<grid, block, 0, st>>>(c, s, nwaves);
+        dsplit_launch<ST, OT, 16, 2>(c, s, nwaves, st);
       else
-        dsplit_kernel<ST, OT, 32, 2><<<grid, block, 0, st>>>(c, s, nwaves);
+        dsplit_launch<ST, OT, 32, 2>(c, s, nwaves, st);
     }
     return hipGetLastError();
   } else {
