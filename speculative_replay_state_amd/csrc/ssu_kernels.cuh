@@ -2485,8 +2485,11 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   //  - 16-bit, from SSU_PAIR_MIN_UNITS (entry, head) pairs, groups of a
   //    multiple of 8 heads, rings up to 16: two heads per wave;
   //  - bf16 (other group sizes or rings) and fp8 without the recurrence
-  //    checkpoint, from kPerHeadPlainUnits pairs: the one-head-per-wave kernel
-  //    with nothing to fold.  Measured against the persistent kernel from
+  //    checkpoint, from kPerHeadPlainUnits pairs, and that fp8 step also up
+  //    to kFusedOneWaveMax pairs (one wave per workgroup): the one-head-per-
+  //    wave kernel with nothing to fold (fp8, 128 heads, batch 1 / 2 / 4:
+  //    9.24 / 9.11 / 9.79 us per call against 10.62 / 10.34 / 10.24 on the
+  //    persistent kernel).  Measured against the persistent kernel from
   //    32768 pairs up: bf16 1-3 % faster (batch 256-1024 of 128 heads), fp8
   //    10 % faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint
   //    20 % and nvfp4 57 % slower (those forms of it hold more registers);
@@ -2501,7 +2504,8 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
       return s.z ? pair_z<ST, OT, true>(c, s, st) : pair_z<ST, OT, false>(c, s, st);
   }
   if constexpr (ST == kBF16 || ST == kFP8) {
-    if ((ST == kBF16 || !c.recur) && (int64_t)s.batch * c.H >= kPerHeadPlainUnits)
+    const int64_t units = (int64_t)s.batch * c.H;
+    if ((ST == kBF16 || !c.recur) && (units >= kPerHeadPlainUnits || (ST == kFP8 && units <= kFusedOneWaveMax)))
       return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
   }
   if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {

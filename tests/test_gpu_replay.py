@@ -55,6 +55,9 @@ CASES = {
                           pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "fp8_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="fp8"), batch=256, T=4,
                          pnat_max=12, out="bf16", n_padding=2),
+    # up to 512 fp8 pairs: one head per wave, one wave per workgroup
+    "fp8_small": dict(spec=dict(num_slots=10, nheads=64, ngroups=8, state_dtype="fp8"), batch=6, T=4,
+                      pnat_max=12, out="bf16", varlen=True, n_padding=1),
     # 16-bit checkpoints from 2048 pairs (groups of a multiple of 8 heads, rings up to 16): two heads per
     # wave (groups of 16 and of 8); prod_f16, mtp_bf16 and large_bf16_varlen above run there too
     "f16_pair": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="f16"), batch=256, T=8,
