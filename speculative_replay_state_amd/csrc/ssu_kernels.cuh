@@ -69,7 +69,7 @@ constexpr int kWaves = 4;        // waves per workgroup of the replay kernels
    : ((KW == 32 || (SEP && !(ST == kNVFP4 && !HAS_Z))) ? 2                        \
       : ((ST == kFP8 && OT == kOutBF16 && !HAS_Z) ? 5 : 3)))
 #endif
-constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels (1, 2, 4 measure alike)
+constexpr int kHeadWaves = 4;    // waves per workgroup of the one-head-per-wave kernels on large grids (1, 2, 4 measure alike there)
 // (entry, head) pairs from which a plain bf16 or fp8 step runs one head per wave
 constexpr int64_t kPerHeadPlainUnits = 32768;
 constexpr int kXS = 40;          // LDS row stride (bf16) of the transposed x window
@@ -1634,20 +1634,27 @@ __global__ __launch_bounds__(kWaves * 64) void precompute_kernel(KCache c, KStep
 __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t ngrid) { return (id & 7) * (ngrid >> 3) + (id >> 3); }
 inline unsigned xcd_grid(int64_t ntiles) { return (unsigned)((ntiles + 7) / 8 * 8); }
 
-template <int ST, int KW, bool SEP>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
-void flush_kernel(KCache c, const int32_t *slot_idx,
-                                                            const int32_t *num_fold, const float *A,
-                                                            int htiles, int64_t ntiles) {
+// (entry, head) pairs up to which the one-head-per-wave kernels (flush, the
+// NVFP4 maxima pass, the fused step) run one wave per workgroup, so that a
+// small grid spreads over every CU instead of filling a quarter of them: fp8
+// fused step, batch 1 of 128 heads, 9.84 us per step against 11.14 with 4
+// waves per workgroup; batch 4, 10.97 against 11.40; from batch 16 up alike.
+constexpr int64_t kFusedOneWaveMax = 512;
+
+// WPG waves (heads) per workgroup: 1 up to kFusedOneWaveMax pairs, else 4.
+template <int ST, int KW, bool SEP, int WPG>
+__global__ __launch_bounds__(WPG * 64) __attribute__((amdgpu_waves_per_eu(ST == kF32 ? 1 : ((KW == 32 || SEP) ? 2 : 3))))
+void flush_kernel(KCache c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int htiles,
+                  int64_t ntiles) {
   using WC = Win<KW>;
   constexpr int kNLD = st_chunks(ST);
   static_assert(ST != kNVFP4 || SEP, "an nvfp4 read checkpoint needs the recurrence checkpoint");
-  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * WC::kXS];
+  __shared__ uint16_t xT_all[WPG][kHeadDim * WC::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= ntiles) return;
   const int j = (int)(tile / htiles);
-  const int h = (int)(tile - (int64_t)j * htiles) * kHeadWaves + wave;
+  const int h = (int)(tile - (int64_t)j * htiles) * WPG + wave;
   if (h >= c.H) return;
   const int slot = slot_idx[j], k = num_fold[j], L = c.L;
   if (slot <= 0 || slot >= c.num_slots) return;
@@ -1737,16 +1744,16 @@ void flush_kernel(KCache c, const int32_t *slot_idx,
 // loads and fold instructions as the encode pass.  STEP: the entries of a
 // fused step (its validity rules; k = num_fold from the ring start at call
 // time); else those of a flush (slot_idx, num_fold, A).
-template <int KW, bool STEP>
-__global__ __launch_bounds__(kHeadWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+template <int KW, bool STEP, int WPG>
+__global__ __launch_bounds__(WPG * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void fold_max_kernel(KCache c, KStep s, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                      int htiles, int64_t ntiles) {
-  __shared__ uint16_t xT_all[kHeadWaves][kHeadDim * Win<KW>::kXS];
+  __shared__ uint16_t xT_all[WPG][kHeadDim * Win<KW>::kXS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   if (tile >= ntiles) return;
   const int j = (int)(tile / htiles);
-  const int h = (int)(tile - (int64_t)j * htiles) * kHeadWaves + wave;
+  const int h = (int)(tile - (int64_t)j * htiles) * WPG + wave;
   if (h >= c.H) return;
   int slot, k, r;
   float Ah;
@@ -2356,38 +2363,30 @@ __global__ void step_ring_advance_kernel(KCache c, KStep s) {
   if (e.mode == 2 && e.k > 0) c.ring_start[e.slot] = e.r;
 }
 
-// The fused kernel at WPG heads per workgroup.
+// The fused kernel at WPG heads per workgroup (with an NVFP4 fold, the maxima
+// pass first: the encode needs the slot's scale).
 template <int ST, int OT, bool HAS_Z, bool SEP, int WPG>
 void fused_launch(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + WPG - 1) / WPG;
   const int64_t ntiles = (int64_t)s.batch * htiles;
+  if constexpr (ST == kNVFP4) {
+    if (s.fold) {
+      if (c.L <= 16)
+        fold_max_kernel<16, true, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, nullptr, nullptr,
+                                                                                         nullptr, htiles, ntiles);
+      else
+        fold_max_kernel<32, true, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, nullptr, nullptr,
+                                                                                         nullptr, htiles, ntiles);
+    }
+  }
   if (c.L <= 16)
     fused_kernel<ST, OT, 16, HAS_Z, SEP, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, htiles, ntiles);
   else
     fused_kernel<ST, OT, 32, HAS_Z, SEP, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, htiles, ntiles);
 }
 
-// (entry, head) pairs up to which the fused kernel runs one wave per
-// workgroup, so that a small grid spreads over every CU: fp8 fused step,
-// batch 1 of 128 heads, 9.84 us per step against 11.14 with 4 waves per
-// workgroup; batch 4, 10.97 against 11.40; from batch 16 up alike.
-constexpr int64_t kFusedOneWaveMax = 512;
-
 template <int ST, int OT, bool HAS_Z, bool SEP>
 hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
-  const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
-  const int64_t ntiles = (int64_t)s.batch * htiles;
-  const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
-  if constexpr (ST == kNVFP4) {  // a step that folds: the maxima pass first (the encode needs the slot's scale)
-    if (s.fold) {
-      if (c.L <= 16)
-        fold_max_kernel<16, true><<<grid, block, 0, st>>>(c, s, nullptr, nullptr, nullptr, htiles, ntiles);
-      else
-        fold_max_kernel<32, true><<<grid, block, 0, st>>>(c, s, nullptr, nullptr, nullptr, htiles, ntiles);
-      hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
-  }
   if ((int64_t)s.batch * c.H <= kFusedOneWaveMax)
     fused_launch<ST, OT, HAS_Z, SEP, 1>(c, s, st);
   else
@@ -2485,11 +2484,13 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   //  - 16-bit, from SSU_PAIR_MIN_UNITS (entry, head) pairs, groups of a
   //    multiple of 8 heads, rings up to 16: two heads per wave;
   //  - bf16 (other group sizes or rings) and fp8 without the recurrence
-  //    checkpoint, from kPerHeadPlainUnits pairs, and that fp8 step also up
-  //    to kFusedOneWaveMax pairs (one wave per workgroup): the one-head-per-
-  //    wave kernel with nothing to fold (fp8, 128 heads, batch 1 / 2 / 4:
-  //    9.24 / 9.11 / 9.79 us per call against 10.62 / 10.34 / 10.24 on the
-  //    persistent kernel).  Measured against the persistent kernel from
+  //    checkpoint from kPerHeadPlainUnits pairs, and fp8 and nvfp4 (with or
+  //    without the recurrence checkpoint) up to kFusedOneWaveMax pairs (one
+  //    wave per workgroup): the one-head-per-wave kernel with nothing to
+  //    fold.  Small steps, 128 heads: fp8 batch 1 / 2 / 4 9.24 / 9.11 /
+  //    9.79 us per call against 10.62 / 10.34 / 10.24 on the persistent
+  //    kernel; fp8 with the recurrence checkpoint batch 1 8.75 against 10.09;
+  //    nvfp4 batch 1 9.53 against 10.33.  Measured against the persistent kernel from
   //    32768 pairs up: bf16 1-3 % faster (batch 256-1024 of 128 heads), fp8
   //    10 % faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint
   //    20 % and nvfp4 57 % slower (those forms of it hold more registers);
@@ -2503,10 +2504,11 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
     if ((int64_t)s.batch * c.H >= SSU_PAIR_MIN_UNITS && c.hpg % kPairHeads == 0 && c.L <= 16)
       return s.z ? pair_z<ST, OT, true>(c, s, st) : pair_z<ST, OT, false>(c, s, st);
   }
-  if constexpr (ST == kBF16 || ST == kFP8) {
+  if constexpr (ST == kBF16 || ST == kFP8 || ST == kNVFP4) {
     const int64_t units = (int64_t)s.batch * c.H;
-    if ((ST == kBF16 || !c.recur) && (units >= kPerHeadPlainUnits || (ST == kFP8 && units <= kFusedOneWaveMax)))
-      return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
+    const bool big = ST != kNVFP4 && (ST == kBF16 || !c.recur) && units >= kPerHeadPlainUnits;
+    const bool small = (ST == kFP8 || ST == kNVFP4) && units <= kFusedOneWaveMax;
+    if (big || small) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
   }
   if constexpr (ST == kF32 || ST == kBF16 || ST == kF16) {
     const int64_t units = (int64_t)s.batch * c.H;
@@ -2522,38 +2524,47 @@ hipError_t split_t(const KCache &c, const KStep &s, hipStream_t st) {
   return s.z ? replay_z<ST, OT, true, true>(c, s, st) : replay_z<ST, OT, true, false>(c, s, st);
 }
 
-template <int ST>
-hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
-                   int n, hipStream_t st) {
-  const int htiles = (c.H + kHeadWaves - 1) / kHeadWaves;
+// The flush's kernels at WPG heads per workgroup (an NVFP4 flush: the maxima
+// pass first, the encode needs the slot's scale).
+template <int ST, int WPG>
+void flush_launch(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int n,
+                  hipStream_t st) {
+  const int htiles = (c.H + WPG - 1) / WPG;
   const int64_t ntiles = (int64_t)n * htiles;
-  const dim3 grid(xcd_grid(ntiles)), block(kHeadWaves * 64);
+  const dim3 grid(xcd_grid(ntiles)), block(WPG * 64);
   bool sep = ST == kNVFP4;
   if constexpr (ST == kFP8) sep = c.recur != nullptr;
-  if constexpr (ST == kNVFP4) {  // the maxima pass first: the encode needs the slot's scale
+  if constexpr (ST == kNVFP4) {
     const KStep none{};
     if (c.L <= 16)
-      fold_max_kernel<16, false><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
+      fold_max_kernel<16, false, WPG><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
     else
-      fold_max_kernel<32, false><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+      fold_max_kernel<32, false, WPG><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
   }
   if (sep) {
     if constexpr (ST == kFP8 || ST == kNVFP4) {
       if (c.L <= 16)
-        flush_kernel<ST, 16, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
+        flush_kernel<ST, 16, true, WPG><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
       else
-        flush_kernel<ST, 32, true><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
+        flush_kernel<ST, 32, true, WPG><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
     }
   } else {
     if constexpr (ST != kNVFP4) {
       if (c.L <= 16)
-        flush_kernel<ST, 16, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
+        flush_kernel<ST, 16, false, WPG><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
       else
-        flush_kernel<ST, 32, false><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
+        flush_kernel<ST, 32, false, WPG><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
     }
   }
+}
+
+template <int ST>
+hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
+                   int n, hipStream_t st) {
+  if ((int64_t)n * c.H <= kFusedOneWaveMax)
+    flush_launch<ST, 1>(c, slot_idx, num_fold, A, n, st);
+  else
+    flush_launch<ST, kHeadWaves>(c, slot_idx, num_fold, A, n, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   ring_advance_kernel<ST><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);
