@@ -28,7 +28,7 @@
 //    fp8 encoder are DPP reductions inside 16-lane rows.
 // The monolith forms C . B inside each replay wave, in the kernel its size
 // picks: each head's rows in parts (small batches), the persistent kernel,
-// two heads per wave (16-bit checkpoints from 2048 pairs) or one head per
+// two heads per wave (16-bit checkpoints from 1536 pairs) or one head per
 // wave (the fused flush-in-step, and some large plain steps); the split
 // writes C . B to a caller-provided fp32 scratch from a precompute kernel and
 // the persistent kernel replays every (entry, head).  All of them run the
@@ -1981,9 +1981,11 @@ void fused_kernel(KCache c, KStep s, int htiles, int64_t ntiles) {
 #ifndef SSU_PAIR_MIN_UNITS
 // (entry, head) pairs from which plain 16-bit steps run two heads per wave.
 // Measured against the persistent kernel (fp16 prod, graph-replayed steps):
-// batch 16 (2048 pairs) 12.47 against 12.78 us, 32: 18.95 / 19.18, 64: 33.16 /
-// 32.84, 128: 61.00 / 64.71, 192: 89.82 / 96.44; bf16 mtp (4096) 18.35 / 18.31.
-#define SSU_PAIR_MIN_UNITS 2048
+// batch 5 (640 pairs) 8.80 against 8.38 us, 8 (1024): 9.66 / 9.50, 12 (1536):
+// 11.05 / 11.96, 16: 12.47 / 12.78, 32: 18.95 / 19.18, 64: 33.16 / 32.84, 128:
+// 61.00 / 64.71, 192: 89.82 / 96.44; bf16 mtp (64 heads) batch 12 (768):
+// 8.56 / 8.02, 24 (1536): 10.52 / 11.37, 64: 18.35 / 18.31.
+#define SSU_PAIR_MIN_UNITS 1536
 #endif
 constexpr int kPairHeads = 2 * kHeadWaves;  // heads per workgroup
 
@@ -2429,10 +2431,12 @@ hipError_t pair_z(const KCache &c, const KStep &s, hipStream_t st) {
 // steps, one MI355X): fp16 prod, batch 1 (128 pairs): 7.25 us per step on the
 // persistent kernel, 5.65 in 2 parts, 5.49 in 4; batch 4 (512): 7.90, 6.17,
 // 7.55; batch 16 (2048): 12.85, 13.79, 17.64; fp32 tiny (16 pairs): 9.71,
-// 6.58, 5.71; bf16 mtp (4096 pairs): 18.24, 19.58, 24.12; batch 8 (1024
-// pairs) in 2 parts 9.96 against about 9.3.
+// 6.58, 5.71; bf16 mtp (4096 pairs): 18.24, 19.58, 24.12.  Between 512 and
+// 1024 pairs, in 2 parts against the persistent kernel: fp16 batch 5 (640)
+// 8.17 / 8.33, 6 (768) 8.73 / 8.85, 7 (896) 9.16 / 9.06, 8 (1024) 9.81 /
+// 9.46; bf16 mtp (64 heads) batch 10 (640) 7.26 / 7.54.
 #ifndef SSU_DSPLIT_MAX_UNITS
-#define SSU_DSPLIT_MAX_UNITS 512
+#define SSU_DSPLIT_MAX_UNITS 768
 #endif
 #ifndef SSU_DSPLIT4_MAX_UNITS
 #define SSU_DSPLIT4_MAX_UNITS 256

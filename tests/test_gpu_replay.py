@@ -58,20 +58,20 @@ CASES = {
     # up to 512 fp8 pairs: one head per wave, one wave per workgroup
     "fp8_small": dict(spec=dict(num_slots=10, nheads=64, ngroups=8, state_dtype="fp8"), batch=6, T=4,
                       pnat_max=12, out="bf16", varlen=True, n_padding=1),
-    # 16-bit checkpoints from 2048 pairs (groups of a multiple of 8 heads, rings up to 16): two heads per
+    # 16-bit checkpoints from 1536 pairs (groups of a multiple of 8 heads, rings up to 16): two heads per
     # wave (groups of 16 and of 8); prod_f16, mtp_bf16 and large_bf16_varlen above run there too
     "f16_pair": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="f16"), batch=256, T=8,
                      pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "bf16_pair_hpg8": dict(spec=dict(num_slots=600, nheads=64, ngroups=8, state_dtype="bf16"), batch=512, T=4,
                            pnat_max=4, out="bf16", n_padding=2),
-    # 513 to 2047 pairs of a 16-bit checkpoint: the persistent kernel
-    "f16_persistent": dict(spec=dict(num_slots=20, nheads=128, ngroups=8, state_dtype="f16"), batch=12, T=8,
+    # 769 to 1535 pairs of a 16-bit checkpoint: the persistent kernel
+    "f16_persistent": dict(spec=dict(num_slots=20, nheads=128, ngroups=8, state_dtype="f16"), batch=10, T=8,
                            pnat_max=8, out="bf16", varlen=True, n_padding=1),
     # 800 pairs of fp32: each head's rows in 2 parts (fp32 plain steps split at any size; the split
     # algorithm runs the persistent kernel)
     "f32_mid": dict(spec=dict(num_slots=120, nheads=8, ngroups=2, state_dtype="f32"), batch=100, T=3,
                     pnat_max=10, out="f32", n_padding=4),
-    # 16-bit up to 512 pairs: each head's rows split over waves, 2 parts from 257 pairs, 4 parts up to 256
+    # 16-bit up to 768 pairs: each head's rows split over waves, 2 parts from 257 pairs, 4 parts up to 256
     # (tiny_f32, bf16_f32out, f32_T16_L32 and f16_hpg1 above run in 4 parts)
     "bf16_dsplit2": dict(spec=dict(num_slots=8, nheads=128, ngroups=8, state_dtype="bf16"), batch=4, T=6,
                          pnat_max=8, out="bf16", varlen=True, n_padding=1),
@@ -259,7 +259,7 @@ def test_status_bits_and_padding():
 
 @pytest.mark.parametrize("state_dtype", ["bf16", "f16"])
 def test_pair_path_empty_entries(state_dtype):
-    """Two heads per wave (plain 16-bit steps from 2048 pairs) with varlen
+    """Two heads per wave (plain 16-bit steps from 1536 pairs) with varlen
     entries that have no new token, padding entries and the last entry empty:
     bit for bit against the split, and against the oracle."""
     from tests.test_gpu_fused import _with_empty_entries
