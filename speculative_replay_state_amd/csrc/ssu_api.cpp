@@ -18,8 +18,8 @@ thread_local char g_err[512] = "";
 
 // Default AUTO crossover in work units (batch * nheads).  On MI355X the
 // monolith is faster than the split at every measured size (128 to 65536
-// work units of fp16 with 128 heads: the split reaches 0.58-0.60 of the
-// monolith's throughput up to 512 units, 0.73-0.92 from 1024 to 8192, and
+// work units of fp16 with 128 heads: the split reaches 0.55-0.60 of the
+// monolith's throughput up to 512 units, 0.74-0.91 from 1024 to 8192, and
 // 0.89-0.90 from 16384 up), because forming C.B on MFMA inside each replay
 // wave costs less than the split's extra launch and scratch round trip.  AUTO
 // therefore never picks the split unless a caller lowers the threshold.
