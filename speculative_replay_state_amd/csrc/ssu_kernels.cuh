@@ -2487,14 +2487,16 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   // arithmetic per output value, bit for bit):
   //  - 16-bit, from SSU_PAIR_MIN_UNITS (entry, head) pairs, groups of a
   //    multiple of 8 heads, rings up to 16: two heads per wave;
-  //  - bf16 (other group sizes or rings) and fp8 without the recurrence
-  //    checkpoint from kPerHeadPlainUnits pairs, and fp8 and nvfp4 (with or
-  //    without the recurrence checkpoint) up to kFusedOneWaveMax pairs (one
-  //    wave per workgroup): the one-head-per-wave kernel with nothing to
-  //    fold.  Small steps, 128 heads: fp8 batch 1 / 2 / 4 9.24 / 9.11 /
-  //    9.79 us per call against 10.62 / 10.34 / 10.24 on the persistent
-  //    kernel; fp8 with the recurrence checkpoint batch 1 8.75 against 10.09;
-  //    nvfp4 batch 1 9.53 against 10.33.  Measured against the persistent kernel from
+  //  - fp8 without the recurrence checkpoint at any size, bf16 (other group
+  //    sizes or rings) from kPerHeadPlainUnits pairs, and fp8 with the
+  //    recurrence checkpoint and nvfp4 up to kFusedOneWaveMax pairs: the
+  //    one-head-per-wave kernel with nothing to fold (one wave per workgroup
+  //    up to kFusedOneWaveMax pairs).  fp8, 128 heads, per call against the
+  //    persistent kernel: batch 1 / 2 / 4 9.24 / 9.11 / 9.79 us against
+  //    10.62 / 10.34 / 10.24, batch 8 / 32 / 128 9.67 / 17.10 / 39.82 against
+  //    10.94 / 18.50 / 41.94.  fp8 with the recurrence checkpoint: batch 1
+  //    8.75 against 10.09, batch 32 19.91 against 17.85; nvfp4: batch 1 9.53
+  //    against 10.33, batch 32 18.18 against 17.72.  Measured against the persistent kernel from
   //    32768 pairs up: bf16 1-3 % faster (batch 256-1024 of 128 heads), fp8
   //    10 % faster; fp16 1.5-5 % slower, fp8 with the recurrence checkpoint
   //    20 % and nvfp4 57 % slower (those forms of it hold more registers);
@@ -2510,7 +2512,7 @@ hipError_t mono_t(const KCache &c, const KStep &s, hipStream_t st) {
   }
   if constexpr (ST == kBF16 || ST == kFP8 || ST == kNVFP4) {
     const int64_t units = (int64_t)s.batch * c.H;
-    const bool big = ST != kNVFP4 && (ST == kBF16 || !c.recur) && units >= kPerHeadPlainUnits;
+    const bool big = (ST == kBF16 && units >= kPerHeadPlainUnits) || (ST == kFP8 && !c.recur);
     const bool small = (ST == kFP8 || ST == kNVFP4) && units <= kFusedOneWaveMax;
     if (big || small) return s.z ? fused_z<ST, OT, true>(c, s, st) : fused_z<ST, OT, false>(c, s, st);
   }

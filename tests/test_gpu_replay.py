@@ -50,7 +50,7 @@ CASES = {
     "f16_hpg1": dict(spec=dict(num_slots=12, nheads=6, ngroups=6, state_dtype="f16", ring_len=12),
                      batch=7, T=5, pnat_max=7, out="bf16"),
     # 342 x 96 = 32832 (entry, head) pairs, groups of 12 heads: a plain bf16 monolith step runs one head per
-    # wave; 33 x 128 fp8 pairs run in the persistent kernel, 256 x 128 in the one-head kernel
+    # wave; plain fp8 steps (33 x 128 and 256 x 128 pairs) run in the one-head kernel at any size
     "bf16_per_head": dict(spec=dict(num_slots=400, nheads=96, ngroups=8, state_dtype="bf16"), batch=342, T=4,
                           pnat_max=8, out="bf16", varlen=True, n_padding=3),
     "fp8_per_head": dict(spec=dict(num_slots=300, nheads=128, ngroups=8, state_dtype="fp8"), batch=256, T=4,
@@ -297,7 +297,7 @@ BAD_RING_PATHS = [
     ("f16_pair", "monolith", False),        # two heads per wave
     ("f16_pair", "split", False),           # C.B precompute + persistent kernel
     ("fp8_per_head", "monolith", False),    # one head per wave, nothing folded
-    ("fp8", "monolith", False),             # persistent kernel, fp8 tile
+    ("fp8", "split", False),                # C.B precompute + persistent kernel, fp8 tile
     ("fp8_per_head", "auto", True),         # fused flush-in-step
 ]
 
