@@ -2368,7 +2368,7 @@ __global__ void step_ring_advance_kernel(KCache c, KStep s) {
 // The fused kernel at WPG heads per workgroup (with an NVFP4 fold, the maxima
 // pass first: the encode needs the slot's scale).
 template <int ST, int OT, bool HAS_Z, bool SEP, int WPG>
-void fused_launch(const KCache &c, const KStep &s, hipStream_t st) {
+hipError_t fused_launch(const KCache &c, const KStep &s, hipStream_t st) {
   const int htiles = (c.H + WPG - 1) / WPG;
   const int64_t ntiles = (int64_t)s.batch * htiles;
   if constexpr (ST == kNVFP4) {
@@ -2379,21 +2379,21 @@ void fused_launch(const KCache &c, const KStep &s, hipStream_t st) {
       else
         fold_max_kernel<32, true, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, nullptr, nullptr,
                                                                                          nullptr, htiles, ntiles);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
     }
   }
   if (c.L <= 16)
     fused_kernel<ST, OT, 16, HAS_Z, SEP, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, htiles, ntiles);
   else
     fused_kernel<ST, OT, 32, HAS_Z, SEP, WPG><<<dim3(xcd_grid(ntiles)), dim3(WPG * 64), 0, st>>>(c, s, htiles, ntiles);
+  return hipGetLastError();
 }
 
 template <int ST, int OT, bool HAS_Z, bool SEP>
 hipError_t fused_zs(const KCache &c, const KStep &s, hipStream_t st) {
-  if ((int64_t)s.batch * c.H <= kFusedOneWaveMax)
-    fused_launch<ST, OT, HAS_Z, SEP, 1>(c, s, st);
-  else
-    fused_launch<ST, OT, HAS_Z, SEP, kHeadWaves>(c, s, st);
-  hipError_t err = hipGetLastError();
+  const hipError_t err = (int64_t)s.batch * c.H <= kFusedOneWaveMax ? fused_launch<ST, OT, HAS_Z, SEP, 1>(c, s, st)
+                                                                     : fused_launch<ST, OT, HAS_Z, SEP, kHeadWaves>(c, s, st);
   if (err != hipSuccess || !s.fold) return err;  // nothing folded: ring_start stays
   step_ring_advance_kernel<ST><<<dim3((unsigned)((s.batch + 255) / 256)), dim3(256), 0, st>>>(c, s);
   return hipGetLastError();
@@ -2533,8 +2533,8 @@ hipError_t split_t(const KCache &c, const KStep &s, hipStream_t st) {
 // The flush's kernels at WPG heads per workgroup (an NVFP4 flush: the maxima
 // pass first, the encode needs the slot's scale).
 template <int ST, int WPG>
-void flush_launch(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int n,
-                  hipStream_t st) {
+hipError_t flush_launch(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A, int n,
+                        hipStream_t st) {
   const int htiles = (c.H + WPG - 1) / WPG;
   const int64_t ntiles = (int64_t)n * htiles;
   const dim3 grid(xcd_grid(ntiles)), block(WPG * 64);
@@ -2546,6 +2546,8 @@ void flush_launch(const KCache &c, const int32_t *slot_idx, const int32_t *num_f
       fold_max_kernel<16, false, WPG><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
     else
       fold_max_kernel<32, false, WPG><<<grid, block, 0, st>>>(c, none, slot_idx, num_fold, A, htiles, ntiles);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
   if (sep) {
     if constexpr (ST == kFP8 || ST == kNVFP4) {
@@ -2562,16 +2564,14 @@ void flush_launch(const KCache &c, const int32_t *slot_idx, const int32_t *num_f
         flush_kernel<ST, 32, false, WPG><<<grid, block, 0, st>>>(c, slot_idx, num_fold, A, htiles, ntiles);
     }
   }
+  return hipGetLastError();
 }
 
 template <int ST>
 hipError_t flush_t(const KCache &c, const int32_t *slot_idx, const int32_t *num_fold, const float *A,
                    int n, hipStream_t st) {
-  if ((int64_t)n * c.H <= kFusedOneWaveMax)
-    flush_launch<ST, 1>(c, slot_idx, num_fold, A, n, st);
-  else
-    flush_launch<ST, kHeadWaves>(c, slot_idx, num_fold, A, n, st);
-  hipError_t err = hipGetLastError();
+  const hipError_t err = (int64_t)n * c.H <= kFusedOneWaveMax ? flush_launch<ST, 1>(c, slot_idx, num_fold, A, n, st)
+                                                               : flush_launch<ST, kHeadWaves>(c, slot_idx, num_fold, A, n, st);
   if (err != hipSuccess) return err;
   ring_advance_kernel<ST><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(c, slot_idx, num_fold, n);
   return hipGetLastError();
