@@ -144,8 +144,10 @@ enum {
  * low nibble); block scales (t < 16, t >= 16) in state_scale bytes
  * l * 8 + rb * 2 + 0 / 1 of the head's 512.
  * Requirements: headdim == 64, dstate == 128, nheads % ngroups == 0,
- * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer and slot stride
- * 16-byte aligned.  status may be NULL.
+ * 1 <= ring_len <= 32, io_dtype == SSU_BF16; every pointer 16-byte aligned
+ * (ring_start and status, i32 arrays: 4-byte), even one that the state dtype
+ * leaves unused; the slot stride of every tensor in use at least one packed
+ * page and a multiple of 16.  status may be NULL.
  */
 typedef struct ssu_cache {
   int32_t num_slots, nheads, ngroups, headdim, dstate, ring_len;
@@ -195,7 +197,9 @@ typedef struct ssu_cache {
  *               nonzero: dt' = dt + dt_bias [FI, the dt_softplus flag].  The
  *               dt ring stores dt' either way.
  * Requirements: 1 <= max_seqlen <= min(16, ring_len); pointers 16-byte
- * aligned (dt, A, D, dt_bias: 4-byte).  Active slots must be unique.
+ * aligned (dt, A, D, dt_bias and the i32 arrays slot_idx, prev_num_accepted,
+ * cu_seqlens, num_fold: 4-byte).  Active slots must be unique.  batch == 0
+ * is a no-op: past the cache and max_seqlen checks nothing else is looked at.
  */
 typedef struct ssu_step {
   int32_t batch, max_seqlen;
@@ -223,7 +227,8 @@ typedef struct ssu_step {
 /* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen): the
  * fp32 C.B products of every (entry, group) [FI Description item 1: the
  * precompute writes C.B to caller-provided, graph-safe scratch, allocated by
- * the caller like the output].  Returns 0 for an invalid cache description. */
+ * the caller like the output].  Returns 0 for an invalid cache description
+ * or a negative batch or max_seqlen. */
 size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen);
 
 /*
@@ -237,7 +242,8 @@ size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seq
  * write recur_state when present (fp16 with the stochastic rounding above,
  * keyed by sr_seed; sr_seed is unused otherwise), zero its x/B/dt rings and
  * set ring_start to 0.  Other ids are ignored.  slot ids must be unique.
- * n == 0 is a no-op.
+ * n == 0 is a no-op; n < 0 is SSU_ERR_INVALID.  states 16-byte aligned and
+ * states_batch_stride >= 0 a multiple of 4; slot_idx 4-byte aligned.
  */
 int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
                    const int32_t *slot_idx, int32_t n, uint64_t sr_seed, hipStream_t stream);
@@ -299,13 +305,16 @@ int ssu_replay_step_noalloc(const ssu_cache *cache, const ssu_step *step, hipStr
  *   h <- exp(cumA_{k-1}) h + sum_{s<k} exp(cumA_{k-1} - cumA_s) dt'_s x_s B_s^T,
  * re-encode it in state_dtype, then advance ring_start[slot] by k (mod L).
  * k == 0 changes nothing.  A: [nheads] f32, the same A the steps use.
- * The caller's next pnat for the slot is pnat + accepted - k.
+ * The caller's next pnat for the slot is pnat + accepted - k.  n == 0 is a
+ * no-op, n < 0 SSU_ERR_INVALID; slot_idx, num_fold and A are 4-byte aligned.
  */
 int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold,
               const float *A, int32_t n, uint64_t sr_seed, hipStream_t stream);
 
-/* The algorithm SSU_ALGO_AUTO resolves to for this step (MONOLITH or SPLIT),
- * or a negative error code. */
+/* The algorithm this step runs (MONOLITH or SPLIT): step->algo when it names
+ * one, else what SSU_ALGO_AUTO resolves to; or the negative error code that
+ * ssu_replay_step would return for these descriptors (the workspace aside).
+ * Launches nothing. */
 int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step);
 
 /* Work-unit threshold (batch * nheads) at or above which AUTO picks SPLIT.
