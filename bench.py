@@ -493,6 +493,7 @@ def main():
 
     # --- what plain streams reach on this GPU (context for the roofline) ----
     streams = None if args.no_streams else hbm_streams(dev)
+    floor_us = None if args.no_streams else launch_floor_us(dev)
 
     wl, spec = res["wl"], res["spec"]
     batch, H, G, T = res["batch"], res["H"], res["G"], res["T"]
@@ -558,6 +559,7 @@ def main():
         "hbm_stream": (None if streams is None else
                        dict(streams, frac_of_copy=achieved / streams["copy_GBps"],
                             frac_of_rmw=achieved / streams["rmw_GBps"])),
+        "launch_floor_us": floor_us,
         "extra": extra,
         "cpu_baseline": cpu,
     }
@@ -597,6 +599,37 @@ def hbm_streams(dev, nbytes=2 ** 31, reps=5):
     del src, dst, rows, acc
     torch.cuda.empty_cache()
     return out
+
+
+def launch_floor_us(dev, n=20, reps=5):
+    """Microseconds per launch of a one-value PyTorch kernel, n launches in a
+    row (each waiting for the one before) captured in one HIP graph and
+    replayed as the steps are: the floor that a step of one launch pays on
+    this GPU whatever it computes.  Median of `reps` replays."""
+    t = torch.zeros(1, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            t.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            t.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del g, t
+    return float(np.median(ms)) * 1e3 / n
 
 
 def cpu_baseline(args, res):
