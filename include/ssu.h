@@ -198,9 +198,15 @@ typedef struct ssu_cache {
  *               dt ring stores dt' either way.
  * Requirements: 1 <= max_seqlen <= min(16, ring_len); pointers 16-byte
  * aligned (dt, A, D, dt_bias and the i32 arrays slot_idx, prev_num_accepted,
- * cu_seqlens, num_fold: 4-byte).  Active slots must be unique.  batch == 0
- * is a no-op: past the cache and max_seqlen checks nothing else is looked at.
+ * cu_seqlens, num_fold: 4-byte); batch * nheads <= SSU_MAX_PAIRS (else
+ * SSU_ERR_UNSUPPORTED).  Active slots must be unique.  batch == 0 is a no-op:
+ * past the cache and max_seqlen checks nothing else is looked at.
  */
+/* (entry, head) pairs one call may cover: every launch grid, in threads,
+ * then fits 32 bits and every token row index 31 bits.  Calls past it
+ * return SSU_ERR_UNSUPPORTED; split such a batch over several calls. */
+#define SSU_MAX_PAIRS ((1 << 24) - 1)
+
 typedef struct ssu_step {
   int32_t batch, max_seqlen;
   const int32_t *slot_idx;
@@ -242,8 +248,9 @@ size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seq
  * write recur_state when present (fp16 with the stochastic rounding above,
  * keyed by sr_seed; sr_seed is unused otherwise), zero its x/B/dt rings and
  * set ring_start to 0.  Other ids are ignored.  slot ids must be unique.
- * n == 0 is a no-op; n < 0 is SSU_ERR_INVALID.  states 16-byte aligned and
- * states_batch_stride >= 0 a multiple of 4; slot_idx 4-byte aligned.
+ * n == 0 is a no-op; n < 0 is SSU_ERR_INVALID, n * nheads > SSU_MAX_PAIRS
+ * SSU_ERR_UNSUPPORTED.  states 16-byte aligned and states_batch_stride >= 0
+ * a multiple of 4; slot_idx 4-byte aligned.
  */
 int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_batch_stride,
                    const int32_t *slot_idx, int32_t n, uint64_t sr_seed, hipStream_t stream);
@@ -306,7 +313,8 @@ int ssu_replay_step_noalloc(const ssu_cache *cache, const ssu_step *step, hipStr
  * re-encode it in state_dtype, then advance ring_start[slot] by k (mod L).
  * k == 0 changes nothing.  A: [nheads] f32, the same A the steps use.
  * The caller's next pnat for the slot is pnat + accepted - k.  n == 0 is a
- * no-op, n < 0 SSU_ERR_INVALID; slot_idx, num_fold and A are 4-byte aligned.
+ * no-op, n < 0 SSU_ERR_INVALID, n * nheads > SSU_MAX_PAIRS
+ * SSU_ERR_UNSUPPORTED; slot_idx, num_fold and A are 4-byte aligned.
  */
 int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *num_fold,
               const float *A, int32_t n, uint64_t sr_seed, hipStream_t stream);

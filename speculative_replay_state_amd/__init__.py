@@ -93,6 +93,7 @@ EXPORTED = ("ssu_workspace_size", "ssu_init_state", "ssu_replay_step", "ssu_repl
             "ssu_resolve_algo", "ssu_get_split_threshold", "ssu_set_split_threshold",
             "ssu_last_error")
 SSU_NOALLOC_SCRATCH_BYTES = 16 << 20
+SSU_MAX_PAIRS = (1 << 24) - 1
 
 
 class SsuError(RuntimeError):

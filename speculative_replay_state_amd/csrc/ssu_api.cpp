@@ -170,6 +170,9 @@ int check_step(const ssu_cache *c, const ssu_step *s) {
     return fail(s->max_seqlen > c->ring_len ? SSU_ERR_INVALID : SSU_ERR_UNSUPPORTED,
                 "max_seqlen %d exceeds min(16, ring_len) = %d", s->max_seqlen, tmax);
   if (s->batch == 0) return SSU_OK;
+  if ((int64_t)s->batch * c->nheads > SSU_MAX_PAIRS)
+    return fail(SSU_ERR_UNSUPPORTED, "batch %d x nheads %d exceeds SSU_MAX_PAIRS (%d) (entry, head) pairs per call",
+                s->batch, c->nheads, SSU_MAX_PAIRS);
   if (!s->slot_idx || !s->prev_num_accepted || !s->x || !s->B || !s->C || !s->dt || !s->A || !s->D ||
       !s->dt_bias || !s->out)
     return fail(SSU_ERR_INVALID, "step tensors must not be NULL (cu_seqlens and workspace may be)");
@@ -335,6 +338,9 @@ int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *nu
   if (rc != SSU_OK) return rc;
   if (n < 0) return fail(SSU_ERR_INVALID, "n must be >= 0 (got %d)", n);
   if (n == 0) return ok();
+  if ((int64_t)n * cache->nheads > SSU_MAX_PAIRS)
+    return fail(SSU_ERR_UNSUPPORTED, "n %d x nheads %d exceeds SSU_MAX_PAIRS (%d) (entry, head) pairs per call", n,
+                cache->nheads, SSU_MAX_PAIRS);
   if (!slot_idx || !num_fold || !A) return fail(SSU_ERR_INVALID, "slot_idx, num_fold and A must not be NULL");
   if (!aligned4(slot_idx) || !aligned4(num_fold) || !aligned4(A))
     return fail(SSU_ERR_INVALID, "slot_idx, num_fold and A must be 4-byte aligned");
@@ -350,6 +356,9 @@ int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_b
   if (rc != SSU_OK) return rc;
   if (n < 0) return fail(SSU_ERR_INVALID, "n must be >= 0 (got %d)", n);
   if (n == 0) return ok();
+  if ((int64_t)n * cache->nheads > SSU_MAX_PAIRS)
+    return fail(SSU_ERR_UNSUPPORTED, "n %d x nheads %d exceeds SSU_MAX_PAIRS (%d) (entry, head) pairs per call", n,
+                cache->nheads, SSU_MAX_PAIRS);
   if (!states || !slot_idx) return fail(SSU_ERR_INVALID, "states and slot_idx must not be NULL");
   if (states_batch_stride < 0) return fail(SSU_ERR_INVALID, "states_batch_stride must be >= 0");
   if (!aligned16(states) || states_batch_stride % 4 != 0 || !aligned4(slot_idx))

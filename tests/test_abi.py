@@ -108,6 +108,7 @@ STEP_ERRORS = [
     (dict(num_fold=FAKE), -2, "monolith only"),
     (dict(num_fold=FAKE + 2, algo=0), -1, "num_fold"),
     (dict(z=FAKE + 8), -1, "z must be 16-byte aligned"),
+    (dict(batch=(1 << 24) // 16), -2, "SSU_MAX_PAIRS"),  # 16 heads: one pair past the bound
 ]
 
 
@@ -146,6 +147,16 @@ def test_auto_defaults_to_monolith(ssu):
     c = _cache(ssu)
     s = _step(ssu, algo=ssu.SSU_ALGO_AUTO, batch=100000)
     assert ssu.ssu_resolve_algo(c, s) == ssu.SSU_ALGO_MONOLITH
+
+
+def test_pairs_per_call_bound(ssu):
+    c = _cache(ssu)  # 16 heads
+    n_max = ssu.SSU_MAX_PAIRS // 16
+    assert ssu.ssu_resolve_algo(c, _step(ssu, batch=n_max)) == ssu.SSU_ALGO_SPLIT
+    assert ssu.ssu_flush(c, FAKE, FAKE, FAKE, n_max + 1) == -2
+    assert "SSU_MAX_PAIRS" in ssu.ssu_last_error()
+    assert ssu.ssu_init_state(c, FAKE, 0, FAKE, n_max + 1) == -2
+    assert "SSU_MAX_PAIRS" in ssu.ssu_last_error()
 
 
 def test_empty_calls_are_noops(ssu):

@@ -102,7 +102,7 @@ def cache_fields(draw):
 @st.composite
 def step_fields(draw, ring_len):
     s = {}
-    s["batch"] = draw(mostly(st.sampled_from([0, 1, 3, 64, 2049]), st.just(-1)))
+    s["batch"] = draw(mostly(st.sampled_from([0, 1, 3, 64, 2049, 1 << 20]), st.just(-1)))
     s["max_seqlen"] = draw(mostly(st.integers(1, max(1, min(16, ring_len))), st.integers(-1, 34)))
     for k in ("x", "B", "C", "out"):
         s[k] = draw(ptr(16))
@@ -189,6 +189,8 @@ def step_violations(c, s):
         v.append(("max_seqlen <= 16", either))
     if s["batch"] <= 0:
         return v  # batch 0 is a no-op: the step's tensors are not looked at
+    if s["batch"] * c["nheads"] > (1 << 24) - 1:
+        v.append(("batch * nheads <= SSU_MAX_PAIRS", {UNSUPPORTED}))
     for k in ("slot_idx", "prev_num_accepted", "x", "B", "C", "dt", "A", "D", "dt_bias", "out"):
         if s[k] is None:
             v.append((k + " not NULL", {INVALID}))
