@@ -332,7 +332,8 @@ int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step);
 int64_t ssu_get_split_threshold(void);
 int64_t ssu_set_split_threshold(int64_t work_units);
 
-/* The calling thread's last error message ("" if none). */
+/* The message of the calling thread's last call that failed; "" after a
+ * call that succeeded (ssu_get/set_split_threshold leave it as it was). */
 const char *ssu_last_error(void);
 
 #ifdef __cplusplus

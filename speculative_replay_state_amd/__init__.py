@@ -159,6 +159,37 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_device(t, name: str):
+    """A tensor the kernels may address: on the GPU (a host pointer handed to
+    a kernel faults the device)."""
+    if t is not None and not getattr(t, "is_cuda", False):
+        raise ValueError("%s must be a device tensor (got one on %s)" % (name, getattr(t, "device", "?")))
+
+
+def _packed(t, name: str, nbytes: Optional[int] = None):
+    """A device tensor whose bytes are packed (C-contiguous) and, when
+    `nbytes` is given, at least that many."""
+    if t is None:
+        return
+    _on_device(t, name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    have = t.numel() * t.element_size()
+    if nbytes is not None and have < nbytes:
+        raise ValueError("%s holds %d bytes; the step addresses %d" % (name, have, nbytes))
+
+
+def _slot_pages(t, name: str, num_slots: int) -> int:
+    """Byte stride between the slot pages of a per-slot cache tensor
+    [num_slots, ...] whose pages are each packed (the rows may be padded)."""
+    _on_device(t, name)
+    if t.dim() < 2 or t.shape[0] != num_slots:
+        raise ValueError("%s must be [num_slots=%d, ...] (got shape %s)" % (name, num_slots, tuple(t.shape)))
+    if not t[0].is_contiguous():
+        raise ValueError("%s: each slot page must be contiguous" % name)
+    return t.stride(0) * t.element_size()
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -192,19 +223,29 @@ class DeviceCache:
     gscale: object = None  # nvfp4: uint8 [num_slots, stride]: f32 slot scale, then the head maxima
 
     def desc(self) -> SsuCache:
+        """The C descriptor.  Raises ValueError for a tensor the kernels could
+        not address as the layout says: on the host, not num_slots pages, a
+        page that is not contiguous, or ring_start / status too small."""
         scaled = self.state_dtype in ("fp8", "nvfp4")
         nvfp4 = self.state_dtype == "nvfp4"
+        n = self.num_slots
+
+        def pages(t, name):
+            return _slot_pages(t, name, n)
+
+        _packed(self.ring_start, "ring_start", 4 * n)
+        _packed(self.status, "status", 4)
         return SsuCache(
-            self.num_slots, self.nheads, self.ngroups, self.headdim, self.dstate, self.ring_len,
+            n, self.nheads, self.ngroups, self.headdim, self.dstate, self.ring_len,
             DTYPE_CODES[self.state_dtype], SSU_BF16,
-            _ptr(self.state), self.state.stride(0),
-            _ptr(self.scale) if scaled else None, self.scale.stride(0) if scaled else 0,
-            _ptr(self.x_cache), self.x_cache.stride(0),
-            _ptr(self.B_cache), self.B_cache.stride(0),
-            _ptr(self.dt_cache), self.dt_cache.stride(0),
+            _ptr(self.state), pages(self.state, "state"),
+            _ptr(self.scale) if scaled else None, pages(self.scale, "scale") if scaled else 0,
+            _ptr(self.x_cache), pages(self.x_cache, "x_cache"),
+            _ptr(self.B_cache), pages(self.B_cache, "B_cache"),
+            _ptr(self.dt_cache), pages(self.dt_cache, "dt_cache"),
             _ptr(self.ring_start), _ptr(self.status),
-            _ptr(self.recur), 0 if self.recur is None else self.recur.stride(0),
-            _ptr(self.gscale) if nvfp4 else None, self.gscale.stride(0) if nvfp4 else 0)
+            _ptr(self.recur), 0 if self.recur is None else pages(self.recur, "recur"),
+            _ptr(self.gscale) if nvfp4 else None, pages(self.gscale, "gscale") if nvfp4 else 0)
 
 
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
@@ -219,8 +260,30 @@ def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A
     # The descriptor holds raw device pointers: it keeps the tensors they point
     # into alive, so that memory a kernel (or a captured graph) writes is never
     # handed to another tensor while the descriptor is in use.
-    desc._tensors = (slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out, workspace, num_fold, z)
+    desc._tensors = dict(slot_idx=slot_idx, prev_num_accepted=pnat, cu_seqlens=cu_seqlens, x=x, B=B, C=C, dt=dt,
+                         A=A, D=D, dt_bias=dt_bias, out=out, workspace=workspace, num_fold=num_fold, z=z)
     return desc
+
+
+def check_step_tensors(cache: DeviceCache, step: SsuStep):
+    """The tensors of a step descriptor made by make_step_desc are device
+    tensors, packed, and (with a fixed T per entry) as large as the layouts of
+    include/ssu.h make the step address; the library checks the rest.  With
+    cu_seqlens the row count lives on the device, so only the per-entry and
+    per-head arrays are sized here.  Raises ValueError."""
+    t = getattr(step, "_tensors", None)
+    if t is None or step.batch <= 0:
+        return
+    H, G, b = cache.nheads, cache.ngroups, step.batch
+    rows = None if t["cu_seqlens"] is not None else b * step.max_seqlen
+    out_bytes = 4 if step.out_dtype == SSU_F32 else 2
+    sizes = dict(slot_idx=4 * b, prev_num_accepted=4 * b, cu_seqlens=4 * (b + 1), num_fold=4 * b,
+                 A=4 * H, D=4 * H, dt_bias=4 * H, workspace=None)
+    if rows is not None:
+        sizes.update(x=rows * H * 64 * 2, B=rows * G * 128 * 2, C=rows * G * 128 * 2, dt=rows * H * 4,
+                     out=rows * H * 64 * out_bytes, z=rows * H * 64 * 2)
+    for name, tensor in t.items():
+        _packed(tensor, name, sizes.get(name))
 
 
 def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:
@@ -230,6 +293,8 @@ def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:
 def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, stream=None, sr_seed=0):
     """ssu_init_state with torch tensors (states f32 [n, H, 64, 128] on device)."""
     n = slot_idx.numel()
+    _on_device(states, "states")
+    _packed(slot_idx, "slot_idx")
     if states_batch_stride is None:
         states_batch_stride = states.stride(0) if n else 0
     _check(ssu_init_state(cache.desc(), _ptr(states), states_batch_stride, _ptr(slot_idx), n,
@@ -237,9 +302,19 @@ def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, s
 
 
 def replay_step(cache: DeviceCache, step: SsuStep, stream=None):
+    check_step_tensors(cache, step)
     _check(ssu_replay_step(cache.desc(), step, _stream(stream)))
 
 
+def replay_step_noalloc(cache: DeviceCache, step: SsuStep, stream=None):
+    check_step_tensors(cache, step)
+    _check(ssu_replay_step_noalloc(cache.desc(), step, _stream(stream)))
+
+
 def flush(cache: DeviceCache, slot_idx, num_fold, A, stream=None, sr_seed=0):
+    n = slot_idx.numel()
+    _packed(slot_idx, "slot_idx")
+    _packed(num_fold, "num_fold", 4 * n)
+    _packed(A, "A", 4 * cache.nheads)
     _check(ssu_flush(cache.desc(), _ptr(slot_idx), _ptr(num_fold), _ptr(A), slot_idx.numel(), int(sr_seed),
                      _stream(stream)))

@@ -243,7 +243,12 @@ int64_t ssu_get_split_threshold(void) { return g_split_threshold.load(); }
 int64_t ssu_set_split_threshold(int64_t work_units) { return g_split_threshold.exchange(work_units); }
 
 size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen) {
-  if (check_cache(cache) != SSU_OK || batch < 0 || max_seqlen < 0) return 0;
+  if (check_cache(cache) != SSU_OK) return 0;
+  if (batch < 0 || max_seqlen < 0) {
+    fail(SSU_ERR_INVALID, "batch and max_seqlen must be >= 0 (got %d, %d)", batch, max_seqlen);
+    return 0;
+  }
+  ok();
   return split_bytes(cache, batch, max_seqlen);
 }
 
@@ -252,6 +257,7 @@ int ssu_resolve_algo(const ssu_cache *cache, const ssu_step *step) {
   if (rc != SSU_OK) return rc;
   rc = check_step(cache, step);
   if (rc != SSU_OK) return rc;
+  ok();
   return resolve(cache, step);
 }
 

@@ -194,3 +194,22 @@ def test_step_desc_keeps_its_tensors_alive(ssu):
     del d
     gc.collect()
     assert ref() is None
+
+
+def test_binding_refuses_host_tensors(ssu):
+    """The torch front end never hands a host pointer to the library: a cache
+    or step tensor that is not on the GPU is a ValueError before any call."""
+    import torch
+    u8 = lambda n: torch.zeros(4, n, dtype=torch.uint8)
+    dc = ssu.DeviceCache(4, 16, 2, 16, "bf16", u8(16 * 64 * 128 * 2), None, u8(16 * 16 * 64 * 2),
+                         u8(2 * 16 * 128 * 2), u8(16 * 16 * 4), torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):
+        dc.desc()
+    t = torch.zeros(64, dtype=torch.int32)
+    d = ssu.make_step_desc(1, 1, t, t, None, t, t, t, t, t, t, t, t)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssu.check_step_tensors(dc, d)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssu.replay_step(dc, d)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssu.flush(dc, t, t, t)

@@ -231,12 +231,13 @@ def test_validation_matches_the_header(ssu, cache_step, threshold):
     old = ssu.ssu_set_split_threshold(threshold)
     try:
         rc = ssu.ssu_resolve_algo(c, s)
+        msg = ssu.ssu_last_error()
     finally:
         ssu.ssu_set_split_threshold(old)
     ws = ssu.ssu_workspace_size(c, 1, 1)
     if cv:
-        assert rc in set().union(*(codes for _, codes in cv)), (rc, ssu.ssu_last_error(), cv)
-        assert ssu.ssu_last_error()
+        assert rc in set().union(*(codes for _, codes in cv)), (rc, msg, cv)
+        assert msg and ssu.ssu_last_error() == msg  # the cache check again
         assert ws == 0
         # every entry point checks the cache first, the same way
         assert ssu.ssu_flush(c, BASE, BASE, BASE, 1) == rc
@@ -244,14 +245,15 @@ def test_validation_matches_the_header(ssu, cache_step, threshold):
         assert ssu.ssu_replay_step(c, s) == rc
         assert ssu.ssu_replay_step_noalloc(c, s) == rc
         return
-    assert ws > 0, ssu.ssu_last_error()
+    assert ws > 0 and ssu.ssu_last_error() == "", ssu.ssu_last_error()
     if sv:
-        assert rc in set().union(*(codes for _, codes in sv)), (rc, ssu.ssu_last_error(), sv)
-        assert ssu.ssu_last_error()
+        assert rc in set().union(*(codes for _, codes in sv)), (rc, msg, sv)
+        assert msg
         assert ssu.ssu_replay_step(c, s) == rc
         assert ssu.ssu_replay_step_noalloc(c, s) == rc
         return
-    assert rc >= 0, (rc, ssu.ssu_last_error())
+    assert rc >= 0, (rc, msg)
+    assert msg == ""
     if step["algo"] in (MONOLITH, SPLIT):
         want = step["algo"]
     elif step["num_fold"] is not None:
