@@ -12,7 +12,11 @@ allows, so that the dispatch meets combinations nobody chose:
   - output dtype, the z gate and dt' without softplus.
 Each draw runs the plain step (monolith and split, bit for bit with each
 other) and the fused flush-in-step, against the oracle at the same bounds as
-the fixed cases.  The draw is printed before its GPU work.
+the fixed cases.  32 more draws do the same with separate checkpoints (an
+fp8 or NVFP4 read checkpoint beside the FP16 recurrence checkpoint, folded
+with stochastic rounding under a drawn seed), whose folds are checked as the
+fixed separate-checkpoint cases check theirs.  The draw is printed before its
+GPU work.
 """
 import numpy as np
 import pytest
@@ -29,6 +33,7 @@ if torch.cuda.is_available():
 from oracle import ssu_oracle as O
 
 N_DRAWS = 64
+N_SEPARATE = 32
 
 
 @pytest.fixture(autouse=True)
@@ -61,7 +66,24 @@ def draw(i):
                 with_z=bool(rng.integers(0, 4) == 0), dt_softplus=bool(rng.integers(0, 4) != 0))
 
 
-def _run(spec, cache, step, out_dtype, algo, k=None):
+def draw_separate(i):
+    """A draw with separate checkpoints: fp8 or NVFP4 read checkpoint."""
+    rng = np.random.default_rng(95000 + i)
+    state = ["fp8", "nvfp4"][i % 2]
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    hpg = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+    L = int(rng.integers(1, 33))
+    T = int(rng.integers(1, min(16, L) + 1))
+    batch = int(rng.integers(1, 41))
+    spec = dict(num_slots=batch + int(rng.integers(1, 8)), nheads=G * hpg, ngroups=G, state_dtype=state,
+                ring_len=L, slot_pad=int(rng.choice([0, 256])), separate=True)
+    return dict(spec=spec, batch=batch, T=T, pnat_max=int(rng.integers(0, L - T + 1)),
+                varlen=bool(rng.integers(0, 2)), n_padding=int(rng.integers(0, batch // 4 + 1)),
+                out="f32" if rng.integers(0, 4) == 0 else "bf16", with_z=bool(rng.integers(0, 4) == 0),
+                dt_softplus=bool(rng.integers(0, 4) != 0), sr_seed=int(rng.integers(0, 2 ** 63)))
+
+
+def _run(spec, cache, step, out_dtype, algo, k=None, sr_seed=0):
     t = sd.upload_cache(cache, gh.DEV)
     st = sd.upload_step(step, gh.DEV)
     dc = gh.device_cache(spec, t)
@@ -73,7 +95,7 @@ def _run(spec, cache, step, out_dtype, algo, k=None):
     kt = None if k is None else torch.from_numpy(k).to(gh.DEV)
     desc = ssu.make_step_desc(step.batch, step.T, st["slot_idx"], st["pnat"], st["cu_seqlens"], st["x"],
                               st["B"], st["C"], st["dt"], st["A"], st["D"], st["dt_bias"], out, out_dtype, ws,
-                              algo, num_fold=kt, z=st["z"], dt_softplus=step.dt_softplus)
+                              algo, num_fold=kt, z=st["z"], dt_softplus=step.dt_softplus, sr_seed=sr_seed)
     ssu.replay_step(dc, desc)
     torch.cuda.synchronize()
     return out, sd.download_cache(spec, t), int(dc.status.item())
@@ -81,8 +103,17 @@ def _run(spec, cache, step, out_dtype, algo, k=None):
 
 @pytest.mark.parametrize("i", range(N_DRAWS))
 def test_random_shape_parity(i):
-    d = draw(i)
+    check_draw(draw(i), i)
+
+
+@pytest.mark.parametrize("i", range(N_SEPARATE))
+def test_random_shape_separate_parity(i):
+    check_draw(draw_separate(i), 1000 + i)
+
+
+def check_draw(d, i):
     spec = synth.CacheSpec(**d["spec"])
+    seed = d.get("sr_seed", 0)
     print("draw", i, {k: v for k, v in d.items() if k != "spec"}, d["spec"], flush=True)
     cache = synth.make_cache(spec, 91000 + i)
     step = synth.make_step(spec, d["batch"], d["T"], 92000 + i, d["pnat_max"], varlen=d["varlen"],
@@ -101,6 +132,9 @@ def test_random_shape_parity(i):
         err = gh.rel_err(gh.to_f64(out), ref)
         assert err <= tol, "%s: max rel err %g" % (algo, err)
         gh.check_cache_after_step(spec, cache, gpu, ref_cache)
+        if spec.separate:  # a plain step leaves the recurrence checkpoint and the slot scales alone
+            assert np.array_equal(gpu.recur, cache.recur)
+            assert np.array_equal(gpu.gscale, cache.gscale)
         outs.append(out)
     view = torch.int32 if outs[0].dtype == torch.float32 else torch.int16
     assert torch.equal(outs[0].view(view), outs[1].view(view))
@@ -108,10 +142,10 @@ def test_random_shape_parity(i):
     # fused flush-in-step with k ~ U{0..pnat}
     rng = np.random.default_rng(93000 + i)
     k = np.array([rng.integers(0, int(p) + 1) for p in step.pnat], np.int32)
-    out, gpu, status = _run(spec, cache, step, out_dtype, "auto", k)
+    out, gpu, status = _run(spec, cache, step, out_dtype, "auto", k, seed)
     assert status == 0
     ref_cache = cache.copy()
-    ref, status = O.replay_step(ref_cache, step, num_fold=k)
+    ref, status = O.replay_step(ref_cache, step, num_fold=k, seed=seed)
     assert status == 0
     gh.check_fused_outputs(spec, step, k, out, gpu, ref, ref_cache, out_dtype)
     assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
@@ -123,3 +157,5 @@ def test_random_shape_parity(i):
     assert gh.rel_err(gd, rd) <= 1e-6
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
+    if spec.separate:
+        gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
