@@ -11,8 +11,8 @@ allows, so that the dispatch meets combinations nobody chose:
   - varlen, padding entries and slot padding;
   - output dtype, the z gate and dt' without softplus.
 Each draw runs the plain step (monolith and split, bit for bit with each
-other) and the fused flush-in-step, against the oracle at the same bounds as
-the fixed cases.  32 more draws do the same with separate checkpoints (an
+other), the fused flush-in-step and a flush of the same k, against the
+oracle at the same bounds as the fixed cases.  32 more draws do the same with separate checkpoints (an
 fp8 or NVFP4 read checkpoint beside the FP16 recurrence checkpoint, folded
 with stochastic rounding under a drawn seed), whose folds are checked as the
 fixed separate-checkpoint cases check theirs.  The draw is printed before its
@@ -156,6 +156,23 @@ def check_draw(d, i):
     rd = ref_cache.dt_cache[:, :nb].view(np.float32).astype(np.float64)
     assert gh.rel_err(gd, rd) <= 1e-6
     touched = sorted({int(s) for s, kk in zip(step.slot_idx, k) if kk > 0 and 0 < s < spec.num_slots})
+    gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
+    if spec.separate:
+        gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
+
+    # the same k as a flush on its own
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    st = sd.upload_step(step, gh.DEV)
+    ssu.flush(dc, st["slot_idx"], torch.from_numpy(k).to(gh.DEV), st["A"], sr_seed=seed)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == 0
+    gpu = sd.download_cache(spec, t)
+    ref_cache = cache.copy()
+    assert O.flush(ref_cache, step.slot_idx, k, step.A, seed) == 0
+    assert np.array_equal(gpu.ring_start, ref_cache.ring_start)
+    for f in ("x_cache", "B_cache", "dt_cache"):
+        assert np.array_equal(getattr(gpu, f), getattr(cache, f)), f
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
     if spec.separate:
         gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
