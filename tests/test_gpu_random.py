@@ -15,8 +15,9 @@ other), the fused flush-in-step and a flush of the same k, against the
 oracle at the same bounds as the fixed cases.  32 more draws do the same with separate checkpoints (an
 fp8 or NVFP4 read checkpoint beside the FP16 recurrence checkpoint, folded
 with stochastic rounding under a drawn seed), whose folds are checked as the
-fixed separate-checkpoint cases check theirs.  The draw is printed before its
-GPU work.
+fixed separate-checkpoint cases check theirs.  24 draws run ssu_init_state
+over random shapes and id lists in every checkpoint form.  The draw is
+printed before its GPU work.
 """
 import numpy as np
 import pytest
@@ -176,3 +177,69 @@ def check_draw(d, i):
     gh.check_state(spec, gpu, ref_cache, cache, touched, (step.slot_idx, k, step.A))
     if spec.separate:
         gh.check_recur(spec, gpu, cache, step.slot_idx, k, step.A, seed)
+
+
+# init over random shapes: (state dtype, separate checkpoints)
+INIT_FORMS = [("f32", False), ("bf16", False), ("f16", False), ("fp8", False), ("fp8", True), ("nvfp4", True)]
+N_INIT = 24
+
+
+@pytest.mark.parametrize("i", range(N_INIT))
+def test_random_init_parity(i):
+    """ssu_init_state over random shapes, id lists (unique valid ids among
+    padding and out-of-range ones), row magnitudes (zero rows among them) and
+    batch strides (a stride-0 broadcast now and then): rings cleared and
+    ring starts zeroed bit for bit; 32- and 16-bit checkpoints bit for bit;
+    fp8 codes >= 99.9 % equal and otherwise one code apart with the row scales
+    bit for bit; the FP16 recurrence checkpoint bit for bit (same Philox
+    bits); NVFP4 slot and block scales bit for bit and >= 99.99 % of the
+    decoded values equal."""
+    rng = np.random.default_rng(97000 + i)
+    state, sep = INIT_FORMS[i % len(INIT_FORMS)]
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    H = G * int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+    num_slots = int(rng.integers(2, 40))
+    spec = synth.CacheSpec(num_slots=num_slots, nheads=H, ngroups=G, state_dtype=state, separate=sep,
+                           ring_len=int(rng.integers(1, 33)), slot_pad=int(rng.choice([0, 64, 256])))
+    valid = rng.permutation(np.arange(1, num_slots))[:int(rng.integers(1, num_slots))]
+    invalid = rng.choice([0, -1, num_slots, num_slots + 5], int(rng.integers(0, 4)))
+    ids = rng.permutation(np.concatenate([valid, invalid])).astype(np.int32)
+    n = ids.size
+    states = (rng.standard_normal((n, H, 64, 128)) * rng.uniform(0.01, 3.0, (n, H, 64, 1))).astype(np.float32)
+    states[rng.random((n, H, 64)) < 0.02] = 0.0
+    broadcast = bool(rng.integers(0, 3) == 0)
+    seed = int(rng.integers(0, 2 ** 63))
+    print("init draw", i, state, "separate", sep, "H", H, "G", G, "L", spec.ring_len, "slots", num_slots, "n", n,
+          "broadcast", broadcast, flush=True)
+    cache = synth.make_cache(spec, 98000 + i)
+    t = sd.upload_cache(cache, gh.DEV)
+    dc = gh.device_cache(spec, t)
+    ssu.init_state(dc, torch.from_numpy(states).to(gh.DEV), torch.from_numpy(ids).to(gh.DEV),
+                   states_batch_stride=0 if broadcast else None, sr_seed=seed)
+    torch.cuda.synchronize()
+    ref = cache.copy()
+    O.init_state(ref, states, ids, states_stride=0 if broadcast else None, seed=seed)
+    gpu = sd.download_cache(spec, t)
+    for f in ("x_cache", "B_cache", "dt_cache", "ring_start"):
+        assert np.array_equal(getattr(gpu, f), getattr(ref, f)), f
+    others = np.setdiff1d(np.arange(num_slots), valid)  # slot 0 and every slot not named: untouched
+    for f in ("state", "scale", "recur", "gscale"):
+        a = getattr(gpu, f)
+        if a is not None:
+            assert np.array_equal(a[others], getattr(cache, f)[others]), f
+    if sep:
+        assert np.array_equal(gpu.recur, ref.recur)
+    if state == "nvfp4":
+        assert np.array_equal(gpu.gscale, ref.gscale)
+        assert np.array_equal(gpu.scale, ref.scale)
+        for sl in valid:
+            g, r = O.decode_state(gpu, int(sl)), O.decode_state(ref, int(sl))
+            assert np.mean(g == r) >= 0.9999, int(sl)
+    elif state == "fp8":
+        assert np.array_equal(gpu.scale, ref.scale)
+        nb = spec.state_bytes()  # the codes of the named slots only
+        frac, dist = gh.fp8_code_agreement(gpu.state[valid, :nb], ref.state[valid, :nb])
+        assert frac >= 0.999 and dist <= 1, (frac, dist)
+        assert np.array_equal(gpu.state[:, nb:], ref.state[:, nb:])  # slot padding
+    else:
+        assert np.array_equal(gpu.state, ref.state)
