@@ -194,15 +194,6 @@ __device__ __forceinline__ int tile_off(int rb, int u, int lane, int chunks) {
   return (rb * chunks + u) * 1024 + lane * 16;
 }
 
-// Blocks are dispatched round-robin over the 8 XCDs; remap so that runs of
-// consecutive logical blocks (which share an entry's B/C rows) stay on one
-// XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = nblocks >> 3;
-  if (bid >= (per << 3)) return bid;
-  return (bid & 7) * per + (bid >> 3);
-}
-
 // ---------------------------------------------------------------------------
 // per-entry metadata and device-side contract checks
 // ---------------------------------------------------------------------------
