@@ -233,8 +233,9 @@ typedef struct ssu_step {
 /* Bytes of scratch the SPLIT algorithm needs for (batch, max_seqlen): the
  * fp32 C.B products of every (entry, group) [FI Description item 1: the
  * precompute writes C.B to caller-provided, graph-safe scratch, allocated by
- * the caller like the output].  Returns 0 for an invalid cache description
- * or a negative batch or max_seqlen. */
+ * the caller like the output].  Returns 0 for an invalid cache description,
+ * a negative batch, a max_seqlen outside [0, min(16, ring_len)] or
+ * batch * nheads > SSU_MAX_PAIRS (with the reason in ssu_last_error). */
 size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen);
 
 /*

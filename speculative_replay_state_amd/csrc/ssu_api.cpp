@@ -41,8 +41,19 @@ int ok() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// A C caller may store any int in the descriptors' enum fields.  Loading a
+// value outside the enumerators' range through the C++ enum type is
+// undefined, so every read of such a field goes through its 32 bits.
+template <class E>
+int32_t raw(const E &e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "the ABI's enums are 32-bit");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // Bytes of one head's checkpoint.
-int64_t state_head_bytes(ssu_dtype t) {
+int64_t state_head_bytes(int32_t t) {
   const int64_t e = (int64_t)ssu::kHeadDim * ssu::kDState;
   switch (t) {
     case SSU_F32: return 4 * e;
@@ -54,7 +65,7 @@ int64_t state_head_bytes(ssu_dtype t) {
   return 0;
 }
 
-int state_type_of(ssu_dtype t) {
+int state_type_of(int32_t t) {
   switch (t) {
     case SSU_F32: return ssu::kF32;
     case SSU_BF16: return ssu::kBF16;
@@ -78,20 +89,20 @@ int check_cache(const ssu_cache *c) {
                 c->headdim, c->dstate);
   if (c->ring_len < 1 || c->ring_len > ssu::kMaxRing)
     return fail(SSU_ERR_UNSUPPORTED, "ring_len must be in [1, %d] (got %d)", ssu::kMaxRing, c->ring_len);
-  if (state_type_of(c->state_dtype) < 0)
-    return fail(SSU_ERR_INVALID, "unknown state_dtype %d", (int)c->state_dtype);
-  if (c->io_dtype != SSU_BF16)
+  const int32_t sd = raw(c->state_dtype);
+  if (state_type_of(sd) < 0) return fail(SSU_ERR_INVALID, "unknown state_dtype %d", sd);
+  if (raw(c->io_dtype) != SSU_BF16)
     return fail(SSU_ERR_UNSUPPORTED, "io_dtype must be SSU_BF16 (x, B, C and the x/B rings)");
   if (!c->state || !c->x_cache || !c->B_cache || !c->dt_cache || !c->ring_start)
     return fail(SSU_ERR_INVALID, "cache tensors must not be NULL");
-  const bool nvfp4 = c->state_dtype == SSU_NVFP4;
-  if ((c->state_dtype == SSU_FP8_E4M3 || nvfp4) && !c->state_scale)
+  const bool nvfp4 = sd == SSU_NVFP4;
+  if ((sd == SSU_FP8_E4M3 || nvfp4) && !c->state_scale)
     return fail(SSU_ERR_INVALID, "fp8 and nvfp4 states require state_scale");
   if (nvfp4 && !c->state_gscale)
     return fail(SSU_ERR_INVALID, "nvfp4 state requires state_gscale");
   if (nvfp4 && !c->recur_state)
     return fail(SSU_ERR_UNSUPPORTED, "an nvfp4 read checkpoint requires recur_state (separate checkpoints)");
-  if (c->recur_state && c->state_dtype != SSU_FP8_E4M3 && !nvfp4)
+  if (c->recur_state && sd != SSU_FP8_E4M3 && !nvfp4)
     return fail(SSU_ERR_UNSUPPORTED, "recur_state (separate checkpoints) requires an fp8 or nvfp4 state");
   if (c->state_gscale && !aligned16(c->state_gscale))
     return fail(SSU_ERR_INVALID, "state_gscale must be 16-byte aligned");
@@ -102,7 +113,7 @@ int check_cache(const ssu_cache *c) {
       (c->status && !aligned4(c->status)))
     return fail(SSU_ERR_INVALID, "cache pointers must be 16-byte aligned (ring_start, status: 4-byte)");
   const int64_t H = c->nheads, G = c->ngroups, L = c->ring_len;
-  const int64_t need_state = H * state_head_bytes(c->state_dtype);
+  const int64_t need_state = H * state_head_bytes(sd);
   struct {
     const char *name;
     int64_t stride, need;
@@ -110,7 +121,7 @@ int check_cache(const ssu_cache *c) {
   } s[] = {
       {"state", c->state_slot_stride, need_state, true},
       {"state_scale", c->scale_slot_stride, nvfp4 ? H * ssu::kHeadDim * ssu::kDState / 16 : H * ssu::kHeadDim * 4,
-       c->state_dtype == SSU_FP8_E4M3 || nvfp4},
+       sd == SSU_FP8_E4M3 || nvfp4},
       {"state_gscale", c->gscale_slot_stride, (1 + H) * 4, nvfp4},
       {"x_cache", c->x_slot_stride, H * L * ssu::kHeadDim * 2, true},
       {"B_cache", c->B_slot_stride, G * L * ssu::kDState * 2, true},
@@ -176,18 +187,18 @@ int check_step(const ssu_cache *c, const ssu_step *s) {
   if (!s->slot_idx || !s->prev_num_accepted || !s->x || !s->B || !s->C || !s->dt || !s->A || !s->D ||
       !s->dt_bias || !s->out)
     return fail(SSU_ERR_INVALID, "step tensors must not be NULL (cu_seqlens and workspace may be)");
-  if (s->out_dtype != SSU_BF16 && s->out_dtype != SSU_F32)
-    return fail(SSU_ERR_UNSUPPORTED, "out_dtype must be SSU_BF16 or SSU_F32");
+  const int32_t od = raw(s->out_dtype), algo = raw(s->algo);
+  if (od != SSU_BF16 && od != SSU_F32) return fail(SSU_ERR_UNSUPPORTED, "out_dtype must be SSU_BF16 or SSU_F32");
   if (!aligned16(s->x) || !aligned16(s->B) || !aligned16(s->C) || !aligned16(s->out))
     return fail(SSU_ERR_INVALID, "x, B, C and out must be 16-byte aligned");
   if (!aligned4(s->dt) || !aligned4(s->A) || !aligned4(s->D) || !aligned4(s->dt_bias) ||
       !aligned4(s->slot_idx) || !aligned4(s->prev_num_accepted) || (s->cu_seqlens && !aligned4(s->cu_seqlens)))
     return fail(SSU_ERR_INVALID, "dt, A, D, dt_bias and the index arrays must be 4-byte aligned");
-  if (s->algo != SSU_ALGO_AUTO && s->algo != SSU_ALGO_MONOLITH && s->algo != SSU_ALGO_SPLIT)
-    return fail(SSU_ERR_INVALID, "unknown algo %d", (int)s->algo);
+  if (algo != SSU_ALGO_AUTO && algo != SSU_ALGO_MONOLITH && algo != SSU_ALGO_SPLIT)
+    return fail(SSU_ERR_INVALID, "unknown algo %d", algo);
   if (s->num_fold && !aligned4(s->num_fold)) return fail(SSU_ERR_INVALID, "num_fold must be 4-byte aligned");
   if (s->z && !aligned16(s->z)) return fail(SSU_ERR_INVALID, "z must be 16-byte aligned");
-  if (s->num_fold && s->algo == SSU_ALGO_SPLIT)
+  if (s->num_fold && algo == SSU_ALGO_SPLIT)
     return fail(SSU_ERR_UNSUPPORTED, "the fused flush (num_fold) runs in the monolith only; use AUTO or MONOLITH");
   return SSU_OK;
 }
@@ -226,7 +237,8 @@ int scratch_of_current_device(void **out) {
 }
 
 int resolve(const ssu_cache *c, const ssu_step *s) {
-  if (s->algo == SSU_ALGO_MONOLITH || s->algo == SSU_ALGO_SPLIT) return s->algo;
+  const int32_t algo = raw(s->algo);
+  if (algo == SSU_ALGO_MONOLITH || algo == SSU_ALGO_SPLIT) return algo;
   if (s->num_fold) return SSU_ALGO_MONOLITH;
   const int64_t units = (int64_t)s->batch * c->nheads;
   return units >= g_split_threshold.load(std::memory_order_relaxed) ? SSU_ALGO_SPLIT : SSU_ALGO_MONOLITH;
@@ -244,8 +256,15 @@ int64_t ssu_set_split_threshold(int64_t work_units) { return g_split_threshold.e
 
 size_t ssu_workspace_size(const ssu_cache *cache, int32_t batch, int32_t max_seqlen) {
   if (check_cache(cache) != SSU_OK) return 0;
-  if (batch < 0 || max_seqlen < 0) {
-    fail(SSU_ERR_INVALID, "batch and max_seqlen must be >= 0 (got %d, %d)", batch, max_seqlen);
+  const int tmax = cache->ring_len < ssu::kMaxTokens ? cache->ring_len : ssu::kMaxTokens;
+  if (batch < 0 || max_seqlen < 0 || max_seqlen > tmax) {
+    fail(SSU_ERR_INVALID, "workspace for batch %d, max_seqlen %d: need batch >= 0 and 0 <= max_seqlen <= %d", batch,
+         max_seqlen, tmax);
+    return 0;
+  }
+  if ((int64_t)batch * cache->nheads > SSU_MAX_PAIRS) {
+    fail(SSU_ERR_UNSUPPORTED, "batch %d x nheads %d exceeds SSU_MAX_PAIRS (%d)", batch, cache->nheads,
+         SSU_MAX_PAIRS);
     return 0;
   }
   ok();
@@ -287,8 +306,8 @@ int replay_step_checked(const ssu_cache *cache, const ssu_step *step, int algo, 
   k.dt_bias = step->dt_bias;
   k.out = step->out;
   k.cb = nullptr;
-  const int st = state_type_of(cache->state_dtype);
-  const int ot = step->out_dtype == SSU_F32 ? ssu::kOutF32 : ssu::kOutBF16;
+  const int st = state_type_of(raw(cache->state_dtype));
+  const int ot = raw(step->out_dtype) == SSU_F32 ? ssu::kOutF32 : ssu::kOutBF16;
   hipError_t err;
   if (algo == SSU_ALGO_SPLIT) {
     const size_t need = split_bytes(cache, step->batch, step->max_seqlen);
@@ -350,8 +369,8 @@ int ssu_flush(const ssu_cache *cache, const int32_t *slot_idx, const int32_t *nu
   if (!slot_idx || !num_fold || !A) return fail(SSU_ERR_INVALID, "slot_idx, num_fold and A must not be NULL");
   if (!aligned4(slot_idx) || !aligned4(num_fold) || !aligned4(A))
     return fail(SSU_ERR_INVALID, "slot_idx, num_fold and A must be 4-byte aligned");
-  hipError_t err =
-      ssu::launch_flush(kcache(cache, sr_seed), slot_idx, num_fold, A, n, state_type_of(cache->state_dtype), stream);
+  hipError_t err = ssu::launch_flush(kcache(cache, sr_seed), slot_idx, num_fold, A, n,
+                                     state_type_of(raw(cache->state_dtype)), stream);
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
 }
@@ -370,7 +389,7 @@ int ssu_init_state(const ssu_cache *cache, const float *states, int64_t states_b
   if (!aligned16(states) || states_batch_stride % 4 != 0 || !aligned4(slot_idx))
     return fail(SSU_ERR_INVALID, "states must be 16-byte aligned with a stride that is a multiple of 4");
   hipError_t err = ssu::launch_init(kcache(cache, sr_seed), states, states_batch_stride, slot_idx, n,
-                                    state_type_of(cache->state_dtype), stream);
+                                    state_type_of(raw(cache->state_dtype)), stream);
   if (err != hipSuccess) return fail(SSU_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
 }

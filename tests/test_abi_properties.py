@@ -271,13 +271,19 @@ def test_validation_matches_the_header(ssu, cache_step, threshold):
 def test_workspace_size_properties(ssu, cache, b1, b2, t):
     """SPLIT's scratch holds one fp32 C.B product per (entry, group, new
     token, ring position): at least batch * ngroups * T * ring_len * 4 bytes,
-    additive over entries, 0 for an empty step or an invalid cache."""
+    additive over entries, 0 for an empty step, an invalid cache or a step
+    past the header's limits (T > min(16, ring_len), batch * nheads >
+    SSU_MAX_PAIRS)."""
     c, _ = build(ssu, cache, {})
     w = lambda b, tt: ssu.ssu_workspace_size(c, b, tt)
     if cache_violations(cache):
         assert w(b1, t) == 0
         return
     G, L = cache["ngroups"], cache["ring_len"]
+    if t > min(16, L):
+        assert w(b1, t) == 0 and ssu.ssu_last_error()
+        return
+    assert w(ssu.SSU_MAX_PAIRS // cache["nheads"] + 1, t) == 0 and "SSU_MAX_PAIRS" in ssu.ssu_last_error()
     assert w(b1, t) >= b1 * G * t * L * 4
     assert w(b1 + b2, t) == w(b1, t) + w(b2, t)
     assert w(0, t) == 0 and w(b1, 0) == 0
