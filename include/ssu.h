@@ -45,6 +45,10 @@
  *    (slot <= 0 or slot >= num_slots, [VD]) writes zero output rows and
  *    touches no cache; an entry that breaks the ring contract is skipped the
  *    same way and ORs a bit into *cache->status when status is not NULL.
+ *    What no kernel can check is the size of the caller's buffers: the token
+ *    rows an entry addresses (b*T + t, or [cu_seqlens[b], cu_seqlens[b+1]))
+ *    must lie inside x, B, C, dt, out and z, and the device index arrays
+ *    must hold batch (batch + 1 for cu_seqlens) entries.
  */
 #ifndef SSU_H
 #define SSU_H
