@@ -251,6 +251,19 @@ class DeviceCache:
 def make_step_desc(batch, max_seqlen, slot_idx, pnat, cu_seqlens, x, B, C, dt, A, D, dt_bias, out,
                    out_dtype="bf16", workspace=None, algo="auto", num_fold=None, z=None,
                    dt_softplus=True, sr_seed=0) -> SsuStep:
+    """The ssu_step descriptor of one step, from device tensors.
+
+    slot_idx, pnat (live ring tokens ahead of the new ones), num_fold: int32
+    [batch]; cu_seqlens: int32 [batch + 1] or None (every entry then has
+    max_seqlen tokens, token t of entry b in row b * max_seqlen + t); x, z:
+    bf16 [rows, H, 64]; B, C: bf16 [rows, G, 128]; dt: f32 [rows, H]; A, D,
+    dt_bias: f32 [H]; out: [rows, H, 64] of out_dtype ("bf16" or "f32").
+    algo: "auto", "monolith" or "split" (split needs `workspace` of
+    workspace_size(cache, batch, max_seqlen) bytes).  num_fold folds the
+    first k live tokens of each entry before its readout (fused flush-in-
+    step); z gates the output; dt_softplus=False takes dt' = dt + dt_bias;
+    sr_seed keys the stochastic rounding of a fused fold into an FP16
+    recurrence checkpoint (pass a new one on every call)."""
     desc = SsuStep(
         batch, max_seqlen, _ptr(slot_idx), _ptr(pnat), _ptr(cu_seqlens),
         _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(dt_bias),
@@ -287,6 +300,8 @@ def check_step_tensors(cache: DeviceCache, step: SsuStep):
 
 
 def workspace_size(cache: DeviceCache, batch: int, max_seqlen: int) -> int:
+    """Bytes of scratch a SPLIT step of (batch, max_seqlen) needs (0 when the
+    cache or the sizes are invalid)."""
     return ssu_workspace_size(cache.desc(), batch, max_seqlen)
 
 
@@ -302,16 +317,25 @@ def init_state(cache: DeviceCache, states, slot_idx, states_batch_stride=None, s
 
 
 def replay_step(cache: DeviceCache, step: SsuStep, stream=None):
+    """ssu_replay_step: read out the step's tokens into step's `out` and append
+    them to the rings (with num_fold: fold first, and advance ring_start).
+    Raises ValueError for tensors the kernels could not address, SsuError for
+    a code the library returns."""
     check_step_tensors(cache, step)
     _check(ssu_replay_step(cache.desc(), step, _stream(stream)))
 
 
 def replay_step_noalloc(cache: DeviceCache, step: SsuStep, stream=None):
+    """ssu_replay_step_noalloc: replay_step with the SPLIT scratch taken from
+    the library's own device array (step's workspace is ignored)."""
     check_step_tensors(cache, step)
     _check(ssu_replay_step_noalloc(cache.desc(), step, _stream(stream)))
 
 
 def flush(cache: DeviceCache, slot_idx, num_fold, A, stream=None, sr_seed=0):
+    """ssu_flush: fold the first num_fold[j] live ring tokens of slot
+    slot_idx[j] into its checkpoint, re-encode it and advance ring_start
+    (slot_idx, num_fold: int32 [n]; A: f32 [H], the steps' A)."""
     n = slot_idx.numel()
     _packed(slot_idx, "slot_idx")
     _packed(num_fold, "num_fold", 4 * n)
